@@ -1,0 +1,223 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts
+ * feed-forward layer library (libmoe.so).
+ *
+ * The layer (Qwen3.8-Flash-Next architecture sheet, FFN / MoE entries): a
+ * softmax router over E expert logits, the top-k experts per token with their
+ * gates renormalised to sum to 1, routed SwiGLU experts (gate, up, down; no
+ * bias, no clamp), one always-on shared expert, and the gate-weighted sum.
+ * Routed experts are stored either in bf16 or in asymmetric AWQ W4A16 with
+ * group size 32 along the input dimension, integer zero points and fp16 scales
+ * in GEMM packing (Qwen3.8-Flash-Next-AWQ-g32 card, "Checkpoint").  Expert
+ * pruning keeps a subset of experts by slicing router rows and expert tensors
+ * (RAZOR E256of512 card, property table and "Selection and calibration"),
+ * and the Refill-RMS pass scores experts to choose that subset (same card,
+ * "Selection and calibration").
+ *
+ * Conventions for every call:
+ *  - Every pointer argument is a DEVICE pointer unless its comment says host.
+ *    bf16 and fp16 values are passed as their uint16_t bit patterns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it; nothing is waited for.  Device-side faults surface at the
+ *    caller's next synchronisation.
+ *  - All argument validation happens on the host before anything is enqueued.
+ *    On any error nothing is enqueued and the status says why.  A failed
+ *    launch returns MOE_ERR_HIP; moe_last_hip_error() then gives the
+ *    hipError_t of the calling thread's last failed HIP call.
+ *  - The library never allocates device memory and keeps no state between
+ *    calls except cached device properties.  The caller owns every buffer,
+ *    including the scratch workspace `ws` whose size comes from
+ *    moe_workspace_bytes().  Calls on different streams need distinct
+ *    workspaces.
+ *  - Results are deterministic: the same inputs give the same bits.
+ *  - T = 0 is a valid no-op for every call.
+ *
+ * Layouts (row-major, all contiguous):
+ *  x           [T][H]        bf16 hidden states (already normalised)
+ *  w_router    [E][H]        bf16, one row per expert, no bias
+ *  topk_idx    [T][k+extra]  int32 expert ids, rank order
+ *  pair id     p = t*kk + slot for kk pairs per token (kk = k, or k+1 for
+ *              Refill-RMS); "rows" are expert outputs in grouped order:
+ *              row r holds the output of pair sorted_pair[r].
+ *  bf16 experts: gate, up [E][F][H]; down [E][H][F]  (row per output feature)
+ *  AWQ experts:  for a projection with input dim I and output dim O
+ *                  qweight [E][I][O/8] int32, qzeros [E][I/32][O/8] int32,
+ *                  scales [E][I/32][O] fp16;
+ *                nibble j (bits 4j..4j+3) of word c holds column
+ *                8c + {0,2,4,6,1,3,5,7}[j];  w[e][o][i] = (q - z) * s.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    MOE_ERR_SHAPE = 2,       /* sizes inconsistent (k > E, negative T, ...)    */
+    MOE_ERR_UNSUPPORTED = 3, /* valid but not supported (E > 1024, H % 32, ...) */
+    MOE_ERR_WORKSPACE = 4,   /* ws_bytes smaller than moe_workspace_bytes()   */
+    MOE_ERR_HIP = 5          /* a HIP call failed; see moe_last_hip_error()   */
+} moe_status;
+
+typedef enum { MOE_W_BF16 = 0, MOE_W_AWQ_G32 = 1 } moe_wfmt;
+typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_dtype;
+
+/* One projection of a bank of experts, input dim in_dim, output dim out_dim. */
+typedef struct {
+    int32_t fmt;              /* moe_wfmt                                     */
+    int32_t in_dim, out_dim;
+    const uint16_t *w;        /* BF16: [E][out][in]                           */
+    const int32_t *qweight;   /* AWQ:  [E][in][out/8]                         */
+    const int32_t *qzeros;    /* AWQ:  [E][in/32][out/8]                      */
+    const uint16_t *scales;   /* AWQ:  [E][in/32][out] fp16                   */
+} moe_proj;
+
+/* A bank of SwiGLU experts: gate, up: hidden -> inter; down: inter -> hidden.
+ * The three projections share one format. */
+typedef struct {
+    int32_t num_experts, hidden, inter;
+    moe_proj gate, up, down;
+} moe_experts;
+
+/* Operation ids for moe_workspace_bytes(). */
+enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_FFN = 2, MOE_OP_REFILL_SCORE = 3 };
+
+/*
+ * Router: logits, softmax, top-k, renormalised gates.
+ * (architecture sheet: softmax gating over the expert logits, 10 of 512
+ * routed experts per token, selected weights renormalised to sum to 1.)
+ *
+ * logit[t][e] = the correctly rounded fp32 value of the exact dot product
+ * x[t] . w_router[e].  Experts are ranked by logit descending, ties to the
+ * lower index (-0.0 == +0.0).  topk_idx[t] lists the first k+extra experts
+ * in rank order; extra = 1 adds the highest-ranked unselected expert used by
+ * Refill-RMS.  topk_gate[t][j] = exp(l_j) / sum_{i<k} exp(l_i) over the
+ * first k (fp32).  topk_logit (nullable) gets the exact logits of the listed
+ * experts.  logits (nullable, [T][E]) gets every exact logit (slower; meant
+ * for tests).  Requires 1 <= k, k + extra <= E <= 1024, extra in {0,1},
+ * H % 8 == 0.
+ */
+moe_status moe_route(const uint16_t *x, const uint16_t *w_router, int32_t T, int32_t H,
+                     int32_t E, int32_t k, int32_t extra, int32_t *topk_idx, float *topk_logit,
+                     float *topk_gate, float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Permutation of (token, slot) pairs by expert: a stable counting sort of the
+ * pair ids p = t*k + slot by topk_idx[p].
+ *   expert_offsets [E+1]: rows of expert e are [offsets[e], offsets[e+1])
+ *   sorted_pair    [T*k]: pair id held by each row, ascending within an expert
+ *   pair_to_row    [T*k]: inverse of sorted_pair
+ * Entries of topk_idx must lie in [0, E); out-of-range ids are not detected
+ * (the row assignment is then undefined but stays inside the buffers).
+ */
+moe_status moe_permute(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E,
+                       int32_t *expert_offsets, int32_t *sorted_pair, int32_t *pair_to_row,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Grouped SwiGLU experts: for every row r with pair p = sorted_pair[r],
+ * token t = p / k, expert e (the group r falls in):
+ *   rows[r] = W_down[e] ( silu(W_gate[e] x[t]) * (W_up[e] x[t]) )
+ * (architecture sheet: SwiGLU, no FFN bias, no GLU clamp).
+ * With sorted_pair == NULL and expert_offsets == NULL the bank must hold one
+ * expert applied to every token (the shared expert): rows[t] = expert(x[t]),
+ * and k must be 1.  `ex` is a HOST pointer to a struct of device pointers.
+ * rows is [T*k][H] of out_dtype.  Intermediates: fp32 accumulation, the
+ * SwiGLU product rounded to bf16 before the down projection.
+ * AWQ requires hidden % 32 == 0 and inter % 32 == 0.
+ */
+moe_status moe_grouped_ffn(const uint16_t *x, int32_t T, int32_t k, const moe_experts *ex,
+                           const int32_t *expert_offsets, const int32_t *sorted_pair,
+                           int32_t out_dtype, void *rows, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/*
+ * Weighted combine (architecture sheet: routed outputs weighted by the
+ * renormalised gates, plus the always-on shared expert):
+ *   y[t] = sum_{j<k} topk_gate[t][j] * rows[pair_to_row[t*k+j]]
+ *          + shared_scale[t] * shared[t]
+ * accumulated in fp32 in slot order, rounded once to bf16.  shared (nullable)
+ * is [T][H] bf16; shared_scale (nullable) defaults to 1.  rows_dtype gives
+ * the element type of rows.
+ */
+moe_status moe_combine(const void *rows, int32_t rows_dtype, const int32_t *pair_to_row,
+                       const float *topk_gate, int32_t T, int32_t k, int32_t H,
+                       const uint16_t *shared, const float *shared_scale, uint16_t *y,
+                       void *stream);
+
+/*
+ * Refill-RMS statistics (RAZOR E256of512 card, "Selection and calibration"):
+ * for each valid token t and each selected slot j < k, drop expert
+ * topk_idx[t][j], promote topk_idx[t][k] (the highest-ranked unselected
+ * expert), renormalise the gates over the new set, and add the squared L2
+ * norm of the change of the routed output to stat_sum[topk_idx[t][j]] and 1
+ * to stat_count[...].  The shared expert cancels in the change and is not
+ * needed.  Inputs come from the k+1 routing: rows are fp32 expert outputs
+ * of the k+1 permutation (expert_offsets, sorted_pair, pair_to_row over
+ * T*(k+1) pairs), topk_idx / topk_logit are [T][k+1].  token_valid
+ * (nullable = all valid) is [T] uint8.  stat_sum (fp32 [E]) and stat_count
+ * (uint32 [E]) are ADDED to, so batches accumulate; each expert's additions
+ * are summed in a fixed order (ascending pair id) and added once per call.
+ */
+moe_status moe_refill_score(const float *rows, const int32_t *expert_offsets,
+                            const int32_t *sorted_pair, const int32_t *pair_to_row,
+                            const int32_t *topk_idx, const float *topk_logit,
+                            const uint8_t *token_valid, int32_t T, int32_t k, int32_t H,
+                            int32_t E, float *stat_sum, uint32_t *stat_count, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * Refill-RMS keep-set (same card and section): score[e] =
+ * sqrt(stat_sum[e] / (stat_count[e] * H)), 0 for experts never routed; rank
+ * by score descending, ties to the lower index; keep the first `keep`.
+ * keep_mask [E] uint8 (1 = kept); keep_idx [keep] lists the kept experts in
+ * ascending original index.  E <= 1024, 0 <= keep <= E.
+ */
+moe_status moe_refill_finalize(const float *stat_sum, const uint32_t *stat_count, int32_t E,
+                               int32_t H, int32_t keep, float *score, uint8_t *keep_mask,
+                               int32_t *keep_idx, void *stream);
+
+/*
+ * Expert pruning by slicing (RAZOR cards: surviving router rows and expert
+ * weights are slices of the base, in the keep-set's order):
+ *   w_router_dst[j] = w_router_src[keep_idx[j]]        (may be NULL to skip)
+ *   every tensor of dst expert j = that of src expert keep_idx[j]
+ * keep_idx is a device array of n_keep ids in [0, src->num_experts); src and
+ * dst are HOST pointers to structs of device pointers with the same format
+ * and sizes, dst->num_experts == n_keep.
+ */
+moe_status moe_prune_slice(const int32_t *keep_idx, int32_t n_keep, const uint16_t *w_router_src,
+                           uint16_t *w_router_dst, int32_t H, const moe_experts *src,
+                           const moe_experts *dst, void *stream);
+
+/*
+ * Router-norm keep policy (RAZOR E256of512 card, "Selection and
+ * calibration": the rule used for the layer that calibration text never
+ * executes): norm[e] = L2 norm of router row e (fp32 of an fp64 sum); rank
+ * descending, ties to the lower index; keep_idx [keep] lists the first
+ * `keep` in ascending index.  E <= 1024.
+ */
+moe_status moe_router_norm_keep(const uint16_t *w_router, int32_t E, int32_t H, int32_t keep,
+                                float *norm, int32_t *keep_idx, void *stream);
+
+/* Scratch bytes an operation needs (0 when none).  For MOE_OP_GROUPED_FFN,
+ * k is the pairs per token and E the bank's expert count.  Sizes grow with T;
+ * a workspace sized for the largest T of a run serves every smaller call. */
+size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
+
+/* Static text for a status code. */
+const char *moe_status_string(moe_status s);
+
+/* hipError_t (as int) of the calling thread's last failed HIP call, 0 if none. */
+int32_t moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,60 @@
+// Grouped-expert dispatcher: picks the weight-streaming GEMV kernels when an
+// expert sees only a few rows (decode) and the MFMA grouped GEMM otherwise.
+#include "ffn_internal.h"
+
+namespace moe {
+
+// Average rows per non-empty expert at or above which the MFMA path is used.
+constexpr int kGemmMinRows = 32;
+
+static bool use_gemm(int P, int E, int H, int F) {
+    const int active = P < E ? P : E;
+    if (active <= 0) return false;
+    if (F % 64 != 0 || H % 128 != 0) return false;
+    return P / active >= kGemmMinRows;
+}
+
+// Workspace for T*k rows, monotone in T: the GEMV path (taken below
+// kGemmMinRows rows per expert) needs at most its size at that bound.
+size_t ffn_ws_bytes(int T, int k, int E, int H, int F) {
+    const long P = (long)T * k;
+    const long Pg = P < (long)kGemmMinRows * E ? P : (long)kGemmMinRows * E;
+    const size_t g1 = gemv_ws_bytes((int)Pg, H, F, 1), g0 = gemv_ws_bytes((int)Pg, H, F, 0);
+    size_t need = g1 > g0 ? g1 : g0;
+    if (F % 64 == 0 && H % 128 == 0 && P >= (long)kGemmMinRows * E) {
+        const size_t gm = gemm_ws_bytes((int)P, F, E);
+        if (gm > need) need = gm;
+    }
+    return need;
+}
+
+hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
+    GroupedArgs a{};
+    a.x = f.x;
+    a.T = f.T;
+    a.k = f.k;
+    a.H = f.H;
+    a.F = f.F;
+    a.E = f.E;
+    a.P = f.T * f.k;
+    a.awq = f.ex->gate.fmt == MOE_W_AWQ_G32;
+    a.offsets = f.offsets;
+    a.sorted_pair = f.sorted_pair;
+    auto pj = [](const moe_proj& p) {
+        ProjDev d;
+        d.w = p.w;
+        d.qweight = p.qweight;
+        d.qzeros = p.qzeros;
+        d.scales = p.scales;
+        return d;
+    };
+    a.gate = pj(f.ex->gate);
+    a.up = pj(f.ex->up);
+    a.down = pj(f.ex->down);
+    a.out_f32 = f.out_f32;
+    a.rows = f.rows;
+    if (use_gemm(a.P, a.offsets ? a.E : 1, a.H, a.F)) return launch_gemm(a, ws, s);
+    return launch_gemv(a, ws, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,446 @@
+// Grouped SwiGLU experts for few rows per expert (decode): weight streaming.
+//
+// Qwen3.8-Flash-Next architecture sheet, FFN / MoE entries: SwiGLU experts
+// (gate, up, down), no bias, no clamp.  AWQ-g32 card, "Checkpoint":
+// asymmetric W4A16, group 32 along the input, integer zeros, fp16 scales,
+// GEMM packing.  With a handful of tokens per expert the work is a stream of
+// the touched experts' weights from HBM; each weight is read once and used
+// for every row of its expert.
+//
+// AWQ path: a word holds 8 output columns of one input row.  Two words of
+// consecutive input rows i, i+1 are merged byte by byte (v_perm) so that each
+// 32-bit register holds the codes of one column for rows i and i+1; OR-ing
+// the exponent pattern 0x4300 makes each half the bf16 value 128 + q.  One
+// v_dot2_f32_bf16 with the activation pair (x_i, x_{i+1}) accumulates
+// sum x (128 + q); per group of 32 rows the column result is
+//   s * (acc - (128 + z) * sum_group(x)) = s * sum x (q - z).
+// Threads own one word column (8 output columns) and whole groups, so the
+// zero/scale correction is paid once per group.
+#include "ffn_internal.h"
+
+namespace moe {
+
+constexpr int kAwqNib[8] = {0, 2, 4, 6, 1, 3, 5, 7};  // nibble j holds column 8c + kAwqNib[j]
+constexpr int kGemvMaxKPairs = 1024;                  // LDS activation pairs per row (2048 inputs)
+
+__device__ __forceinline__ int row_token(const int32_t* sorted_pair, int k, int r) {
+    return sorted_pair ? sorted_pair[r] / k : r;
+}
+
+// Accumulate the AWQ GEMV of groups [g_begin, g_end) stepping by g_step for one
+// word column c of a projection (I inputs, OW = O/8 words per input row).
+// xs: activation pairs [RCH][npairs] (row pairs relative to group g_base),
+// xsum: [RCH][ngroups] group sums.  res[j][i]: column 8c + kAwqNib[j], row i.
+template <int RCH>
+__device__ __forceinline__ void awq_gemv_groups(const int32_t* __restrict__ qw,
+                                                const int32_t* __restrict__ qz,
+                                                const uint16_t* __restrict__ sc, int O, int OW,
+                                                int c, int g_base, int g_begin, int g_end,
+                                                int g_step, const uint32_t* xs, int npairs,
+                                                const float* xsum, int ngroups,
+                                                float (&res)[8][RCH]) {
+    for (int g = g_begin; g < g_end; g += g_step) {
+        float acc[8][RCH];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) acc[j][i] = 0.0f;
+        const int32_t* wp = qw + (size_t)g * 32 * OW + c;
+        const int lg = g - g_base;
+#pragma unroll 4
+        for (int q = 0; q < 16; ++q) {
+            const uint32_t w0 = (uint32_t)wp[(size_t)(2 * q) * OW];
+            const uint32_t w1 = (uint32_t)wp[(size_t)(2 * q + 1) * OW];
+            uint32_t v[8];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                // bytes: [w0.b, 0, w1.b, 0]
+                const uint32_t t = __builtin_amdgcn_perm(w1, w0, 0x0C000C00u | b | ((4u + b) << 16));
+                v[2 * b] = (t & 0x000F000Fu) | 0x43004300u;
+                v[2 * b + 1] = ((t >> 4) & 0x000F000Fu) | 0x43004300u;
+            }
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) {
+                const uint32_t xp = xs[i * npairs + lg * 16 + q];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j][i] = dot2_bf16(v[j], xp, acc[j][i]);
+            }
+        }
+        const uint32_t zw = (uint32_t)qz[(size_t)g * OW + c];
+        const uint4 s4 = *reinterpret_cast<const uint4*>(sc + (size_t)g * O + 8 * c);
+        const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = kAwqNib[j];
+            const float s = f16_to_f32((sw[col / 2] >> (16 * (col % 2))) & 0xFFFFu);
+            const float zc = 128.0f + (float)((zw >> (4 * j)) & 15u);
+#pragma unroll
+            for (int i = 0; i < RCH; ++i)
+                res[j][i] = fmaf(s, fmaf(-zc, xsum[i * ngroups + lg], acc[j][i]), res[j][i]);
+        }
+    }
+}
+
+// Group sums of the staged activation pairs.
+template <int RCH>
+__device__ __forceinline__ void stage_group_sums(const uint32_t* xs, int npairs, int ngroups,
+                                                 float* xsum) {
+    for (int it = threadIdx.x; it < RCH * ngroups; it += blockDim.x) {
+        const int i = it / ngroups, g = it % ngroups;
+        float s = 0.0f;
+        for (int q = 0; q < 16; ++q) {
+            const uint32_t v = xs[i * npairs + g * 16 + q];
+            s += bf16_to_f32(v & 0xFFFFu) + bf16_to_f32(v >> 16);
+        }
+        xsum[it] = s;
+    }
+}
+
+// Deterministic reduction of per-row-phase results into red[RCH][8*OWC]:
+// phases add in order 0, 1, ..., RP-1.
+template <int RCH>
+__device__ __forceinline__ void reduce_phases(const float (&res)[8][RCH], int cl, int rp, int RP,
+                                              int ncols, float* red) {
+    for (int q = 0; q < RP; ++q) {
+        if (rp == q) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < RCH; ++i) {
+                    float* d = &red[i * ncols + 8 * cl + kAwqNib[j]];
+                    *d = q == 0 ? res[j][i] : *d + res[j][i];
+                }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// AWQ gate/up: grid (expert slot, 2*KS); block = OW * RP threads.
+// part[ks][r][mat*F + col] (fp32 partial over the WG's groups).
+// ---------------------------------------------------------------------------
+template <int RCH>
+__global__ __launch_bounds__(512) void awq_gateup_kernel(GroupedArgs a, int KS, float* __restrict__ part) {
+    __shared__ uint32_t xs[RCH * kGemvMaxKPairs];
+    __shared__ float xsum[RCH * 64];
+    extern __shared__ float red[];  // [RCH][F]
+    int r0, r1;
+    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    if (!a.offsets) { r0 = 0; r1 = a.T; }
+    if (e < 0) return;
+    const int mat = blockIdx.y / KS, ks = blockIdx.y % KS;
+    const int H = a.H, F = a.F, OW = F / 8, G = H / 32;
+    const int g0 = ks * G / KS, g1 = (ks + 1) * G / KS, ng = g1 - g0, npairs = ng * 16;
+    const int c = threadIdx.x % OW, rp = threadIdx.x / OW, RP = blockDim.x / OW;
+    const ProjDev& pj = mat ? a.up : a.gate;
+    const int32_t* qw = pj.qweight + (size_t)e * H * OW;
+    const int32_t* qz = pj.qzeros + (size_t)e * G * OW;
+    const uint16_t* sc = pj.scales + (size_t)e * G * F;
+    for (int rc = r0; rc < r1; rc += RCH) {
+        const int nr = min(RCH, r1 - rc);
+        __syncthreads();
+        for (int it = threadIdx.x; it < RCH * npairs; it += blockDim.x) {
+            const int i = it / npairs, q = it % npairs;
+            uint32_t v = 0;
+            if (i < nr) {
+                const int t = row_token(a.sorted_pair, a.k, rc + i);
+                v = reinterpret_cast<const uint32_t*>(a.x + (size_t)t * H + g0 * 32)[q];
+            }
+            xs[it] = v;
+        }
+        __syncthreads();
+        stage_group_sums<RCH>(xs, npairs, ng, xsum);
+        __syncthreads();
+        float res[8][RCH];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) res[j][i] = 0.0f;
+        if (rp < RP)
+            awq_gemv_groups<RCH>(qw, qz, sc, F, OW, c, g0, g0 + rp, g1, RP, xs, npairs, xsum, ng, res);
+        reduce_phases<RCH>(res, c, rp < RP ? rp : RP, RP, F, red);
+        for (int it = threadIdx.x; it < nr * F; it += blockDim.x) {
+            const int i = it / F, col = it % F;
+            part[((size_t)ks * a.P + rc + i) * (2 * F) + mat * F + col] = red[i * F + col];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 gate/up: grid (expert slot, F/32 column chunks); block 256 (4 waves).
+// Waves 0,1: gate columns c0..c0+31, waves 2,3: up.  16 lanes per weight row.
+// part[0][r][mat*F + col].
+// ---------------------------------------------------------------------------
+constexpr int kBfChunkK = 2048;
+
+template <int RCH>
+__global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, float* __restrict__ part) {
+    __shared__ uint4 xs[RCH * kBfChunkK / 8];
+    __shared__ float outv[64][RCH];
+    int r0, r1;
+    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    if (!a.offsets) { r0 = 0; r1 = a.T; }
+    if (e < 0) return;
+    const int H = a.H, F = a.F;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int sub = lane / 16, l16 = lane % 16;  // 4 rows per pass, 16 lanes each
+    const int c0 = blockIdx.y * 32;
+    const int mat = wave / 2;
+    const uint16_t* W = (mat ? a.up.w : a.gate.w) + (size_t)e * F * H;
+    for (int rc = r0; rc < r1; rc += RCH) {
+        const int nr = min(RCH, r1 - rc);
+        float acc[4][RCH];
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
+        for (int k0 = 0; k0 < H; k0 += kBfChunkK) {
+            const int kl = min(kBfChunkK, H - k0), nv = kl / 8;
+            __syncthreads();
+            for (int it = threadIdx.x; it < RCH * nv; it += blockDim.x) {
+                const int i = it / nv, v = it % nv;
+                uint4 val = make_uint4(0, 0, 0, 0);
+                if (i < nr) {
+                    const int t = row_token(a.sorted_pair, a.k, rc + i);
+                    val = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + k0)[v];
+                }
+                xs[i * (kBfChunkK / 8) + v] = val;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ps = 0; ps < 4; ++ps) {
+                const int col = c0 + (wave % 2) * 16 + ps * 4 + sub;
+                const uint4* wr = reinterpret_cast<const uint4*>(W + (size_t)col * H + k0);
+                for (int v = l16; v < nv; v += 16) {
+                    const uint4 w = wr[v];
+#pragma unroll
+                    for (int i = 0; i < RCH; ++i) {
+                        const uint4 xv = xs[i * (kBfChunkK / 8) + v];
+                        float s = acc[ps][i];
+                        s = dot2_bf16(w.x, xv.x, s);
+                        s = dot2_bf16(w.y, xv.y, s);
+                        s = dot2_bf16(w.z, xv.z, s);
+                        s = dot2_bf16(w.w, xv.w, s);
+                        acc[ps][i] = s;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) {
+                float v = acc[ps][i];
+                v += __shfl_xor(v, 1, kWave);
+                v += __shfl_xor(v, 2, kWave);
+                v += __shfl_xor(v, 4, kWave);
+                v += __shfl_xor(v, 8, kWave);
+                if (l16 == 0) outv[wave * 16 + ps * 4 + sub][i] = v;
+            }
+        __syncthreads();
+        for (int it = threadIdx.x; it < 64 * nr; it += blockDim.x) {
+            const int o = it % 64, i = it / 64;
+            const int m = o / 32, col = c0 + o % 32;
+            part[((size_t)rc + i) * (2 * F) + m * F + col] = outv[o][i];
+        }
+    }
+}
+
+// SwiGLU of the reduced gate/up partials for rows [rc, rc+nr) into LDS as
+// bf16 pairs h2[RCH][F/2] (the product rounded to bf16 once).
+template <int RCH>
+__device__ __forceinline__ void stage_swiglu(const float* __restrict__ part, int KS, int P, int F,
+                                             int rc, int nr, uint32_t* h2) {
+    for (int it = threadIdx.x; it < RCH * (F / 2); it += blockDim.x) {
+        const int i = it / (F / 2), f = 2 * (it % (F / 2));
+        float hv[2] = {0.0f, 0.0f};
+        if (i < nr) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float g = 0.0f, up = 0.0f;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const float* pp = part + ((size_t)ks * P + rc + i) * (2 * F);
+                    g += pp[f + u];
+                    up += pp[F + f + u];
+                }
+                hv[u] = silu(g) * up;
+            }
+        }
+        h2[it] = pack_bf16x2(hv[0], hv[1]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// AWQ down: grid (expert slot, OW/OWC column chunks); block = OWC * RP.
+// ---------------------------------------------------------------------------
+template <int RCH>
+__global__ __launch_bounds__(512) void awq_down_kernel(GroupedArgs a, int KS, int OWC,
+                                                       const float* __restrict__ part) {
+    __shared__ uint32_t xs[RCH * kGemvMaxKPairs];
+    __shared__ float xsum[RCH * 64];
+    extern __shared__ float red[];  // [RCH][8*OWC]
+    int r0, r1;
+    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    if (!a.offsets) { r0 = 0; r1 = a.T; }
+    if (e < 0) return;
+    const int H = a.H, F = a.F, OW = H / 8, G = F / 32, npairs = F / 2;
+    const int cl = threadIdx.x % OWC, rp = threadIdx.x / OWC, RP = blockDim.x / OWC;
+    const int c = blockIdx.y * OWC + cl;
+    const int32_t* qw = a.down.qweight + (size_t)e * F * OW;
+    const int32_t* qz = a.down.qzeros + (size_t)e * G * OW;
+    const uint16_t* sc = a.down.scales + (size_t)e * G * H;
+    for (int rc = r0; rc < r1; rc += RCH) {
+        const int nr = min(RCH, r1 - rc);
+        __syncthreads();
+        stage_swiglu<RCH>(part, KS, a.P, F, rc, nr, xs);
+        __syncthreads();
+        stage_group_sums<RCH>(xs, npairs, G, xsum);
+        __syncthreads();
+        float res[8][RCH];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) res[j][i] = 0.0f;
+        awq_gemv_groups<RCH>(qw, qz, sc, H, OW, c, 0, rp, G, RP, xs, npairs, xsum, G, res);
+        reduce_phases<RCH>(res, cl, rp, RP, 8 * OWC, red);
+        const int ncol = 8 * OWC;
+        for (int it = threadIdx.x; it < nr * ncol; it += blockDim.x) {
+            const int i = it / ncol, col = it % ncol;
+            const size_t o = (size_t)(rc + i) * H + (size_t)blockIdx.y * ncol + col;
+            const float v = red[i * ncol + col];
+            if (a.out_f32) static_cast<float*>(a.rows)[o] = v;
+            else static_cast<uint16_t*>(a.rows)[o] = (uint16_t)f32_to_bf16_bits(v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 down: grid (expert slot, H/64 row chunks); block 256; 16 lanes per row.
+// ---------------------------------------------------------------------------
+template <int RCH>
+__global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
+                                                        const float* __restrict__ part) {
+    __shared__ uint32_t h2[RCH * kGemvMaxKPairs];
+    __shared__ float outv[64][RCH];
+    int r0, r1;
+    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    if (!a.offsets) { r0 = 0; r1 = a.T; }
+    if (e < 0) return;
+    const int H = a.H, F = a.F, nv = F / 8;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int sub = lane / 16, l16 = lane % 16;
+    const int o0 = blockIdx.y * 64;
+    const uint16_t* W = a.down.w + (size_t)e * H * F;
+    const uint4* hv = reinterpret_cast<const uint4*>(h2);
+    for (int rc = r0; rc < r1; rc += RCH) {
+        const int nr = min(RCH, r1 - rc);
+        __syncthreads();
+        stage_swiglu<RCH>(part, KS, a.P, F, rc, nr, h2);
+        __syncthreads();
+        float acc[4][RCH];
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps) {
+            const int o = o0 + wave * 16 + ps * 4 + sub;
+            const uint4* wr = reinterpret_cast<const uint4*>(W + (size_t)o * F);
+            for (int v = l16; v < nv; v += 16) {
+                const uint4 w = wr[v];
+#pragma unroll
+                for (int i = 0; i < RCH; ++i) {
+                    const uint4 xv = hv[i * (F / 8) + v];
+                    float s = acc[ps][i];
+                    s = dot2_bf16(w.x, xv.x, s);
+                    s = dot2_bf16(w.y, xv.y, s);
+                    s = dot2_bf16(w.z, xv.z, s);
+                    s = dot2_bf16(w.w, xv.w, s);
+                    acc[ps][i] = s;
+                }
+            }
+        }
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) {
+                float v = acc[ps][i];
+                v += __shfl_xor(v, 1, kWave);
+                v += __shfl_xor(v, 2, kWave);
+                v += __shfl_xor(v, 4, kWave);
+                v += __shfl_xor(v, 8, kWave);
+                if (l16 == 0) outv[wave * 16 + ps * 4 + sub][i] = v;
+            }
+        __syncthreads();
+        for (int it = threadIdx.x; it < 64 * nr; it += blockDim.x) {
+            const int o = it % 64, i = it / 64;
+            const size_t idx = (size_t)(rc + i) * H + o0 + o;
+            const float v = outv[o][i];
+            if (a.out_f32) static_cast<float*>(a.rows)[idx] = v;
+            else static_cast<uint16_t*>(a.rows)[idx] = (uint16_t)f32_to_bf16_bits(v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+int gemv_ksplit(const GroupedArgs& a) {
+    if (!a.awq) return 1;
+    const int G = a.H / 32;
+    int ks = 5;                            // 16 groups per workgroup at H = 2560
+    while (ks > 1 && G % ks) --ks;
+    while ((G + ks - 1) / ks * 16 > kGemvMaxKPairs) ++ks;  // LDS bound
+    return ks;
+}
+
+size_t gemv_ws_bytes(int P, int H, int F, int awq) {
+    GroupedArgs a{};
+    a.H = H;
+    a.awq = awq;
+    return (size_t)gemv_ksplit(a) * P * 2 * F * sizeof(float);
+}
+
+static int down_owc(int OW) {
+    const int cand[5] = {64, 32, 16, 8, 4};
+    if (OW <= 64) return OW;
+    for (int c : cand)
+        if (OW % c == 0) return c;
+    return 4;
+}
+
+template <int RCH>
+static hipError_t launch_gemv_rch(const GroupedArgs& a, float* part, hipStream_t s) {
+    const int slots = a.offsets ? (a.P < a.E ? a.P : a.E) : 1;
+    const int F = a.F, H = a.H;
+    if (a.awq) {
+        const int KS = gemv_ksplit(a);
+        const int OW = F / 8;
+        int RP = 256 / OW;
+        if (RP < 1) RP = 1;
+        if (RP > 16) RP = 16;
+        const size_t red_bytes = (size_t)RCH * F * sizeof(float);
+        hipLaunchKernelGGL(awq_gateup_kernel<RCH>, dim3(slots, 2 * KS), dim3(OW * RP), red_bytes, s,
+                           a, KS, part);
+        const int OWd = H / 8, OWC = down_owc(OWd);
+        int RPd = 256 / OWC;
+        if (RPd < 1) RPd = 1;
+        if (RPd > 16) RPd = 16;
+        hipLaunchKernelGGL(awq_down_kernel<RCH>, dim3(slots, OWd / OWC), dim3(OWC * RPd),
+                           (size_t)RCH * 8 * OWC * sizeof(float), s, a, KS, OWC,
+                           (const float*)part);
+    } else {
+        hipLaunchKernelGGL(bf16_gateup_kernel<RCH>, dim3(slots, F / 32), dim3(256), 0, s, a, part);
+        hipLaunchKernelGGL(bf16_down_kernel<RCH>, dim3(slots, H / 64), dim3(256), 0, s, a, 1,
+                           (const float*)part);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(const GroupedArgs& a, void* ws, hipStream_t s) {
+    float* part = static_cast<float*>(ws);
+    if (!a.offsets && a.T > 4) return launch_gemv_rch<8>(a, part, s);
+    return launch_gemv_rch<4>(a, part, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,179 @@
+// Permutation of (token, slot) pairs by expert: a stable counting sort.
+//
+// The pages route each token to its top-k experts (Qwen3.8-Flash-Next
+// architecture sheet, MoE entries) without spelling out how the pairs are
+// grouped; this is the plain grouping: rows of expert e are
+// [offsets[e], offsets[e+1]), holding its pair ids in ascending order.
+//
+// Stability inside a chunk of 64 pairs comes from a wave-wide "match":
+// ballots over the bits of the expert id give each lane the mask of lanes
+// with the same expert; a lane's rank is the count of such lanes below it.
+// Chunks are processed in order by one wave, so the order is deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kPermChunk = 2048;     // pairs per block in the multi-block path
+constexpr int kSmallPairs = 4096;    // single-workgroup path up to this many pairs
+
+// Expert ids outside [0, E) are clamped so that every row stays inside the buffers.
+__device__ __forceinline__ int clamp_expert(int e, int E) { return min(max(e, 0), E - 1); }
+
+__device__ __forceinline__ int bits_for(int E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b;
+}
+
+// One wave scatters pairs [p0, p1) in order; cursor[e] (LDS) is the next row of e.
+__device__ void wave_scatter(const int32_t* __restrict__ idx, int p0, int p1, int E, int nbits,
+                             int* cursor, int32_t* __restrict__ sorted_pair,
+                             int32_t* __restrict__ pair_to_row) {
+    const int lane = threadIdx.x % kWave;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    for (int c = p0; c < p1; c += kWave) {
+        const int p = c + lane;
+        const bool active = p < p1;
+        const int e = active ? clamp_expert(idx[p], E) : 0;
+        uint64_t peers = __ballot(active);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(active && bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & below);
+        const int cnt = __popcll(peers);
+        const int base = active ? cursor[e] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (active) {
+            const int row = base + rank;
+            sorted_pair[row] = p;
+            pair_to_row[p] = row;
+        }
+        if (active && rank == 0) cursor[e] = base + cnt;
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Single workgroup: histogram, scan, scatter.  block = 256.
+__global__ __launch_bounds__(256) void permute_small_kernel(const int32_t* __restrict__ idx, int P,
+                                                            int E, int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_pair,
+                                                            int32_t* __restrict__ pair_to_row) {
+    __shared__ int cnt[1024];
+    __shared__ int scan_tmp[256];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&cnt[clamp_expert(idx[p], E)], 1);
+    __syncthreads();
+    // exclusive scan over E (<= 1024): each thread owns 4 consecutive experts
+    int local[4], sum = 0;
+    for (int j = 0; j < 4; ++j) {
+        const int e = threadIdx.x * 4 + j;
+        local[j] = e < E ? cnt[e] : 0;
+        sum += local[j];
+    }
+    scan_tmp[threadIdx.x] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        int v = threadIdx.x >= off ? scan_tmp[threadIdx.x - off] : 0;
+        __syncthreads();
+        scan_tmp[threadIdx.x] += v;
+        __syncthreads();
+    }
+    int run = scan_tmp[threadIdx.x] - sum;
+    for (int j = 0; j < 4; ++j) {
+        const int e = threadIdx.x * 4 + j;
+        if (e < E) {
+            cnt[e] = run;          // becomes the cursor
+            offsets[e] = run;
+        }
+        run += local[j];
+    }
+    if (threadIdx.x == 0) offsets[E] = P;
+    __syncthreads();
+    if (threadIdx.x < kWave) wave_scatter(idx, 0, P, E, bits_for(E), cnt, sorted_pair, pair_to_row);
+}
+
+// Multi-block path, pass 1: per-block histograms counts[b][e].
+__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ idx, int P,
+                                                           int E, int32_t* __restrict__ counts) {
+    __shared__ int cnt[1024];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    const int p0 = blockIdx.x * kPermChunk, p1 = min(P, p0 + kPermChunk);
+    for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) atomicAdd(&cnt[clamp_expert(idx[p], E)], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Pass 2 (one block of 1024): counts[b][e] becomes the first row of block b's
+// pairs of expert e; offsets[] gets the expert boundaries.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ counts, int nb,
+                                                            int E, int P,
+                                                            int32_t* __restrict__ offsets) {
+    __shared__ int tot[1024];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int b = 0; b < nb; ++b) {
+            const int c = counts[(size_t)b * E + e];
+            counts[(size_t)b * E + e] = run;
+            run += c;
+        }
+    }
+    tot[e] = e < E ? run : 0;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        int v = e >= off ? tot[e - off] : 0;
+        __syncthreads();
+        tot[e] += v;
+        __syncthreads();
+    }
+    const int base = tot[e] - (e < E ? run : 0);
+    if (e < E) {
+        offsets[e] = base;
+        for (int b = 0; b < nb; ++b) counts[(size_t)b * E + e] += base;
+    }
+    if (e == 0) offsets[E] = P;
+}
+
+// Pass 3: one wave per block scatters its chunk in order.
+__global__ __launch_bounds__(64) void permute_scatter_kernel(const int32_t* __restrict__ idx, int P,
+                                                             int E,
+                                                             const int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ sorted_pair,
+                                                             int32_t* __restrict__ pair_to_row) {
+    __shared__ int cursor[1024];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] = counts[(size_t)blockIdx.x * E + e];
+    __syncthreads();
+    const int p0 = blockIdx.x * kPermChunk, p1 = min(P, p0 + kPermChunk);
+    wave_scatter(idx, p0, p1, E, bits_for(E), cursor, sorted_pair, pair_to_row);
+}
+
+size_t permute_ws_bytes(int T, int k, int E) {
+    const long P = (long)T * k;
+    if (P <= kSmallPairs) return 0;
+    const long nb = (P + kPermChunk - 1) / kPermChunk;
+    return (size_t)nb * E * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_to_row, void* ws, hipStream_t s) {
+    const int P = T * k;
+    if (P <= kSmallPairs) {
+        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(256), 0, s, idx, P, E, offsets,
+                           sorted_pair, pair_to_row);
+        return hipGetLastError();
+    }
+    const int nb = (P + kPermChunk - 1) / kPermChunk;
+    int32_t* counts = static_cast<int32_t*>(ws);
+    hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(256), 0, s, idx, P, E, counts);
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nb, E, P, offsets);
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(64), 0, s, idx, P, E, counts,
+                       sorted_pair, pair_to_row);
+    return hipGetLastError();
+}
+
+}  // namespace moe

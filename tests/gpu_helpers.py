@@ -1,0 +1,56 @@
+"""Helpers for the GPU parity tests: device inputs from the seeded generator,
+oracle banks built from the same bytes, and the tolerance checks."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from tests.helpers import allclose_report
+
+# Output tolerance for bf16 layer outputs: |gpu - ref| <= ATOL + RTOL * |ref|, ref = fp64 oracle.
+ATOL, RTOL = 1e-2, 2e-2
+# A normwise bound that systematic errors (a dropped term, a wrong scale) cannot
+# hide under the elementwise allowance: ||gpu - ref|| <= NORM_RTOL * ||ref||.
+# bf16 storage of h and of the outputs contributes ~2^-9 relative each.
+NORM_RTOL = 1e-2
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_moe_expert_router_amd as moe
+    moe.lib()  # fails loudly when the library is missing
+    return moe
+
+
+def bits(t):
+    return workloads.bits(t)
+
+
+def oracle_bank(bank: dict, experts=None) -> O.Bank:
+    """Oracle view of a device bank dict, optionally only the listed experts (host copies)."""
+    sel = None if experts is None else torch.as_tensor(np.asarray(experts), dtype=torch.long)
+    d = {}
+    for name, t in bank.items():
+        if name == "fmt":
+            d[name] = t
+        else:
+            tt = t if sel is None else t.index_select(0, sel.to(t.device))
+            d[name] = bits(tt)
+    return O.bank_from_tensors(d)
+
+
+def check_close(got, ref, what="", atol=ATOL, rtol=RTOL, norm_rtol=NORM_RTOL):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    ok, excess, i = allclose_report(got, ref, atol, rtol)
+    assert ok, f"{what}: elementwise tolerance exceeded by {excess:.3e} at flat index {i} " \
+               f"(got {got.ravel()[i]:.6g}, ref {ref.ravel()[i]:.6g})"
+    num = np.linalg.norm(got - ref)
+    den = np.linalg.norm(ref)
+    assert num <= norm_rtol * den + 1e-12, f"{what}: normwise error {num / max(den, 1e-30):.3e}"
+
+
+def gpu_inputs(w, seed=0, device="cuda", copy=0):
+    return workloads.generate(w, seed=seed, device=device, copy=copy)

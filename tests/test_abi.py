@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every entry point include/moe.h declares,
+and rejects bad arguments on the host before touching the GPU (these calls
+return before any HIP call, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_expert_router_amd as moe
+from sparse_moe_expert_router_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe.h")
+OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = moe.lib()
+    for s in range(6):
+        assert L.moe_status_string(s)
+    assert L.moe_last_hip_error() == 0
+
+
+def test_route_validation():
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    args = lambda T, H, E, k, extra, x=fake: (x, fake, T, H, E, k, extra, fake, None, fake, None,
+                                              fake, 1 << 30, None)
+    assert L.moe_route(*args(4, 64, 8, 9, 0)) == SHAPE       # k > E
+    assert L.moe_route(*args(4, 64, 8, 8, 1)) == SHAPE       # k + extra > E
+    assert L.moe_route(*args(-1, 64, 8, 2, 0)) == SHAPE
+    assert L.moe_route(*args(4, 64, 2048, 2, 0)) == UNSUP    # E > 1024
+    assert L.moe_route(*args(4, 60, 8, 2, 0)) == UNSUP       # H % 8
+    assert L.moe_route(*args(0, 64, 8, 2, 0)) == OK          # T = 0: no-op
+    assert L.moe_route(*args(4, 64, 8, 2, 0, x=None)) == NULL
+    assert L.moe_route(fake, fake, 4, 64, 8, 2, 0, fake, None, fake, None, fake, 16, None) == WS
+
+
+def test_permute_and_combine_validation():
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    assert L.moe_permute(fake, 4, 0, 8, fake, fake, fake, None, 0, None) == SHAPE
+    assert L.moe_permute(fake, 4, 2, 4096, fake, fake, fake, None, 0, None) == UNSUP
+    assert L.moe_permute(None, 4, 2, 8, fake, fake, fake, None, 0, None) == NULL
+    assert L.moe_permute(fake, 100000, 10, 512, fake, fake, fake, None, 0, None) == WS
+    assert L.moe_combine(fake, 0, fake, fake, 4, 2, 60, None, None, fake, None) == UNSUP
+    assert L.moe_combine(fake, 7, fake, fake, 4, 2, 64, None, None, fake, None) == UNSUP
+    assert L.moe_combine(None, 0, fake, fake, 4, 2, 64, None, None, fake, None) == NULL
+
+
+def _bank(fmt=0, E=4, H=256, F=128, ptr=256):
+    mk = lambda i, o: _lib._Proj(fmt, i, o, ptr, ptr, ptr, ptr)
+    return _lib._Experts(E, H, F, mk(H, F), mk(H, F), mk(F, H))
+
+
+def test_grouped_ffn_validation():
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    b = _bank()
+    call = lambda bank, T=8, k=2, off=fake, sp=fake, dt=0, ws=1 << 30: L.moe_grouped_ffn(
+        fake, T, k, ctypes.byref(bank), off, sp, dt, fake, fake, ws, None)
+    assert call(b, k=0) == SHAPE
+    assert call(_bank(E=0)) == SHAPE
+    assert call(_bank(H=200)) == UNSUP                     # hidden % 64
+    assert call(_bank(fmt=1, F=48)) == UNSUP               # AWQ width % 32
+    assert call(_bank(fmt=5)) == UNSUP
+    assert call(b, off=None) == NULL                       # half of the permutation
+    assert call(b, off=None, sp=None) == SHAPE             # identity needs one expert and k = 1
+    assert call(_bank(E=1), k=1, off=None, sp=None, T=0) == OK
+    assert call(b, dt=3) == UNSUP
+    assert call(b, ws=0) == WS
+    bad = _bank()
+    bad.down.in_dim = 64                                   # inconsistent projection sizes
+    assert call(bad) == SHAPE
+    assert L.moe_grouped_ffn(fake, 8, 2, None, fake, fake, 0, fake, fake, 1 << 30, None) == NULL
+
+
+def test_refill_and_keep_validation():
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    assert L.moe_refill_score(fake, fake, fake, fake, fake, fake, None, 8, 10, 64, 10, fake, fake,
+                              fake, 1 << 30, None) == SHAPE   # E < k + 1
+    assert L.moe_refill_score(fake, fake, fake, fake, fake, fake, None, 8, 40, 64, 512, fake, fake,
+                              fake, 1 << 30, None) == UNSUP   # k + 1 > 32
+    assert L.moe_refill_score(fake, fake, fake, fake, fake, fake, None, 8, 10, 64, 512, fake, fake,
+                              fake, 0, None) == WS
+    assert L.moe_refill_finalize(fake, fake, 16, 64, 17, fake, fake, fake, None) == SHAPE
+    assert L.moe_refill_finalize(fake, fake, 2048, 64, 17, fake, fake, fake, None) == UNSUP
+    assert L.moe_router_norm_keep(fake, 16, 64, -1, fake, fake, None) == SHAPE
+    src, dst = _bank(E=8), _bank(E=3)
+    assert L.moe_prune_slice(fake, 4, fake, fake, 256, ctypes.byref(src), ctypes.byref(dst), None) == SHAPE
+    assert L.moe_prune_slice(fake, 3, fake, None, 256, ctypes.byref(src), ctypes.byref(dst), None) == NULL
+
+
+def test_workspace_sizes_monotone_in_tokens():
+    for op, k in ((moe.OP_ROUTE, 10), (moe.OP_PERMUTE, 10), (moe.OP_GROUPED_FFN, 10),
+                  (moe.OP_REFILL_SCORE, 10)):
+        sizes = [moe.workspace_bytes(op, T, k, 512, 2560, 640) for T in (16, 256, 4096, 32768)]
+        assert sizes == sorted(sizes), (op, sizes)
