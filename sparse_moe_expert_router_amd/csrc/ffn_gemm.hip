@@ -225,7 +225,7 @@ __global__ __launch_bounds__(2 * BM) void grouped_gemm_kernel(GroupedArgs a,
                     const int b = j >> 1;
                     // float bits 0x41 | byte | 00 | 00  ->  16 + q
                     const uint32_t mbits =
-                        __builtin_amdgcn_perm(0x41000000u, src, 0x070C0C0Cu | ((uint32_t)b << 16));
+                        __builtin_amdgcn_perm(0x41000000u, src, 0x07000C0Cu | ((uint32_t)b << 16));
                     const int col = awq_perm(j);
                     const float w = fmaf(__uint_as_float(mbits), s[col], c[col]);
                     const __bf16 wb = (__bf16)w;

@@ -409,6 +409,14 @@ static int down_owc(int OW) {
     return 4;
 }
 
+// Row phases for OW word columns: about 256 threads, a whole number of waves.
+static int row_phases(int OW) {
+    int rp = 256 / OW;
+    if (rp < 1) rp = 1;
+    while ((OW * rp) % kWave != 0 && OW * (rp + 1) <= 512) ++rp;
+    return rp;
+}
+
 template <int RCH>
 static hipError_t launch_gemv_rch(const GroupedArgs& a, float* part, hipStream_t s) {
     const int slots = a.offsets ? (a.P < a.E ? a.P : a.E) : 1;
@@ -416,16 +424,12 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, float* part, hipStream_t
     if (a.awq) {
         const int KS = gemv_ksplit(a);
         const int OW = F / 8;
-        int RP = 256 / OW;
-        if (RP < 1) RP = 1;
-        if (RP > 16) RP = 16;
+        const int RP = row_phases(OW);
         const size_t red_bytes = (size_t)RCH * F * sizeof(float);
         hipLaunchKernelGGL(awq_gateup_kernel<RCH>, dim3(slots, 2 * KS), dim3(OW * RP), red_bytes, s,
                            a, KS, part);
         const int OWd = H / 8, OWC = down_owc(OWd);
-        int RPd = 256 / OWC;
-        if (RPd < 1) RPd = 1;
-        if (RPd > 16) RPd = 16;
+        const int RPd = row_phases(OWC);
         hipLaunchKernelGGL(awq_down_kernel<RCH>, dim3(slots, OWd / OWC), dim3(OWC * RPd),
                            (size_t)RCH * 8 * OWC * sizeof(float), s, a, KS, OWC,
                            (const float*)part);

@@ -45,12 +45,15 @@ __device__ __forceinline__ int slot_expert(const int32_t* offsets, int E, int sl
     __shared__ unsigned long long s_mask[16];
     __shared__ int s_e, s_r0, s_r1;
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, wave = tid / kWave, nwaves = blockDim.x / kWave;
-    for (int chunk = wave; chunk < 16; chunk += nwaves) {
-        const int e = chunk * kWave + lane;
-        const bool ne = e < E && offsets[e + 1] > offsets[e];
-        const unsigned long long m = __ballot(ne);
-        if (lane == 0) s_mask[chunk] = m;
+    // ballots from complete waves only (a partial wave would see a partial mask)
+    const int lane = tid % kWave, wave = tid / kWave, nfull = blockDim.x / kWave;
+    if (wave < nfull) {
+        for (int chunk = wave; chunk < 16; chunk += nfull) {
+            const int e = chunk * kWave + lane;
+            const bool ne = e < E && offsets[e + 1] > offsets[e];
+            const unsigned long long m = __ballot(ne);
+            if (lane == 0) s_mask[chunk] = m;
+        }
     }
     __syncthreads();
     if (tid == 0) {
