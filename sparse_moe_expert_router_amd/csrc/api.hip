@@ -22,7 +22,16 @@ bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p % 16) == 0;
 
 constexpr int kMaxE = 1024;
 
-size_t route_ws(int T, int E) { return (size_t)T * E * sizeof(float); }
+// Screened routing (approximate MFMA logits + exact recompute of candidates)
+// for batches of at least kFilterMinT tokens and E a multiple of 256;
+// otherwise every logit is computed exactly.
+constexpr int kFilterMinT = 64;
+bool route_filtered(int T, int H, int E) { return T >= kFilterMinT && E % 256 == 0 && H % 32 == 0; }
+
+size_t route_ws(int T, int E, int H) {
+    if (route_filtered(T, H, E)) return moe::route_filter_ws_bytes(T, E, H);
+    return (size_t)T * E * sizeof(float);
+}
 
 bool proj_ok(const moe_proj& p, int fmt, int in_dim, int out_dim, int E, moe_status* st) {
     if (p.fmt != fmt || p.in_dim != in_dim || p.out_dim != out_dim) {
@@ -70,13 +79,20 @@ moe_status moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int
     if (T == 0) return MOE_OK;
     if (!x || !w_router || !topk_idx) return MOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!logits && route_filtered(T, H, E)) {
+        if (ws_bytes < route_ws(T, E, H)) return MOE_ERR_WORKSPACE;
+        if (!ws) return MOE_ERR_NULL;
+        if (!aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+        return hip_status(moe::launch_route_filter(x, w_router, T, H, E, k, extra, topk_idx,
+                                                   topk_logit, topk_gate, ws, s));
+    }
     float* lbuf = logits;
     if (!lbuf) {
-        if (ws_bytes < route_ws(T, E)) return MOE_ERR_WORKSPACE;
+        if (ws_bytes < route_ws(T, E, H)) return MOE_ERR_WORKSPACE;
         if (!ws) return MOE_ERR_NULL;
         lbuf = static_cast<float*>(ws);
     }
-    hipStream_t s = static_cast<hipStream_t>(stream);
     moe_status st = hip_status(moe::launch_exact_logits(x, w_router, T, H, E, lbuf, s));
     if (st != MOE_OK) return st;
     return hip_status(moe::launch_topk(lbuf, T, E, k, extra, topk_idx, topk_logit, topk_gate, s));
@@ -236,7 +252,7 @@ moe_status moe_router_norm_keep(const uint16_t* w_router, int32_t E, int32_t H, 
 size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
     if (T <= 0 || k <= 0 || E <= 0) return 0;
     switch (op) {
-        case MOE_OP_ROUTE: return route_ws(T, E);
+        case MOE_OP_ROUTE: return route_ws(T, E, H);
         case MOE_OP_PERMUTE: return moe::permute_ws_bytes(T, k, E);
         case MOE_OP_GROUPED_FFN: return moe::ffn_ws_bytes(T, k, E, H, F);
         case MOE_OP_REFILL_SCORE: return moe::refill_ws_bytes(T, k);

@@ -10,7 +10,7 @@ constexpr int kGemmMinRows = 32;
 static bool use_gemm(int P, int E, int H, int F) {
     const int active = P < E ? P : E;
     if (active <= 0) return false;
-    if (F % 64 != 0 || H % 128 != 0) return false;
+    if (F % 128 != 0 || H % 256 != 0) return false;
     return P / active >= kGemmMinRows;
 }
 
@@ -21,7 +21,7 @@ size_t ffn_ws_bytes(int T, int k, int E, int H, int F) {
     const long Pg = P < (long)kGemmMinRows * E ? P : (long)kGemmMinRows * E;
     const size_t g1 = gemv_ws_bytes((int)Pg, H, F, 1), g0 = gemv_ws_bytes((int)Pg, H, F, 0);
     size_t need = g1 > g0 ? g1 : g0;
-    if (F % 64 == 0 && H % 128 == 0 && P >= (long)kGemmMinRows * E) {
+    if (F % 128 == 0 && H % 256 == 0 && P >= (long)kGemmMinRows * E) {
         const size_t gm = gemm_ws_bytes((int)P, F, E);
         if (gm > need) need = gm;
     }

@@ -8,30 +8,45 @@
 // Two passes per bank, both a grouped GEMM over the rows of each expert:
 //   gate/up: h[r] = silu(W_gate x_t) * (W_up x_t)   A = gathered token rows
 //   down:    rows[r] = W_down h[r]                  A = h rows (contiguous)
-// Workgroup tile: BM rows (64, 128 or 256, from the average rows per expert)
-// x 128 B-columns, K step 32 (= one AWQ group), BM/32 waves as BM/64 (rows)
-// x 2 (columns), each wave 64 x 64 on
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  For gate/up the 128
-// B-columns are 64 gate and the same 64 up columns, so SwiGLU is applied in
-// registers.  A and B tiles are staged in LDS, double buffered through
-// registers.
 //
-// AWQ B tile: each thread owns one input row of one packed word (8 columns).
-// A code q is placed in the top mantissa bits of an fp32 with exponent 2^4,
-// giving m = 16 + q exactly; with c = -(16 + z) * s (exact: 5 x 11 bits),
-// fma(m, s, c) = (q - z) * s exactly, then one RNE to bf16.  s and c per
-// column of the group are computed once per K step by 128 threads into LDS.
+// Workgroup: 4 waves, tile BM rows x 256 B-columns, K step 32 (= one AWQ
+// group).  BM = 256: waves 2 x 2, each 128 x 128 (64 accumulator tiles of
+// v_mfma_f32_16x16x32_bf16, 256 fp32 per lane); BM = 128 / 64: waves 1 x 4,
+// each BM x 64.  For gate/up the 256 B-columns are 128 gate columns and the
+// same 128 up columns; every wave holds matching gate and up tiles, so SwiGLU
+// is applied in registers.
+//
+// Pipeline: A and B tiles go global -> registers -> LDS (two LDS stages);
+// the loads for step k+2 are issued before the MFMAs of step k, and step k+1
+// is written to LDS after them, with one barrier per step.
+//
+// AWQ B tile: a thread owns 4 consecutive input rows of one packed word
+// (8 columns).  A code q is placed in the top mantissa bits of an fp32 with
+// exponent 2^4 (m = 16 + q, exact); with c = -(16 + z) * s (exact: 5 x 11
+// bits), fma(m, s, c) = (q - z) * s exactly, then one RNE to bf16.  The four
+// rows of a column are contiguous in the K-major LDS tile: one 8-byte store.
 //
 // Tiles are enumerated per expert (ceil(rows / BM) each) by a small kernel;
 // workgroup ids are remapped so that each XCD (ids are dealt round-robin over
-// 8 XCDs) works on a contiguous range of tiles with the column tiles of one
-// row tile adjacent: the A rows and the expert's weights are then reused from
-// that XCD's L2.
+// 8 XCDs) works on a contiguous range of tiles, the column tiles of one row
+// tile adjacent: the A rows and the expert's weights are then reused from that
+// XCD's L2.
 #include "ffn_internal.h"
 
 namespace moe {
 
-constexpr int kBN = 128, kBK = 32, kLDK = kBK + 8;  // LDS row stride (bf16)
+constexpr int kBN = 256, kBK = 32;  // B-columns per workgroup, K step
+
+// LDS tiles are [row][32] bf16 (64-byte rows, no padding).  The 16-byte chunk
+// c of row r is stored at chunk c ^ ((r >> 2) & 3): sixteen lanes that read
+// 16 consecutive rows at one chunk, or write four rows x four chunks, then
+// touch 256 distinct bytes (all 64 banks once).
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3); }
+
+// AWQ B tiles store B-column c at LDS row c ^ ((c >> 3) & 3): the 8-byte stores
+// of four adjacent packed words (columns 8 apart) then land in four different
+// row classes.  The permutation stays inside aligned groups of 8 columns.
+constexpr int kThreads = 256;
 constexpr int kXcd = 8;
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
@@ -77,18 +92,100 @@ __device__ __forceinline__ int xcd_remap(int p, int G) {
 
 // Packing order {0,2,4,6,1,3,5,7}: nibble j holds column awq_perm(j) of its word.
 __device__ __forceinline__ int awq_perm(int j) { return (j < 4) ? 2 * j : 2 * (j - 4) + 1; }
-__device__ __forceinline__ int awq_nibble_of_col(int c8) { return (c8 & 1) ? 4 + (c8 >> 1) : (c8 >> 1); }
+__device__ __forceinline__ int awq_row(int c) { return c ^ ((c >> 3) & 3); }
+
+template <int BM>
+struct GemmShape {
+    static constexpr int WM = BM == 256 ? 2 : 1;  // waves along rows
+    static constexpr int WN = 4 / WM;             // waves along columns
+    static constexpr int MW = BM / WM;            // rows per wave
+    static constexpr int NW = kBN / WN;           // B-columns per wave
+    static constexpr int TM = MW / 16, TN = NW / 16;
+    static constexpr int APER = BM * 4 / kThreads;  // 16-byte A chunks per thread per step
+};
+
+// Registers of one K step -> LDS stage (A chunks; bf16 B chunks or dequantised AWQ words).
+template <int MODE, bool AWQ, int APER>
+__device__ __forceinline__ void store_stage(const uint4 (&ra)[APER], const uint4 (&rb)[AWQ ? 1 : 4],
+                                            const uint32_t (&rw)[4], uint32_t rz, uint16_t* As,
+                                            uint16_t* Bs, int tid) {
+#pragma unroll
+    for (int i = 0; i < APER; ++i) {
+        const int q = tid + i * kThreads;
+        *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[i];
+    }
+    if (!AWQ) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + i * kThreads;
+            *reinterpret_cast<uint4*>(&Bs[lds_off(q / 4, q % 4)]) = rb[i];
+        }
+    } else {
+        const int quad = tid % 8, wc = tid / 8;  // rows 4*quad .. +3 of word column wc
+        const int cbase = MODE == MODE_GATEUP ? (wc / 16) * 128 + (wc % 16) * 8 : wc * 8;
+        const uint32_t sw[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
+        uint32_t even[4], odd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // bytes with the code in bits 3..6 and bit 7 set (the exponent LSB)
+            even[i] = ((rw[i] << 3) & 0x78787878u) | 0x80808080u;  // nibbles 0,2,4,6
+            odd[i] = ((rw[i] >> 1) & 0x78787878u) | 0x80808080u;   // nibbles 1,3,5,7
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = awq_perm(j);
+            const float s = f16_to_f32((sw[col / 2] >> (16 * (col % 2))) & 0xFFFFu);
+            const float c = -(16.0f + (float)((rz >> (4 * j)) & 15u)) * s;
+            const uint32_t sel = 0x07000C0Cu | ((uint32_t)(j >> 1) << 16);
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // float bits 0x41 | byte | 00 | 00  ->  16 + q
+                const uint32_t mbits = __builtin_amdgcn_perm(0x41000000u, (j & 1) ? odd[i] : even[i], sel);
+                v[i] = fmaf(__uint_as_float(mbits), s, c);
+            }
+            uint2 out;
+            out.x = pack_bf16x2(v[0], v[1]);
+            out.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(&Bs[lds_off(awq_row(cbase + col), quad / 2) + 4 * (quad % 2)]) = out;
+        }
+    }
+}
+
+// MFMAs of one K step on an LDS stage.
+template <int MODE, bool AWQ, int BM>
+__device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* Bs,
+                                           f32x4_t (&acc)[GemmShape<BM>::TM][GemmShape<BM>::TN],
+                                           int wm, int wn, int lane) {
+    using S = GemmShape<BM>;
+    constexpr int TM = S::TM, TN = S::TN;
+    bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off(wm * S::MW + mi * 16 + lane % 16, lane / 16)]);
+#pragma unroll
+    for (int nj = 0; nj < TN; ++nj) {
+        // gate/up: the wave's first TN/2 tiles are gate columns, the rest the matching up columns
+        const int bcol = MODE == MODE_GATEUP ? (nj / (TN / 2)) * (kBN / 2) + wn * (S::NW / 2) + (nj % (TN / 2)) * 16
+                                             : wn * S::NW + nj * 16;
+        const int brow = AWQ ? awq_row(bcol + lane % 16) : bcol + lane % 16;
+        bfr[nj] = *reinterpret_cast<const bf16x8_t*>(&Bs[lds_off(brow, lane / 16)]);
+    }
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < TN; ++nj)
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
+}
 
 template <int MODE, bool AWQ, int BM>
-__global__ __launch_bounds__(2 * BM) void grouped_gemm_kernel(GroupedArgs a,
-                                                                    const int32_t* __restrict__ tiles,
-                                                                    uint16_t* __restrict__ hbuf,
-                                                                    int NT) {
-    constexpr int kThreads = 2 * BM;  // waves: (BM/64) along rows x 2 along columns
-    constexpr int kBPer = kBN * kBK / 8 / kThreads;  // B items per thread
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kLDK];
-    __shared__ __attribute__((aligned(16))) float2 Ps[2][kBN];  // AWQ (s, -(16+z)s) per column
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GroupedArgs a,
+                                                               const int32_t* __restrict__ tiles,
+                                                               uint16_t* __restrict__ hbuf, int NT) {
+    using S = GemmShape<BM>;
+    constexpr int TM = S::TM, TN = S::TN, APER = S::APER;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kBK];
 
     const int l = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = l / NT, nt = l % NT;
@@ -98,21 +195,19 @@ __global__ __launch_bounds__(2 * BM) void grouped_gemm_kernel(GroupedArgs a,
     const int m1 = a.offsets ? min(m0 + BM, (int)a.offsets[e + 1]) : min(m0 + BM, a.P);
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / S::WN, wn = wave % S::WN;
     const int H = a.H, F = a.F;
-    const int K = MODE == MODE_GATEUP ? H : F;       // reduction dim
-    const int NOUT = MODE == MODE_GATEUP ? F : H;    // output dim of the projection(s)
+    const int K = MODE == MODE_GATEUP ? H : F;     // reduction dim
+    const int NOUT = MODE == MODE_GATEUP ? F : H;  // output dim of the projection(s)
     const int n0 = MODE == MODE_GATEUP ? nt * (kBN / 2) : nt * kBN;
     const int nk = K / kBK;
 
-    // ---- A sources: 2 x 16-byte chunks per thread: chunk q -> row q/4, k-offset (q%4)*8
-    const uint16_t* asrc[2];
-    int arow[2];
+    // ---- A sources: chunk q -> row q/4, k-offset (q%4)*8
+    const uint16_t* asrc[APER];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < APER; ++i) {
         const int q = tid + i * kThreads;
         const int row = q / 4, kc = q % 4;
-        arow[i] = row;
         const int gr = min(m0 + row, m1 - 1);
         if (MODE == MODE_GATEUP) {
             const int t = a.sorted_pair ? a.sorted_pair[gr] / a.k : gr;
@@ -121,181 +216,119 @@ __global__ __launch_bounds__(2 * BM) void grouped_gemm_kernel(GroupedArgs a,
             asrc[i] = hbuf + (size_t)gr * F + kc * 8;
         }
     }
-    // ---- B sources, kBPer items per thread (item u = tid + i*kThreads)
-    // bf16: a 16-byte chunk: B-column bc = u/4, k-offset (u%4)*8
-    // awq : one packed word: k-row kr = u/16, word column wc = u%16
-    const uint16_t* bsrc[kBPer];
-    const int32_t* wsrc[kBPer];
+    // ---- B sources.  bf16: 4 chunks (B-column q/4, k-offset (q%4)*8), q = tid + i*256.
+    // awq: word column wc = tid % 32 (of the 32 words spanning 256 columns), rows
+    // 4*(tid/32) .. +3 of the group.
+    const uint16_t* bsrc[4];
+    const int32_t* wsrc = nullptr;
     const int32_t* zsrc = nullptr;
     const uint16_t* ssrc = nullptr;
-    int pcol = 0;  // AWQ: the B-column whose (s, c) this thread prepares (tid < kBN)
+    int OW = NOUT / 8;
+    if (!AWQ) {
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-        const int u = tid + i * kThreads;
-        if (!AWQ) {
-            const int bc = u / 4, kc = u % 4;
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + i * kThreads;
+            const int bc = q / 4, kc = q % 4;
             const uint16_t* W;
             int col;
             if (MODE == MODE_GATEUP) {
-                W = (bc < kBN / 2 ? a.gate.w : a.up.w) + (size_t)e * F * H;
+                const uint16_t* gw = a.gate.w;
+                const uint16_t* uw = a.up.w;
+                W = (bc < kBN / 2 ? gw : uw) + (size_t)e * F * H;
                 col = n0 + bc % (kBN / 2);
             } else {
                 W = a.down.w + (size_t)e * H * F;
                 col = n0 + bc;
             }
             bsrc[i] = W + (size_t)col * K + kc * 8;
-            wsrc[i] = nullptr;
-        } else {
-            const int kr = u / 16, wc = u % 16;
-            const ProjDev& pj = MODE == MODE_GATEUP ? (wc < 8 ? a.gate : a.up) : a.down;
-            const int OW = NOUT / 8;
-            const int word = MODE == MODE_GATEUP ? n0 / 8 + wc % 8 : n0 / 8 + wc;
-            wsrc[i] = pj.qweight + (size_t)e * K * OW + (size_t)kr * OW + word;
-            bsrc[i] = nullptr;
         }
-    }
-    if (AWQ && tid < kBN) {
-        pcol = tid;
-        const ProjDev& pp = MODE == MODE_GATEUP ? (tid < 64 ? a.gate : a.up) : a.down;
-        const int col = MODE == MODE_GATEUP ? n0 + tid % 64 : n0 + tid;
-        const int OW = NOUT / 8;
-        zsrc = pp.qzeros + (size_t)e * (K / 32) * OW + col / 8;
-        ssrc = pp.scales + (size_t)e * (K / 32) * NOUT + col;
+    } else {
+        const int wc = tid / 8, kr = 4 * (tid % 8);
+        // select by value (a reference into the kernel-argument struct would force a stack copy)
+        const bool up = MODE == MODE_GATEUP && wc >= 16;
+        const int32_t* qw = MODE == MODE_DOWN ? a.down.qweight : (up ? a.up.qweight : a.gate.qweight);
+        const int32_t* qz = MODE == MODE_DOWN ? a.down.qzeros : (up ? a.up.qzeros : a.gate.qzeros);
+        const uint16_t* sc = MODE == MODE_DOWN ? a.down.scales : (up ? a.up.scales : a.gate.scales);
+        const int word = MODE == MODE_GATEUP ? n0 / 8 + wc % 16 : n0 / 8 + wc;
+        wsrc = qw + (size_t)e * K * OW + (size_t)kr * OW + word;
+        zsrc = qz + (size_t)e * (K / 32) * OW + word;
+        ssrc = sc + (size_t)e * (K / 32) * NOUT + 8 * word;
     }
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    uint4 areg[2];
-    uint4 breg[kBPer];
-    uint32_t wreg[kBPer];
+    // register stages: the raw global data of one K step, two in flight
+    // (separately named so that no index into them can become dynamic)
+    uint4 ra0[APER], ra1[APER];
+    uint4 rb0[AWQ ? 1 : 4], rb1[AWQ ? 1 : 4];
+    uint32_t rw0[4], rw1[4];
+    uint32_t rz0 = 0, rz1 = 0;
 
-    auto load_global = [&](int kt) {
-        const int k0 = kt * kBK;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) areg[i] = *reinterpret_cast<const uint4*>(asrc[i] + k0);
-#pragma unroll
-        for (int i = 0; i < kBPer; ++i) {
-            if (!AWQ) breg[i] = *reinterpret_cast<const uint4*>(bsrc[i] + k0);
-            else wreg[i] = (uint32_t)wsrc[i][(size_t)k0 * (NOUT / 8)];
-        }
-    };
-    // AWQ per-column parameters of group kt into Ps[buf]
-    auto make_params = [&](int kt, int buf) {
-        if (AWQ && tid < kBN) {
-            const int OW = NOUT / 8;
-            const uint32_t zw = (uint32_t)zsrc[(size_t)kt * OW];
-            const int c8 = (MODE == MODE_GATEUP ? n0 + pcol % 64 : n0 + pcol) % 8;
-            const float z = (float)((zw >> (4 * awq_nibble_of_col(c8))) & 15u);
-            const float s = f16_to_f32(ssrc[(size_t)kt * NOUT]);
-            Ps[buf][pcol] = make_float2(s, -(16.0f + z) * s);
-        }
-    };
-    auto store_lds = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = tid + i * kThreads;
-            *reinterpret_cast<uint4*>(&As[buf][arow[i] * kLDK + (q % 4) * 8]) = areg[i];
-        }
-#pragma unroll
-        for (int ii = 0; ii < kBPer; ++ii) {
-            const int u = tid + ii * kThreads;
-            if (!AWQ) {
-                const int bc = u / 4, kc = u % 4;
-                *reinterpret_cast<uint4*>(&Bs[buf][bc * kLDK + kc * 8]) = breg[ii];
-            } else {
-                const int kr = u / 16, wc = u % 16;
-                const int cbase = MODE == MODE_GATEUP ? (wc / 8) * 64 + (wc % 8) * 8 : wc * 8;
-                const float4* pv = reinterpret_cast<const float4*>(&Ps[buf][cbase]);
-                float s[8], c[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float4 v = pv[i];
-                    s[2 * i] = v.x; c[2 * i] = v.y; s[2 * i + 1] = v.z; c[2 * i + 1] = v.w;
-                }
-                // bytes with the code in bits 3..6 and bit 7 set (the exponent LSB)
-                const uint32_t even = ((wreg[ii] << 3) & 0x78787878u) | 0x80808080u;  // nibbles 0,2,4,6
-                const uint32_t odd = ((wreg[ii] >> 1) & 0x78787878u) | 0x80808080u;   // nibbles 1,3,5,7
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t src = (j & 1) ? odd : even;
-                    const int b = j >> 1;
-                    // float bits 0x41 | byte | 00 | 00  ->  16 + q
-                    const uint32_t mbits =
-                        __builtin_amdgcn_perm(0x41000000u, src, 0x07000C0Cu | ((uint32_t)b << 16));
-                    const int col = awq_perm(j);
-                    const float w = fmaf(__uint_as_float(mbits), s[col], c[col]);
-                    const __bf16 wb = (__bf16)w;
-                    Bs[buf][(cbase + col) * kLDK + kr] = __builtin_bit_cast(uint16_t, wb);
-                }
-            }
-        }
-    };
+#define MOE_LOAD(RA, RB, RW, RZ, KT)                                                          \
+    do {                                                                                      \
+        const int k0_ = (KT) * kBK;                                                           \
+        _Pragma("unroll") for (int i = 0; i < APER; ++i) RA[i] =                              \
+            *reinterpret_cast<const uint4*>(asrc[i] + k0_);                                   \
+        if (!AWQ) {                                                                           \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) RB[i] =                             \
+                *reinterpret_cast<const uint4*>(bsrc[i] + k0_);                               \
+        } else {                                                                              \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) RW[i] =                             \
+                (uint32_t)wsrc[(size_t)(k0_ + i) * OW];                                       \
+            RZ = (uint32_t)zsrc[(size_t)(KT) * OW];                                           \
+            RB[0] = *reinterpret_cast<const uint4*>(ssrc + (size_t)(KT) * NOUT);              \
+        }                                                                                     \
+    } while (0)
 
-    // prologue: step 0
-    load_global(0);
-    make_params(0, 0);
+    // stage 0 holds the step being written to LDS next, stage 1 the step in flight;
+    // they swap by value each step (register moves, no addressable arrays)
+    MOE_LOAD(ra0, rb0, rw0, rz0, 0);
+    store_stage<MODE, AWQ, APER>(ra0, rb0, rw0, rz0, As[0], Bs[0], tid);
+    if (nk > 1) MOE_LOAD(ra1, rb1, rw1, rz1, 1);
     __syncthreads();
-    store_lds(0);
-
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1, nxt = cur ^ 1;
-        __syncthreads();  // As/Bs[cur] complete; all reads of [nxt] done
-        const bool more = kt + 1 < nk;
-        if (more) {
-            load_global(kt + 1);
-            make_params(kt + 1, nxt);
-        }
-        // MFMA on the current tiles
-        bf16x8_t af[4], bfr[4];
+        const int cur = kt & 1;
+        if (kt + 2 < nk) MOE_LOAD(ra0, rb0, rw0, rz0, kt + 2);  // stage 0 is free: its step is in LDS
+        mfma_stage<MODE, AWQ, BM>(As[cur], Bs[cur], acc, wm, wn, lane);
+        if (kt + 1 < nk) store_stage<MODE, AWQ, APER>(ra1, rb1, rw1, rz1, As[cur ^ 1], Bs[cur ^ 1], tid);
+        __syncthreads();
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-            af[mi] = *reinterpret_cast<const bf16x8_t*>(
-                &As[cur][(wm * 64 + mi * 16 + lane % 16) * kLDK + (lane / 16) * 8]);
+        for (int i = 0; i < APER; ++i) { const uint4 t = ra0[i]; ra0[i] = ra1[i]; ra1[i] = t; }
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) {
-            const int bcol = MODE == MODE_GATEUP ? (nj / 2) * 64 + wn * 32 + (nj % 2) * 16
-                                                 : wn * 64 + nj * 16;
-            bfr[nj] = *reinterpret_cast<const bf16x8_t*>(
-                &Bs[cur][(bcol + lane % 16) * kLDK + (lane / 16) * 8]);
-        }
+        for (int i = 0; i < (AWQ ? 1 : 4); ++i) { const uint4 t = rb0[i]; rb0[i] = rb1[i]; rb1[i] = t; }
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int nj = 0; nj < 4; ++nj)
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
-        if (more) {
-            if (AWQ) __syncthreads();  // Ps[nxt] visible to every thread
-            store_lds(nxt);
-        }
+        for (int i = 0; i < 4; ++i) { const uint32_t t = rw0[i]; rw0[i] = rw1[i]; rw1[i] = t; }
+        { const uint32_t t = rz0; rz0 = rz1; rz1 = t; }
     }
+#undef MOE_LOAD
 
     // ---- epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile
-    const int rbase = m0 + wm * 64 + 4 * (lane / 16);
+    const int rbase = m0 + wm * S::MW + 4 * (lane / 16);
     if (MODE == MODE_GATEUP) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-            for (int nj = 0; nj < 2; ++nj) {
-                const int col = n0 + wn * 32 + nj * 16 + lane % 16;
+            for (int nj = 0; nj < TN / 2; ++nj) {
+                const int col = n0 + wn * (S::NW / 2) + nj * 16 + lane % 16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = rbase + mi * 16 + r;
                     if (row < m1) {
-                        const float g = acc[mi][nj][r], u = acc[mi][nj + 2][r];
+                        const float g = acc[mi][nj][r], u = acc[mi][nj + TN / 2][r];
                         hbuf[(size_t)row * F + col] = (uint16_t)f32_to_bf16_bits(silu(g) * u);
                     }
                 }
             }
     } else {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-            for (int nj = 0; nj < 4; ++nj) {
-                const int col = n0 + wn * 64 + nj * 16 + lane % 16;
+            for (int nj = 0; nj < TN; ++nj) {
+                const int col = n0 + wn * S::NW + nj * 16 + lane % 16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = rbase + mi * 16 + r;
@@ -322,25 +355,25 @@ static int pick_bm(int P, int E) {
     return avg >= 192 ? 256 : (avg >= 96 ? 128 : 64);
 }
 
-size_t gemm_ws_bytes(int P, int F, int E) {
-    const size_t tiles = (size_t)(1 + 2 * max_tiles(P, E, 64)) * sizeof(int32_t);
-    const size_t tiles_al = (tiles + 255) & ~(size_t)255;
-    return tiles_al + (size_t)P * F * sizeof(uint16_t);
+static size_t tiles_bytes(int P, int E) {
+    return (((size_t)(1 + 2 * max_tiles(P, E, 64)) * sizeof(int32_t)) + 255) & ~(size_t)255;
 }
+
+size_t gemm_ws_bytes(int P, int F, int E) { return tiles_bytes(P, E) + (size_t)P * F * sizeof(uint16_t); }
 
 template <int BM>
 static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int mt,
                            hipStream_t s) {
     const int NT1 = a.F / (kBN / 2), NT2 = a.H / kBN;
     if (a.awq) {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, true, BM>), dim3(mt * NT1), dim3(2 * BM), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, true, BM>), dim3(mt * NT1), dim3(kThreads), 0,
                            s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, true, BM>), dim3(mt * NT2), dim3(2 * BM), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, true, BM>), dim3(mt * NT2), dim3(kThreads), 0,
                            s, a, tiles, hbuf, NT2);
     } else {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, false, BM>), dim3(mt * NT1), dim3(2 * BM), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, false, BM>), dim3(mt * NT1), dim3(kThreads), 0,
                            s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, BM>), dim3(mt * NT2), dim3(2 * BM), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, BM>), dim3(mt * NT2), dim3(kThreads), 0,
                            s, a, tiles, hbuf, NT2);
     }
 }
@@ -350,13 +383,49 @@ hipError_t launch_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
     const int BM = pick_bm(a.P, E);
     const int mt = max_tiles(a.P, E, BM);
     int32_t* tiles = static_cast<int32_t*>(ws);
-    const size_t tiles_al =
-        (((size_t)(1 + 2 * max_tiles(a.P, E, 64)) * sizeof(int32_t)) + 255) & ~(size_t)255;
-    uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + tiles_al);
+    uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + tiles_bytes(a.P, E));
     hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, BM, tiles);
     if (BM == 256) launch_gemm_bm<256>(a, tiles, hbuf, mt, s);
     else if (BM == 128) launch_gemm_bm<128>(a, tiles, hbuf, mt, s);
     else launch_gemm_bm<64>(a, tiles, hbuf, mt, s);
+    return hipGetLastError();
+}
+
+// Dense C[M][N] (fp32) = A[M][K] (bf16, rows) x B[N][K]^T (bf16, rows): the
+// grouped GEMM's down pass with one group and identity rows.
+size_t dense_gemm_ws_bytes(int M) { return tiles_bytes(M, 1); }
+
+hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t* B, int N, float* C,
+                                 void* ws, hipStream_t s) {
+    GroupedArgs a{};
+    a.T = M;
+    a.k = 1;
+    a.P = M;
+    a.F = K;  // reduction dim of the down pass
+    a.H = N;  // its output dim
+    a.E = 1;
+    a.awq = 0;
+    a.offsets = nullptr;
+    a.sorted_pair = nullptr;
+    a.down.w = B;
+    a.out_f32 = 1;
+    a.rows = C;
+    const int BM = pick_bm(M, 1);
+    const int mt = max_tiles(M, 1, BM);
+    int32_t* tiles = static_cast<int32_t*>(ws);
+    uint16_t* Ain = const_cast<uint16_t*>(A);
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, (const int32_t*)nullptr, 1, M, BM,
+                       tiles);
+    const int NT = N / kBN;
+    if (BM == 256)
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 256>), dim3(mt * NT), dim3(kThreads), 0,
+                           s, a, tiles, Ain, NT);
+    else if (BM == 128)
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 128>), dim3(mt * NT), dim3(kThreads), 0,
+                           s, a, tiles, Ain, NT);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 64>), dim3(mt * NT), dim3(kThreads), 0,
+                           s, a, tiles, Ain, NT);
     return hipGetLastError();
 }
 

@@ -81,6 +81,21 @@ __device__ __forceinline__ void awq_gemv_groups(const int32_t* __restrict__ qw,
     }
 }
 
+template <int R>
+struct RowsTag {
+    static constexpr int value = R;
+};
+
+// Calls body(RowsTag<R>) with the smallest R in {1, 2, 4, RCH} that covers nr
+// rows, so that experts with one or two rows do not pay for RCH.
+template <int RCH, class Body>
+__device__ __forceinline__ void dispatch_rows(int nr, Body&& body) {
+    if (nr <= 1) body(RowsTag<1>{});
+    else if (nr <= 2 || RCH < 4) body(RowsTag<(RCH < 2 ? RCH : 2)>{});
+    else if (nr <= 4 || RCH < 8) body(RowsTag<(RCH < 4 ? RCH : 4)>{});
+    else body(RowsTag<RCH>{});
+}
+
 // Group sums of the staged activation pairs.
 template <int RCH>
 __device__ __forceinline__ void stage_group_sums(const uint32_t* xs, int npairs, int ngroups,
@@ -151,14 +166,17 @@ __global__ __launch_bounds__(512) void awq_gateup_kernel(GroupedArgs a, int KS, 
         __syncthreads();
         stage_group_sums<RCH>(xs, npairs, ng, xsum);
         __syncthreads();
-        float res[8][RCH];
+        auto body = [&](auto rtag) {
+            constexpr int R = decltype(rtag)::value;
+            float res[8][R];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int i = 0; i < RCH; ++i) res[j][i] = 0.0f;
-        if (rp < RP)
-            awq_gemv_groups<RCH>(qw, qz, sc, F, OW, c, g0, g0 + rp, g1, RP, xs, npairs, xsum, ng, res);
-        reduce_phases<RCH>(res, c, rp < RP ? rp : RP, RP, F, red);
+                for (int i = 0; i < R; ++i) res[j][i] = 0.0f;
+            awq_gemv_groups<R>(qw, qz, sc, F, OW, c, g0, g0 + rp, g1, RP, xs, npairs, xsum, ng, res);
+            reduce_phases<R>(res, c, rp, RP, F, red);
+        };
+        dispatch_rows<RCH>(nr, body);
         for (int it = threadIdx.x; it < nr * F; it += blockDim.x) {
             const int i = it / F, col = it % F;
             part[((size_t)ks * a.P + rc + i) * (2 * F) + mat * F + col] = red[i * F + col];
@@ -167,14 +185,38 @@ __global__ __launch_bounds__(512) void awq_gateup_kernel(GroupedArgs a, int KS, 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 gate/up: grid (expert slot, F/32 column chunks); block 256 (4 waves).
-// Waves 0,1: gate columns c0..c0+31, waves 2,3: up.  16 lanes per weight row.
-// part[0][r][mat*F + col].
+// bf16 gate/up: grid (expert slot, F/32 column chunks, KS input splits);
+// block 256 (4 waves).  Waves 0,1: gate columns c0..c0+31, waves 2,3: up.
+// 16 lanes per weight row.  part[ks][r][mat*F + col].
 // ---------------------------------------------------------------------------
 constexpr int kBfChunkK = 2048;
 
+template <int R>
+__device__ __forceinline__ void bf16_rows_dot(const uint16_t* __restrict__ W, int H, int k0, int nv,
+                                              int c0, int wave, int sub, int l16, const uint4* xs,
+                                              float (&acc)[4][8]) {
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+        const int col = c0 + (wave % 2) * 16 + ps * 4 + sub;
+        const uint4* wr = reinterpret_cast<const uint4*>(W + (size_t)col * H + k0);
+        for (int v = l16; v < nv; v += 16) {
+            const uint4 w = wr[v];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint4 xv = xs[i * (kBfChunkK / 8) + v];
+                float t = acc[ps][i];
+                t = dot2_bf16(w.x, xv.x, t);
+                t = dot2_bf16(w.y, xv.y, t);
+                t = dot2_bf16(w.z, xv.z, t);
+                t = dot2_bf16(w.w, xv.w, t);
+                acc[ps][i] = t;
+            }
+        }
+    }
+}
+
 template <int RCH>
-__global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, float* __restrict__ part) {
+__global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, int KS, float* __restrict__ part) {
     __shared__ uint4 xs[RCH * kBfChunkK / 8];
     __shared__ float outv[64][RCH];
     int r0, r1;
@@ -182,6 +224,8 @@ __global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, float* 
     if (!a.offsets) { r0 = 0; r1 = a.T; }
     if (e < 0) return;
     const int H = a.H, F = a.F;
+    const int ks = blockIdx.z;
+    const int kb = (int)((long)H / 8 * ks / KS) * 8, ke = (int)((long)H / 8 * (ks + 1) / KS) * 8;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int sub = lane / 16, l16 = lane % 16;  // 4 rows per pass, 16 lanes each
     const int c0 = blockIdx.y * 32;
@@ -189,42 +233,25 @@ __global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, float* 
     const uint16_t* W = (mat ? a.up.w : a.gate.w) + (size_t)e * F * H;
     for (int rc = r0; rc < r1; rc += RCH) {
         const int nr = min(RCH, r1 - rc);
-        float acc[4][RCH];
+        float acc[4][8];
 #pragma unroll
         for (int ps = 0; ps < 4; ++ps)
 #pragma unroll
-            for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
-        for (int k0 = 0; k0 < H; k0 += kBfChunkK) {
-            const int kl = min(kBfChunkK, H - k0), nv = kl / 8;
+            for (int i = 0; i < 8; ++i) acc[ps][i] = 0.0f;
+        for (int k0 = kb; k0 < ke; k0 += kBfChunkK) {
+            const int kl = min(kBfChunkK, ke - k0), nv = kl / 8;
             __syncthreads();
-            for (int it = threadIdx.x; it < RCH * nv; it += blockDim.x) {
+            for (int it = threadIdx.x; it < nr * nv; it += blockDim.x) {
                 const int i = it / nv, v = it % nv;
-                uint4 val = make_uint4(0, 0, 0, 0);
-                if (i < nr) {
-                    const int t = row_token(a.sorted_pair, a.k, rc + i);
-                    val = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + k0)[v];
-                }
-                xs[i * (kBfChunkK / 8) + v] = val;
+                const int t = row_token(a.sorted_pair, a.k, rc + i);
+                xs[i * (kBfChunkK / 8) + v] = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + k0)[v];
             }
             __syncthreads();
-#pragma unroll
-            for (int ps = 0; ps < 4; ++ps) {
-                const int col = c0 + (wave % 2) * 16 + ps * 4 + sub;
-                const uint4* wr = reinterpret_cast<const uint4*>(W + (size_t)col * H + k0);
-                for (int v = l16; v < nv; v += 16) {
-                    const uint4 w = wr[v];
-#pragma unroll
-                    for (int i = 0; i < RCH; ++i) {
-                        const uint4 xv = xs[i * (kBfChunkK / 8) + v];
-                        float s = acc[ps][i];
-                        s = dot2_bf16(w.x, xv.x, s);
-                        s = dot2_bf16(w.y, xv.y, s);
-                        s = dot2_bf16(w.z, xv.z, s);
-                        s = dot2_bf16(w.w, xv.w, s);
-                        acc[ps][i] = s;
-                    }
-                }
-            }
+            auto body = [&](auto rtag) {
+                constexpr int R = decltype(rtag)::value;
+                bf16_rows_dot<R>(W, H, k0, nv, c0, wave, sub, l16, xs, acc);
+            };
+            dispatch_rows<RCH>(nr, body);
         }
 #pragma unroll
         for (int ps = 0; ps < 4; ++ps)
@@ -241,7 +268,7 @@ __global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, float* 
         for (int it = threadIdx.x; it < 64 * nr; it += blockDim.x) {
             const int o = it % 64, i = it / 64;
             const int m = o / 32, col = c0 + o % 32;
-            part[((size_t)rc + i) * (2 * F) + m * F + col] = outv[o][i];
+            part[((size_t)ks * a.P + rc + i) * (2 * F) + m * F + col] = outv[o][i];
         }
     }
 }
@@ -296,13 +323,17 @@ __global__ __launch_bounds__(512) void awq_down_kernel(GroupedArgs a, int KS, in
         __syncthreads();
         stage_group_sums<RCH>(xs, npairs, G, xsum);
         __syncthreads();
-        float res[8][RCH];
+        auto body = [&](auto rtag) {
+            constexpr int R = decltype(rtag)::value;
+            float res[8][R];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int i = 0; i < RCH; ++i) res[j][i] = 0.0f;
-        awq_gemv_groups<RCH>(qw, qz, sc, H, OW, c, 0, rp, G, RP, xs, npairs, xsum, G, res);
-        reduce_phases<RCH>(res, cl, rp, RP, 8 * OWC, red);
+                for (int i = 0; i < R; ++i) res[j][i] = 0.0f;
+            awq_gemv_groups<R>(qw, qz, sc, H, OW, c, 0, rp, G, RP, xs, npairs, xsum, G, res);
+            reduce_phases<R>(res, cl, rp, RP, 8 * OWC, red);
+        };
+        dispatch_rows<RCH>(nr, body);
         const int ncol = 8 * OWC;
         for (int it = threadIdx.x; it < nr * ncol; it += blockDim.x) {
             const int i = it / ncol, col = it % ncol;
@@ -315,21 +346,48 @@ __global__ __launch_bounds__(512) void awq_down_kernel(GroupedArgs a, int KS, in
 }
 
 // ---------------------------------------------------------------------------
-// bf16 down: grid (expert slot, H/64 row chunks); block 256; 16 lanes per row.
+// bf16 down: grid (expert slot, H/(16*npass) row chunks); block 256; 16 lanes
+// per weight row; each WG covers 16*npass output rows.
 // ---------------------------------------------------------------------------
-template <int RCH>
+template <int R, int NPASS>
+__device__ __forceinline__ void bf16_down_dot(const uint16_t* __restrict__ W, int F, int o0,
+                                              int wave, int sub, int l16, const uint4* hv,
+                                              float (&acc)[4][8]) {
+    const int nv = F / 8;
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+        const int o = o0 + ps * 16 + wave * 4 + sub;
+        const uint4* wr = reinterpret_cast<const uint4*>(W + (size_t)o * F);
+        for (int v = l16; v < nv; v += 16) {
+            const uint4 w = wr[v];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint4 xv = hv[i * (F / 8) + v];
+                float t = acc[ps][i];
+                t = dot2_bf16(w.x, xv.x, t);
+                t = dot2_bf16(w.y, xv.y, t);
+                t = dot2_bf16(w.z, xv.z, t);
+                t = dot2_bf16(w.w, xv.w, t);
+                acc[ps][i] = t;
+            }
+        }
+    }
+}
+
+template <int RCH, int NPASS>
 __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
                                                         const float* __restrict__ part) {
+    constexpr int npass = NPASS;
     __shared__ uint32_t h2[RCH * kGemvMaxKPairs];
     __shared__ float outv[64][RCH];
     int r0, r1;
     const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
     if (!a.offsets) { r0 = 0; r1 = a.T; }
     if (e < 0) return;
-    const int H = a.H, F = a.F, nv = F / 8;
+    const int H = a.H, F = a.F;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int sub = lane / 16, l16 = lane % 16;
-    const int o0 = blockIdx.y * 64;
+    const int o0 = blockIdx.y * 16 * npass;
     const uint16_t* W = a.down.w + (size_t)e * H * F;
     const uint4* hv = reinterpret_cast<const uint4*>(h2);
     for (int rc = r0; rc < r1; rc += RCH) {
@@ -337,29 +395,16 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
         __syncthreads();
         stage_swiglu<RCH>(part, KS, a.P, F, rc, nr, h2);
         __syncthreads();
-        float acc[4][RCH];
+        float acc[4][8];
 #pragma unroll
         for (int ps = 0; ps < 4; ++ps)
 #pragma unroll
-            for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
-#pragma unroll
-        for (int ps = 0; ps < 4; ++ps) {
-            const int o = o0 + wave * 16 + ps * 4 + sub;
-            const uint4* wr = reinterpret_cast<const uint4*>(W + (size_t)o * F);
-            for (int v = l16; v < nv; v += 16) {
-                const uint4 w = wr[v];
-#pragma unroll
-                for (int i = 0; i < RCH; ++i) {
-                    const uint4 xv = hv[i * (F / 8) + v];
-                    float s = acc[ps][i];
-                    s = dot2_bf16(w.x, xv.x, s);
-                    s = dot2_bf16(w.y, xv.y, s);
-                    s = dot2_bf16(w.z, xv.z, s);
-                    s = dot2_bf16(w.w, xv.w, s);
-                    acc[ps][i] = s;
-                }
-            }
-        }
+            for (int i = 0; i < 8; ++i) acc[ps][i] = 0.0f;
+        auto body = [&](auto rtag) {
+            constexpr int R = decltype(rtag)::value;
+            bf16_down_dot<R, NPASS>(W, F, o0, wave, sub, l16, hv, acc);
+        };
+        dispatch_rows<RCH>(nr, body);
 #pragma unroll
         for (int ps = 0; ps < 4; ++ps)
 #pragma unroll
@@ -369,11 +414,12 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
                 v += __shfl_xor(v, 2, kWave);
                 v += __shfl_xor(v, 4, kWave);
                 v += __shfl_xor(v, 8, kWave);
-                if (l16 == 0) outv[wave * 16 + ps * 4 + sub][i] = v;
+                if (l16 == 0 && ps < npass) outv[ps * 16 + wave * 4 + sub][i] = v;
             }
         __syncthreads();
-        for (int it = threadIdx.x; it < 64 * nr; it += blockDim.x) {
-            const int o = it % 64, i = it / 64;
+        const int nrows = 16 * npass;
+        for (int it = threadIdx.x; it < nrows * nr; it += blockDim.x) {
+            const int o = it % nrows, i = it / nrows;
             const size_t idx = (size_t)(rc + i) * H + o0 + o;
             const float v = outv[o][i];
             if (a.out_f32) static_cast<float*>(a.rows)[idx] = v;
@@ -385,8 +431,17 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+// Input splits of the gate/up pass.  AWQ: groups per workgroup bounded by the
+// LDS activation stage (16 groups at H = 2560).  bf16: enough workgroups when
+// few experts are active (the shared expert is a single expert).
 int gemv_ksplit(const GroupedArgs& a) {
-    if (!a.awq) return 1;
+    if (!a.awq) {
+        const int slots = a.offsets ? (a.P < a.E ? a.P : a.E) : 1;
+        const long wgs = (long)slots * (a.F / 32);
+        int ks = 1;
+        while (wgs * ks < 1024 && ks < 8 && (a.H / 8) % (ks * 2) == 0) ks *= 2;
+        return ks;
+    }
     const int G = a.H / 32;
     int ks = 5;                            // 16 groups per workgroup at H = 2560
     while (ks > 1 && G % ks) --ks;
@@ -395,6 +450,7 @@ int gemv_ksplit(const GroupedArgs& a) {
 }
 
 size_t gemv_ws_bytes(int P, int H, int F, int awq) {
+    if (!awq) return (size_t)8 * P * 2 * F * sizeof(float);  // at most 8 splits
     GroupedArgs a{};
     a.H = H;
     a.awq = awq;
@@ -434,9 +490,16 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, float* part, hipStream_t
                            (size_t)RCH * 8 * OWC * sizeof(float), s, a, KS, OWC,
                            (const float*)part);
     } else {
-        hipLaunchKernelGGL(bf16_gateup_kernel<RCH>, dim3(slots, F / 32), dim3(256), 0, s, a, part);
-        hipLaunchKernelGGL(bf16_down_kernel<RCH>, dim3(slots, H / 64), dim3(256), 0, s, a, 1,
-                           (const float*)part);
+        const int KS = gemv_ksplit(a);
+        hipLaunchKernelGGL(bf16_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS,
+                           part);
+        // rows per down workgroup: 64, or 16 when few experts are active
+        if ((long)slots * (H / 64) >= 1024)
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4>), dim3(slots, H / 64), dim3(256), 0, s, a, KS,
+                               (const float*)part);
+        else
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1>), dim3(slots, H / 16), dim3(256), 0, s, a, KS,
+                               (const float*)part);
     }
     return hipGetLastError();
 }

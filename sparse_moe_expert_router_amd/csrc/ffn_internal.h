@@ -37,6 +37,11 @@ hipError_t launch_gemv(const GroupedArgs& a, void* ws, hipStream_t s);
 size_t gemm_ws_bytes(int P, int F, int E);
 hipError_t launch_gemm(const GroupedArgs& a, void* ws, hipStream_t s);
 
+// Dense fp32 GEMM on the same kernels (used by the router's screening pass).
+size_t dense_gemm_ws_bytes(int M);
+hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t* B, int N, float* C,
+                                 void* ws, hipStream_t s);
+
 // Find the expert of work slot `slot` among the non-empty experts of
 // offsets[0..E] (slot-th non-empty expert in index order).  Block-wide; every
 // thread gets the same answer.  Returns -1 when there is no such expert.

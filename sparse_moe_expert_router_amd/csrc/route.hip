@@ -8,6 +8,7 @@
 // final fp64 -> fp32 rounding reproduces that value unless an fp64 addition
 // rounded AND the sum lies within an fp64 rounding error of an fp32 tie point.
 #include "common.h"
+#include "ffn_internal.h"
 #include "kernels.h"
 
 namespace moe {
@@ -177,6 +178,250 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int extra, int3
         hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, T, E, K, k, idx, topk_logit, gate);
     else
         hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, T, E, K, k, idx, topk_logit, gate);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Screened routing for many tokens.
+//
+// 1. Approximate logits la = x . w (bf16 MFMA, fp32 accumulation) for all
+//    (token, expert) pairs.
+// 2. A bound on |la - l| that holds for any order of fp32 accumulation inside
+//    the MFMA: each K-step of 32 products adds at most 16 ulp-units
+//    (2^-20) of (|partial sum| + sum |products|), over S = H/32 steps:
+//      |la - l| <= 2^-20 (S + 1) sum_h |x_h w_h| + H 2^-100
+//               <= 2^-20 (S + 1) ||x|| ||w_e|| + H 2^-100      (Cauchy-Schwarz).
+//    Products of bf16 values are exact in fp32; the absolute term covers
+//    flushed denormal products.
+// 3. Experts whose upper bound reaches the K-th largest lower bound are the
+//    only ones that can be in the exact top K; their logits are recomputed
+//    exactly (fp64 FMAs, one fp32 rounding) and ranked exactly.  When more
+//    than 64 experts qualify (near-degenerate logits) the token is recomputed
+//    for all experts.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void row_norms_kernel(const uint16_t* __restrict__ w, int E, int H,
+                                                        double* __restrict__ norm) {
+    const int lane = threadIdx.x % kWave;
+    const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (e >= E) return;
+    double s = 0.0;
+    for (int h = lane; h < H; h += kWave) {
+        const double v = (double)bf16_to_f32(w[(size_t)e * H + h]);
+        s = fma(v, v, s);
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) s += shfl_xor_f64(s, m);
+    if (lane == 0) norm[e] = sqrt(s) * (1.0 + 1e-12);
+}
+
+// Exact fp32 logit of one (token, expert): fp64 FMAs over the wave, one rounding.
+__device__ __forceinline__ float wave_exact_logit(const uint16_t* __restrict__ xr,
+                                                  const uint16_t* __restrict__ wr, int H) {
+    const int lane = threadIdx.x % kWave;
+    double acc = 0.0;
+    for (int c = lane; c < H / 8; c += kWave) {
+        const uint4 x4 = reinterpret_cast<const uint4*>(xr)[c];
+        const uint4 w4 = reinterpret_cast<const uint4*>(wr)[c];
+        const uint32_t xx[4] = {x4.x, x4.y, x4.z, x4.w};
+        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = fma((double)bf16_to_f32(xx[i] & 0xFFFFu), (double)bf16_to_f32(ww[i] & 0xFFFFu), acc);
+            acc = fma((double)bf16_to_f32(xx[i] >> 16), (double)bf16_to_f32(ww[i] >> 16), acc);
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) acc += shfl_xor_f64(acc, m);
+    return (float)acc;
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void route_refine_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ la,
+    const double* __restrict__ wnorm, int T, int H, int E, int K, int k, int32_t* __restrict__ idx,
+    float* __restrict__ topk_logit, float* __restrict__ gate) {
+    __shared__ int cand[4][kWave];
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;  // whole wave; no block barrier below
+    const uint16_t* xr = x + (size_t)t * H;
+    float* lrow = la + (size_t)t * E;
+
+    // ||x_t|| (fp64) and the bound factor
+    double xs = 0.0;
+    for (int h = lane; h < H; h += kWave) {
+        const double v = (double)bf16_to_f32(xr[h]);
+        xs = fma(v, v, xs);
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) xs += shfl_xor_f64(xs, m);
+    const double S = (double)((H + 31) / 32);
+    const double fac = ldexp(S + 1.0, -20) * sqrt(xs) * (1.0 + 1e-12);
+    const double dabs = (double)H * ldexp(1.0, -100);
+
+    double lo[VPL], hi[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int e = v * kWave + lane;
+        if (e < E) {
+            const double d = fac * wnorm[e] + dabs;
+            const double l = (double)lrow[e];
+            lo[v] = l - d;
+            hi[v] = l + d;
+        } else {
+            lo[v] = -INFINITY;
+            hi[v] = -INFINITY;
+        }
+    }
+    // K-th largest lower bound (K rounds of a wave max, removing one entry each)
+    double tau = 0.0;
+    {
+        double tmp[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) tmp[v] = lo[v];
+        for (int r = 0; r < K; ++r) {
+            double best = -INFINITY;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int e = v * kWave + lane;
+                if (tmp[v] > best || (tmp[v] == best && e < bi)) { best = tmp[v]; bi = e; }
+            }
+#pragma unroll
+            for (int m = 1; m < kWave; m <<= 1) {
+                const double ob = __shfl_xor(best, m, kWave);
+                const int oi = __shfl_xor(bi, m, kWave);
+                if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+            }
+#pragma unroll
+            for (int v = 0; v < VPL; ++v)
+                if (v * kWave + lane == bi) tmp[v] = -INFINITY;
+            tau = best;
+        }
+    }
+    // candidates: hi >= tau
+    int ncand = 0;
+    bool overflow = false;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const bool c = (v * kWave + lane < E) && hi[v] >= tau;
+        const uint64_t m = __ballot(c);
+        const int n = __popcll(m);
+        if (!overflow && ncand + n <= kWave) {
+            if (c) cand[wv][ncand + __popcll(m & ((1ull << lane) - 1ull))] = v * kWave + lane;
+        } else {
+            overflow = true;
+        }
+        ncand += n;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (ncand > kWave) overflow = true;
+
+    uint64_t key = 0;  // this lane's candidate (or nothing)
+    if (!overflow) {
+        float mine = 0.0f;
+        for (int j = 0; j < ncand; ++j) {
+            const int e = cand[wv][j];
+            const float l = wave_exact_logit(xr, wr + (size_t)e * H, H);
+            if (lane == j) mine = l;
+        }
+        if (lane < ncand) {
+            const int e = cand[wv][lane];
+            key = ((uint64_t)float_order_key(mine) << 32) | (uint32_t)(~e);
+        }
+        int my_e = 0;
+        float my_l = 0.0f;
+        for (int r = 0; r < K; ++r) {
+            const uint64_t best = wave_max_u64(key);
+            const int e = (int)(~(uint32_t)best);
+            if (key == best) key = 0;
+            if (lane == r) {
+                my_e = e;
+                my_l = float_from_order_key((uint32_t)(best >> 32));
+            }
+        }
+        if (lane < K) {
+            idx[(size_t)t * K + lane] = my_e;
+            if (topk_logit) topk_logit[(size_t)t * K + lane] = my_l;
+        }
+        if (gate) {
+            const float l0 = __shfl(my_l, 0, kWave);
+            const float p = lane < k ? expf(my_l - l0) : 0.0f;
+            const float z = wave_sum_f32(p);
+            if (lane < k) gate[(size_t)t * k + lane] = p / z;
+        }
+        return;
+    }
+    // fallback: every logit of this token exactly (kept in the owning lane's
+    // registers), then the plain top-K
+    uint64_t keys[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) keys[v] = 0;
+    for (int e = 0; e < E; ++e) {
+        const float l = wave_exact_logit(xr, wr + (size_t)e * H, H);
+        const uint64_t kk = ((uint64_t)float_order_key(l) << 32) | (uint32_t)(~e);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            if (v * kWave + lane == e) keys[v] = kk;
+    }
+    int my_e = 0;
+    float my_l = 0.0f;
+    for (int r = 0; r < K; ++r) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) best = keys[v] > best ? keys[v] : best;
+        best = wave_max_u64(best);
+        const int e = (int)(~(uint32_t)best);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            if (v * kWave + lane == e) keys[v] = 0;
+        if (lane == r) {
+            my_e = e;
+            my_l = float_from_order_key((uint32_t)(best >> 32));
+        }
+    }
+    if (lane < K) {
+        idx[(size_t)t * K + lane] = my_e;
+        if (topk_logit) topk_logit[(size_t)t * K + lane] = my_l;
+    }
+    if (gate) {
+        const float l0 = __shfl(my_l, 0, kWave);
+        const float p = lane < k ? expf(my_l - l0) : 0.0f;
+        const float z = wave_sum_f32(p);
+        if (lane < k) gate[(size_t)t * k + lane] = p / z;
+    }
+}
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t route_filter_ws_bytes(int T, int E, int H) {
+    (void)H;
+    return align256((size_t)T * E * sizeof(float)) + align256((size_t)E * sizeof(double)) +
+           dense_gemm_ws_bytes(T);
+}
+
+hipError_t launch_route_filter(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
+                               int extra, int32_t* idx, float* topk_logit, float* gate, void* ws,
+                               hipStream_t s) {
+    char* p = static_cast<char*>(ws);
+    float* la = reinterpret_cast<float*>(p);
+    p += align256((size_t)T * E * sizeof(float));
+    double* wn = reinterpret_cast<double*>(p);
+    p += align256((size_t)E * sizeof(double));
+    hipLaunchKernelGGL(row_norms_kernel, dim3((E + 3) / 4), dim3(256), 0, s, wr, E, H, wn);
+    hipError_t err = launch_dense_gemm_f32(x, T, H, wr, E, la, p, s);
+    if (err != hipSuccess) return err;
+    const int K = k + extra;
+    const int vpl = (E + kWave - 1) / kWave;
+    dim3 grid((T + 3) / 4), block(256);
+#define MOE_REFINE(V) \
+    hipLaunchKernelGGL(route_refine_kernel<V>, grid, block, 0, s, x, wr, la, wn, T, H, E, K, k, idx, \
+                       topk_logit, gate)
+    if (vpl <= 2) MOE_REFINE(2);
+    else if (vpl <= 4) MOE_REFINE(4);
+    else if (vpl <= 8) MOE_REFINE(8);
+    else MOE_REFINE(16);
+#undef MOE_REFINE
     return hipGetLastError();
 }
 

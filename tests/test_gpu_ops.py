@@ -43,6 +43,43 @@ def test_route_matches_oracle(T, H, E, k, extra):
     np.testing.assert_array_equal(gate.cpu().numpy(), gate2.cpu().numpy())
 
 
+@pytest.mark.parametrize("T,H,E,k,extra", [(4096, 2560, 512, 10, 0), (2000, 2560, 256, 10, 1),
+                                           (64, 256, 256, 8, 1), (517, 512, 1024, 20, 0)])
+def test_route_screened_matches_oracle(T, H, E, k, extra):
+    """Batches of >= 64 tokens with E % 256 == 0 take the screened path."""
+    moe = require_gpu()
+    w = _wl(T, H, E)
+    x = workloads.activations(w, seed=5, device="cuda")
+    wr = workloads.router(w, seed=5, device="cuda")
+    idx, tl, gate, _ = moe.route(x, wr, k, extra)
+    torch.cuda.synchronize()
+    ref_l, _ = O.router_logits(bits(x), bits(wr))
+    ref_idx = O.rank(ref_l, k + extra)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(tl.cpu().numpy(), np.take_along_axis(ref_l, ref_idx, 1))
+    np.testing.assert_allclose(gate.cpu().numpy(), O.gates(ref_l, ref_idx, k), rtol=1e-5, atol=1e-7)
+
+
+def test_route_screened_ties_and_degenerate_tokens():
+    """Exact ties between router rows, and tokens whose logits are all equal
+    (every expert is a candidate: the per-token fallback)."""
+    moe = require_gpu()
+    w = _wl(256, 512, 256)
+    x = workloads.activations(w, seed=6, device="cuda")
+    wr = workloads.router(w, seed=6, device="cuda")
+    for dst, src in ((9, 4), (100, 4), (200, 17), (201, 17)):
+        wr[dst] = wr[src]
+    x[5] = 0          # all logits 0: top-k = lowest indices
+    x[6] = x[7]
+    idx, tl, gate, _ = moe.route(x, wr, 10, 1)
+    torch.cuda.synchronize()
+    ref_l, _ = O.router_logits(bits(x), bits(wr))
+    ref_idx = O.rank(ref_l, 11)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(idx.cpu().numpy()[5], np.arange(11))
+    np.testing.assert_allclose(gate.cpu().numpy()[5], 0.1, rtol=1e-6)
+
+
 def test_route_ties_take_lowest_index():
     moe = require_gpu()
     w = _wl(40, 128, 32)
