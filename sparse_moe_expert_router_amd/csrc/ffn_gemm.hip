@@ -46,7 +46,6 @@ __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 32 + (
 // AWQ B tiles store B-column c at LDS row c ^ ((c >> 3) & 3): the 8-byte stores
 // of four adjacent packed words (columns 8 apart) then land in four different
 // row classes.  The permutation stays inside aligned groups of 8 columns.
-constexpr int kThreads = 256;
 constexpr int kXcd = 8;
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
@@ -97,69 +96,99 @@ __device__ __forceinline__ int awq_row(int c) { return c ^ ((c >> 3) & 3); }
 template <int BM>
 struct GemmShape {
     static constexpr int WM = BM == 256 ? 2 : 1;  // waves along rows
-    static constexpr int WN = 4 / WM;             // waves along columns
+    static constexpr int WN = 4;                  // waves along columns
+    static constexpr int NT = WM * WN * kWave;    // threads
     static constexpr int MW = BM / WM;            // rows per wave
     static constexpr int NW = kBN / WN;           // B-columns per wave
     static constexpr int TM = MW / 16, TN = NW / 16;
-    static constexpr int APER = BM * 4 / kThreads;  // 16-byte A chunks per thread per step
+    static constexpr int APER = BM * 4 / NT;      // 16-byte A chunks per thread per step
+    static constexpr int BPER = kBN * 4 / NT;     // 16-byte bf16 B chunks per thread per step
+    static constexpr int RPT = 1024 / NT;         // AWQ: input rows per thread per step (one word column)
 };
 
+// Dequantise word column rows of one AWQ B job (RPT consecutive input rows of
+// one packed word) and store column j (nibble j) into the K-major LDS tile.
+template <int MODE, int RPT>
+__device__ __forceinline__ void awq_store_col(int j, const uint32_t (&even)[RPT], const uint32_t (&odd)[RPT],
+                                              const uint32_t (&sw)[4], uint32_t rz, uint16_t* Bs, int cbase,
+                                              int sub) {
+    const int col = awq_perm(j);
+    const float sc = f16_to_f32((sw[col / 2] >> (16 * (col % 2))) & 0xFFFFu);
+    const float c = -(16.0f + (float)((rz >> (4 * j)) & 15u)) * sc;
+    const uint32_t sel = 0x07000C0Cu | ((uint32_t)(j >> 1) << 16);
+    float v[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        // float bits 0x41 | byte | 00 | 00  ->  16 + q
+        const uint32_t mbits = __builtin_amdgcn_perm(0x41000000u, (j & 1) ? odd[i] : even[i], sel);
+        v[i] = fmaf(__uint_as_float(mbits), sc, c);
+    }
+    const int k0 = RPT * sub;  // first input row of the job within the step
+    uint16_t* dst = &Bs[lds_off(awq_row(cbase + col), k0 / 8) + k0 % 8];
+    if (RPT == 4) {
+        uint2 out;
+        out.x = pack_bf16x2(v[0], v[1]);
+        out.y = pack_bf16x2(v[2 % RPT], v[3 % RPT]);
+        *reinterpret_cast<uint2*>(dst) = out;
+    } else {
+        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v[0], v[1 % RPT]);
+    }
+}
+
+template <int MODE, int RPT>
+__device__ __forceinline__ void awq_job(int tid, int* cbase, int* sub) {
+    constexpr int jobs = 32 / RPT;  // jobs per word column
+    const int wc = tid / jobs;
+    *sub = tid % jobs;
+    *cbase = MODE == MODE_GATEUP ? (wc / 16) * 128 + (wc % 16) * 8 : wc * 8;
+}
+
+template <int RPT>
+__device__ __forceinline__ void awq_split(const uint32_t (&rw)[4], uint32_t (&even)[RPT], uint32_t (&odd)[RPT]) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        even[i] = ((rw[i] << 3) & 0x78787878u) | 0x80808080u;  // nibbles 0,2,4,6 in bits 3..6
+        odd[i] = ((rw[i] >> 1) & 0x78787878u) | 0x80808080u;   // nibbles 1,3,5,7
+    }
+}
+
 // Registers of one K step -> LDS stage (A chunks; bf16 B chunks or dequantised AWQ words).
-template <int MODE, bool AWQ, int APER>
-__device__ __forceinline__ void store_stage(const uint4 (&ra)[APER], const uint4 (&rb)[AWQ ? 1 : 4],
+template <int MODE, bool AWQ, int BM>
+__device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APER],
+                                            const uint4 (&rb)[AWQ ? 1 : GemmShape<BM>::BPER],
                                             const uint32_t (&rw)[4], uint32_t rz, uint16_t* As,
                                             uint16_t* Bs, int tid) {
+    using S = GemmShape<BM>;
 #pragma unroll
-    for (int i = 0; i < APER; ++i) {
-        const int q = tid + i * kThreads;
+    for (int i = 0; i < S::APER; ++i) {
+        const int q = tid + i * S::NT;
         *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[i];
     }
     if (!AWQ) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + i * kThreads;
+        for (int i = 0; i < S::BPER; ++i) {
+            const int q = tid + i * S::NT;
             *reinterpret_cast<uint4*>(&Bs[lds_off(q / 4, q % 4)]) = rb[i];
         }
     } else {
-        const int quad = tid % 8, wc = tid / 8;  // rows 4*quad .. +3 of word column wc
-        const int cbase = MODE == MODE_GATEUP ? (wc / 16) * 128 + (wc % 16) * 8 : wc * 8;
+        int cbase, sub;
+        awq_job<MODE, S::RPT>(tid, &cbase, &sub);
         const uint32_t sw[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
-        uint32_t even[4], odd[4];
+        uint32_t even[S::RPT], odd[S::RPT];
+        awq_split<S::RPT>(rw, even, odd);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // bytes with the code in bits 3..6 and bit 7 set (the exponent LSB)
-            even[i] = ((rw[i] << 3) & 0x78787878u) | 0x80808080u;  // nibbles 0,2,4,6
-            odd[i] = ((rw[i] >> 1) & 0x78787878u) | 0x80808080u;   // nibbles 1,3,5,7
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int col = awq_perm(j);
-            const float s = f16_to_f32((sw[col / 2] >> (16 * (col % 2))) & 0xFFFFu);
-            const float c = -(16.0f + (float)((rz >> (4 * j)) & 15u)) * s;
-            const uint32_t sel = 0x07000C0Cu | ((uint32_t)(j >> 1) << 16);
-            float v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // float bits 0x41 | byte | 00 | 00  ->  16 + q
-                const uint32_t mbits = __builtin_amdgcn_perm(0x41000000u, (j & 1) ? odd[i] : even[i], sel);
-                v[i] = fmaf(__uint_as_float(mbits), s, c);
-            }
-            uint2 out;
-            out.x = pack_bf16x2(v[0], v[1]);
-            out.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(&Bs[lds_off(awq_row(cbase + col), quad / 2) + 4 * (quad % 2)]) = out;
-        }
+        for (int j = 0; j < 8; ++j) awq_store_col<MODE, S::RPT>(j, even, odd, sw, rz, Bs, cbase, sub);
     }
 }
 
-// MFMAs of one K step on an LDS stage.
+// MFMA operand fragments of one K step from an LDS stage.
 template <int MODE, bool AWQ, int BM>
-__device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* Bs,
-                                           f32x4_t (&acc)[GemmShape<BM>::TM][GemmShape<BM>::TN],
-                                           int wm, int wn, int lane) {
+__device__ __forceinline__ void read_frags(const uint16_t* As, const uint16_t* Bs,
+                                           bf16x8_t (&af)[GemmShape<BM>::TM],
+                                           bf16x8_t (&bfr)[GemmShape<BM>::TN], int wm, int wn,
+                                           int lane) {
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
-    bf16x8_t af[TM], bfr[TN];
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi)
         af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off(wm * S::MW + mi * 16 + lane % 16, lane / 16)]);
@@ -171,19 +200,59 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* As, const uint16_t* B
         const int brow = AWQ ? awq_row(bcol + lane % 16) : bcol + lane % 16;
         bfr[nj] = *reinterpret_cast<const bf16x8_t*>(&Bs[lds_off(brow, lane / 16)]);
     }
+}
+
+// One K step, interleaved by hand: the next stage's LDS stores (A chunks, and
+// bf16 B chunks or one dequantised AWQ column) are cut into 8 slices, each
+// followed by 1/8 of this step's MFMAs; scheduling barriers keep the slices
+// in order, so that the VALU and LDS work issues while earlier MFMAs execute.
+template <int MODE, bool AWQ, int BM>
+__device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<BM>::TM],
+                                                 const bf16x8_t (&bfr)[GemmShape<BM>::TN],
+                                                 f32x4_t (&acc)[GemmShape<BM>::TM][GemmShape<BM>::TN],
+                                                 const uint4 (&ra)[GemmShape<BM>::APER],
+                                                 const uint4 (&rb)[AWQ ? 1 : GemmShape<BM>::BPER],
+                                                 const uint32_t (&rw)[4], uint32_t rz, uint16_t* As,
+                                                 uint16_t* Bs, int tid) {
+    using S = GemmShape<BM>;
+    constexpr int TM = S::TM, TN = S::TN;
+    constexpr int NM = TM * TN;  // MFMAs this step
+    constexpr int PER = NM / 8;  // per slice
+    int cbase = 0, sub = 0;
+    uint32_t even[S::RPT], odd[S::RPT];
+    if (AWQ) {
+        awq_job<MODE, S::RPT>(tid, &cbase, &sub);
+        awq_split<S::RPT>(rw, even, odd);
+    }
+    const uint32_t sw[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi)
+    for (int j = 0; j < 8; ++j) {
+        if (j < S::APER) {
+            const int q = tid + j * S::NT;
+            *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[j];
+        }
+        if (!AWQ) {
+            if (j < S::BPER) {
+                const int q = tid + j * S::NT;
+                *reinterpret_cast<uint4*>(&Bs[lds_off(q / 4, q % 4)]) = rb[j];
+            }
+        } else {
+            awq_store_col<MODE, S::RPT>(j, even, odd, sw, rz, Bs, cbase, sub);
+        }
 #pragma unroll
-        for (int nj = 0; nj < TN; ++nj)
-            acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
+        for (int m = j * PER; m < (j + 1) * PER; ++m)
+            acc[m / TN][m % TN] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m / TN], bfr[m % TN], acc[m / TN][m % TN], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 template <int MODE, bool AWQ, int BM>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GroupedArgs a,
+__global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(GroupedArgs a,
                                                                const int32_t* __restrict__ tiles,
                                                                uint16_t* __restrict__ hbuf, int NT) {
     using S = GemmShape<BM>;
-    constexpr int TM = S::TM, TN = S::TN, APER = S::APER;
+    constexpr int TM = S::TM, TN = S::TN, APER = S::APER, BPER = S::BPER, NTHR = S::NT;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kBK];
 
@@ -206,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GroupedArgs a,
     const uint16_t* asrc[APER];
 #pragma unroll
     for (int i = 0; i < APER; ++i) {
-        const int q = tid + i * kThreads;
+        const int q = tid + i * NTHR;
         const int row = q / 4, kc = q % 4;
         const int gr = min(m0 + row, m1 - 1);
         if (MODE == MODE_GATEUP) {
@@ -216,18 +285,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GroupedArgs a,
             asrc[i] = hbuf + (size_t)gr * F + kc * 8;
         }
     }
-    // ---- B sources.  bf16: 4 chunks (B-column q/4, k-offset (q%4)*8), q = tid + i*256.
-    // awq: word column wc = tid % 32 (of the 32 words spanning 256 columns), rows
-    // 4*(tid/32) .. +3 of the group.
-    const uint16_t* bsrc[4];
+    // ---- B sources.  bf16: BPER chunks (B-column q/4, k-offset (q%4)*8), q = tid + i*NT.
+    // awq: one word column of the 32 spanning 256 columns, RPT consecutive rows.
+    const uint16_t* bsrc[BPER];
     const int32_t* wsrc = nullptr;
     const int32_t* zsrc = nullptr;
     const uint16_t* ssrc = nullptr;
     int OW = NOUT / 8;
     if (!AWQ) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + i * kThreads;
+        for (int i = 0; i < BPER; ++i) {
+            const int q = tid + i * NTHR;
             const int bc = q / 4, kc = q % 4;
             const uint16_t* W;
             int col;
@@ -243,7 +311,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GroupedArgs a,
             bsrc[i] = W + (size_t)col * K + kc * 8;
         }
     } else {
-        const int wc = tid / 8, kr = 4 * (tid % 8);
+        constexpr int jobs = 32 / S::RPT;
+        const int wc = tid / jobs, kr = S::RPT * (tid % jobs);
         // select by value (a reference into the kernel-argument struct would force a stack copy)
         const bool up = MODE == MODE_GATEUP && wc >= 16;
         const int32_t* qw = MODE == MODE_DOWN ? a.down.qweight : (up ? a.up.qweight : a.gate.qweight);
@@ -264,8 +333,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GroupedArgs a,
     // register stages: the raw global data of one K step, two in flight
     // (separately named so that no index into them can become dynamic)
     uint4 ra0[APER], ra1[APER];
-    uint4 rb0[AWQ ? 1 : 4], rb1[AWQ ? 1 : 4];
-    uint32_t rw0[4], rw1[4];
+    uint4 rb0[AWQ ? 1 : BPER], rb1[AWQ ? 1 : BPER];
+    uint32_t rw0[4] = {0, 0, 0, 0}, rw1[4] = {0, 0, 0, 0};
     uint32_t rz0 = 0, rz1 = 0;
 
 #define MOE_LOAD(RA, RB, RW, RZ, KT)                                                          \
@@ -274,10 +343,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GroupedArgs a,
         _Pragma("unroll") for (int i = 0; i < APER; ++i) RA[i] =                              \
             *reinterpret_cast<const uint4*>(asrc[i] + k0_);                                   \
         if (!AWQ) {                                                                           \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) RB[i] =                             \
+            _Pragma("unroll") for (int i = 0; i < BPER; ++i) RB[i] =                          \
                 *reinterpret_cast<const uint4*>(bsrc[i] + k0_);                               \
         } else {                                                                              \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) RW[i] =                             \
+            _Pragma("unroll") for (int i = 0; i < S::RPT; ++i) RW[i] =                        \
                 (uint32_t)wsrc[(size_t)(k0_ + i) * OW];                                       \
             RZ = (uint32_t)zsrc[(size_t)(KT) * OW];                                           \
             RB[0] = *reinterpret_cast<const uint4*>(ssrc + (size_t)(KT) * NOUT);              \
@@ -285,21 +354,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GroupedArgs a,
     } while (0)
 
     // stage 0 holds the step being written to LDS next, stage 1 the step in flight;
-    // they swap by value each step (register moves, no addressable arrays)
+    // they swap by value each step (register moves, no addressable arrays).  The
+    // loop body has no branches (loads past the end repeat the last step, and
+    // the spare LDS stage absorbs the last store), so the whole step is one
+    // scheduling region.
     MOE_LOAD(ra0, rb0, rw0, rz0, 0);
-    store_stage<MODE, AWQ, APER>(ra0, rb0, rw0, rz0, As[0], Bs[0], tid);
-    if (nk > 1) MOE_LOAD(ra1, rb1, rw1, rz1, 1);
+    store_stage<MODE, AWQ, BM>(ra0, rb0, rw0, rz0, As[0], Bs[0], tid);
+    MOE_LOAD(ra1, rb1, rw1, rz1, (nk > 1 ? 1 : 0));
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 2 < nk) MOE_LOAD(ra0, rb0, rw0, rz0, kt + 2);  // stage 0 is free: its step is in LDS
-        mfma_stage<MODE, AWQ, BM>(As[cur], Bs[cur], acc, wm, wn, lane);
-        if (kt + 1 < nk) store_stage<MODE, AWQ, APER>(ra1, rb1, rw1, rz1, As[cur ^ 1], Bs[cur ^ 1], tid);
+        MOE_LOAD(ra0, rb0, rw0, rz0, min(kt + 2, nk - 1));  // stage 0 is free: its step is in LDS
+        bf16x8_t af[TM], bfr[TN];
+        read_frags<MODE, AWQ, BM>(As[cur], Bs[cur], af, bfr, wm, wn, lane);
+        step_interleaved<MODE, AWQ, BM>(af, bfr, acc, ra1, rb1, rw1, rz1, As[cur ^ 1], Bs[cur ^ 1], tid);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < APER; ++i) { const uint4 t = ra0[i]; ra0[i] = ra1[i]; ra1[i] = t; }
 #pragma unroll
-        for (int i = 0; i < (AWQ ? 1 : 4); ++i) { const uint4 t = rb0[i]; rb0[i] = rb1[i]; rb1[i] = t; }
+        for (int i = 0; i < (AWQ ? 1 : BPER); ++i) { const uint4 t = rb0[i]; rb0[i] = rb1[i]; rb1[i] = t; }
 #pragma unroll
         for (int i = 0; i < 4; ++i) { const uint32_t t = rw0[i]; rw0[i] = rw1[i]; rw1[i] = t; }
         { const uint32_t t = rz0; rz0 = rz1; rz1 = t; }
@@ -366,14 +439,14 @@ static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t*
                            hipStream_t s) {
     const int NT1 = a.F / (kBN / 2), NT2 = a.H / kBN;
     if (a.awq) {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, true, BM>), dim3(mt * NT1), dim3(kThreads), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, true, BM>), dim3(mt * NT1), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, true, BM>), dim3(mt * NT2), dim3(kThreads), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, true, BM>), dim3(mt * NT2), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT2);
     } else {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, false, BM>), dim3(mt * NT1), dim3(kThreads), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, false, BM>), dim3(mt * NT1), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, BM>), dim3(mt * NT2), dim3(kThreads), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, BM>), dim3(mt * NT2), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT2);
     }
 }
@@ -418,13 +491,13 @@ hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t
                        tiles);
     const int NT = N / kBN;
     if (BM == 256)
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 256>), dim3(mt * NT), dim3(kThreads), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 256>), dim3(mt * NT), dim3(GemmShape<256>::NT), 0,
                            s, a, tiles, Ain, NT);
     else if (BM == 128)
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 128>), dim3(mt * NT), dim3(kThreads), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 128>), dim3(mt * NT), dim3(GemmShape<128>::NT), 0,
                            s, a, tiles, Ain, NT);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 64>), dim3(mt * NT), dim3(kThreads), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 64>), dim3(mt * NT), dim3(GemmShape<64>::NT), 0,
                            s, a, tiles, Ain, NT);
     return hipGetLastError();
 }
