@@ -106,22 +106,21 @@ struct GemmShape {
     static constexpr int RPT = 1024 / NT;         // AWQ: input rows per thread per step (one word column)
 };
 
-// Dequantise word column rows of one AWQ B job (RPT consecutive input rows of
-// one packed word) and store column j (nibble j) into the K-major LDS tile.
+// Dequantise column j (nibble j) of one AWQ B job (RPT consecutive input rows
+// of one packed word) and store it into the K-major LDS tile.  s[] and c[] are
+// the job's 8 columns' scale and -(16 + zero) * scale, in column order.
 template <int MODE, int RPT>
 __device__ __forceinline__ void awq_store_col(int j, const uint32_t (&even)[RPT], const uint32_t (&odd)[RPT],
-                                              const uint32_t (&sw)[4], uint32_t rz, uint16_t* Bs, int cbase,
-                                              int sub) {
+                                              const float (&s)[8], const float (&c)[8], uint16_t* Bs,
+                                              int cbase, int sub) {
     const int col = awq_perm(j);
-    const float sc = f16_to_f32((sw[col / 2] >> (16 * (col % 2))) & 0xFFFFu);
-    const float c = -(16.0f + (float)((rz >> (4 * j)) & 15u)) * sc;
     const uint32_t sel = 0x07000C0Cu | ((uint32_t)(j >> 1) << 16);
     float v[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         // float bits 0x41 | byte | 00 | 00  ->  16 + q
         const uint32_t mbits = __builtin_amdgcn_perm(0x41000000u, (j & 1) ? odd[i] : even[i], sel);
-        v[i] = fmaf(__uint_as_float(mbits), sc, c);
+        v[i] = fmaf(__uint_as_float(mbits), s[col], c[col]);
     }
     const int k0 = RPT * sub;  // first input row of the job within the step
     uint16_t* dst = &Bs[lds_off(awq_row(cbase + col), k0 / 8) + k0 % 8];
@@ -135,6 +134,19 @@ __device__ __forceinline__ void awq_store_col(int j, const uint32_t (&even)[RPT]
     }
 }
 
+// The job's 8 column parameters from the step's LDS table.
+__device__ __forceinline__ void awq_params(const float2* Ps, int cbase, float (&s)[8], float (&c)[8]) {
+    const float4* pv = reinterpret_cast<const float4*>(&Ps[cbase]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 v = pv[i];
+        s[2 * i] = v.x;
+        c[2 * i] = v.y;
+        s[2 * i + 1] = v.z;
+        c[2 * i + 1] = v.w;
+    }
+}
+
 template <int MODE, int RPT>
 __device__ __forceinline__ void awq_job(int tid, int* cbase, int* sub) {
     constexpr int jobs = 32 / RPT;  // jobs per word column
@@ -144,7 +156,7 @@ __device__ __forceinline__ void awq_job(int tid, int* cbase, int* sub) {
 }
 
 template <int RPT>
-__device__ __forceinline__ void awq_split(const uint32_t (&rw)[4], uint32_t (&even)[RPT], uint32_t (&odd)[RPT]) {
+__device__ __forceinline__ void awq_split(const uint32_t (&rw)[RPT], uint32_t (&even)[RPT], uint32_t (&odd)[RPT]) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         even[i] = ((rw[i] << 3) & 0x78787878u) | 0x80808080u;  // nibbles 0,2,4,6 in bits 3..6
@@ -155,9 +167,9 @@ __device__ __forceinline__ void awq_split(const uint32_t (&rw)[4], uint32_t (&ev
 // Registers of one K step -> LDS stage (A chunks; bf16 B chunks or dequantised AWQ words).
 template <int MODE, bool AWQ, int BM>
 __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APER],
-                                            const uint4 (&rb)[AWQ ? 1 : GemmShape<BM>::BPER],
-                                            const uint32_t (&rw)[4], uint32_t rz, uint16_t* As,
-                                            uint16_t* Bs, int tid) {
+                                            const uint4 (&rb)[GemmShape<BM>::BPER],
+                                            const uint32_t (&rw)[GemmShape<BM>::RPT], const float2* Ps,
+                                            uint16_t* As, uint16_t* Bs, int tid) {
     using S = GemmShape<BM>;
 #pragma unroll
     for (int i = 0; i < S::APER; ++i) {
@@ -173,11 +185,12 @@ __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APE
     } else {
         int cbase, sub;
         awq_job<MODE, S::RPT>(tid, &cbase, &sub);
-        const uint32_t sw[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
+        float sc[8], cc[8];
+        awq_params(Ps, cbase, sc, cc);
         uint32_t even[S::RPT], odd[S::RPT];
         awq_split<S::RPT>(rw, even, odd);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) awq_store_col<MODE, S::RPT>(j, even, odd, sw, rz, Bs, cbase, sub);
+        for (int j = 0; j < 8; ++j) awq_store_col<MODE, S::RPT>(j, even, odd, sc, cc, Bs, cbase, sub);
     }
 }
 
@@ -211,20 +224,21 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
                                                  const bf16x8_t (&bfr)[GemmShape<BM>::TN],
                                                  f32x4_t (&acc)[GemmShape<BM>::TM][GemmShape<BM>::TN],
                                                  const uint4 (&ra)[GemmShape<BM>::APER],
-                                                 const uint4 (&rb)[AWQ ? 1 : GemmShape<BM>::BPER],
-                                                 const uint32_t (&rw)[4], uint32_t rz, uint16_t* As,
-                                                 uint16_t* Bs, int tid) {
+                                                 const uint4 (&rb)[GemmShape<BM>::BPER],
+                                                 const uint32_t (&rw)[GemmShape<BM>::RPT],
+                                                 const float2* Ps, uint16_t* As, uint16_t* Bs, int tid) {
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
     constexpr int NM = TM * TN;  // MFMAs this step
     constexpr int PER = NM / 8;  // per slice
     int cbase = 0, sub = 0;
     uint32_t even[S::RPT], odd[S::RPT];
+    float sc[8], cc[8];
     if (AWQ) {
         awq_job<MODE, S::RPT>(tid, &cbase, &sub);
+        awq_params(Ps, cbase, sc, cc);
         awq_split<S::RPT>(rw, even, odd);
     }
-    const uint32_t sw[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         if (j < S::APER) {
@@ -237,7 +251,7 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
                 *reinterpret_cast<uint4*>(&Bs[lds_off(q / 4, q % 4)]) = rb[j];
             }
         } else {
-            awq_store_col<MODE, S::RPT>(j, even, odd, sw, rz, Bs, cbase, sub);
+            awq_store_col<MODE, S::RPT>(j, even, odd, sc, cc, Bs, cbase, sub);
         }
 #pragma unroll
         for (int m = j * PER; m < (j + 1) * PER; ++m)
@@ -255,6 +269,7 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
     constexpr int TM = S::TM, TN = S::TN, APER = S::APER, BPER = S::BPER, NTHR = S::NT;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kBK];
+    __shared__ __attribute__((aligned(16))) float2 Ps[2][kBN];  // AWQ (s, -(16 + z) s) per column
 
     const int l = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = l / NT, nt = l % NT;
@@ -285,13 +300,16 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
             asrc[i] = hbuf + (size_t)gr * F + kc * 8;
         }
     }
-    // ---- B sources.  bf16: BPER chunks (B-column q/4, k-offset (q%4)*8), q = tid + i*NT.
-    // awq: one word column of the 32 spanning 256 columns, RPT consecutive rows.
+    // ---- B sources.  bf16: BPER chunks (B-column q/4, k-offset (q%4)*8), q = tid + i*NTHR.
+    // awq: one word column of the 32 spanning 256 columns, RPT consecutive rows;
+    // threads < 256 also fetch one column's zero word and scale for the
+    // per-step parameter table.
     const uint16_t* bsrc[BPER];
     const int32_t* wsrc = nullptr;
     const int32_t* zsrc = nullptr;
     const uint16_t* ssrc = nullptr;
-    int OW = NOUT / 8;
+    int pnib = 0;  // nibble of the parameter column in its zero word
+    const int OW = NOUT / 8;
     if (!AWQ) {
 #pragma unroll
         for (int i = 0; i < BPER; ++i) {
@@ -316,12 +334,16 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
         // select by value (a reference into the kernel-argument struct would force a stack copy)
         const bool up = MODE == MODE_GATEUP && wc >= 16;
         const int32_t* qw = MODE == MODE_DOWN ? a.down.qweight : (up ? a.up.qweight : a.gate.qweight);
-        const int32_t* qz = MODE == MODE_DOWN ? a.down.qzeros : (up ? a.up.qzeros : a.gate.qzeros);
-        const uint16_t* sc = MODE == MODE_DOWN ? a.down.scales : (up ? a.up.scales : a.gate.scales);
         const int word = MODE == MODE_GATEUP ? n0 / 8 + wc % 16 : n0 / 8 + wc;
         wsrc = qw + (size_t)e * K * OW + (size_t)kr * OW + word;
-        zsrc = qz + (size_t)e * (K / 32) * OW + word;
-        ssrc = sc + (size_t)e * (K / 32) * NOUT + 8 * word;
+        const int pc = min(tid, kBN - 1);  // parameter column (threads >= 256 duplicate the last)
+        const bool pup = MODE == MODE_GATEUP && pc >= 128;
+        const int32_t* qz = MODE == MODE_DOWN ? a.down.qzeros : (pup ? a.up.qzeros : a.gate.qzeros);
+        const uint16_t* sc = MODE == MODE_DOWN ? a.down.scales : (pup ? a.up.scales : a.gate.scales);
+        const int col = MODE == MODE_GATEUP ? n0 + pc % 128 : n0 + pc;
+        zsrc = qz + (size_t)e * (K / 32) * OW + col / 8;
+        ssrc = sc + (size_t)e * (K / 32) * NOUT + col;
+        pnib = (col & 1) ? 4 + ((col & 7) >> 1) : ((col & 7) >> 1);
     }
 
     f32x4_t acc[TM][TN];
@@ -330,54 +352,70 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // register stages: the raw global data of one K step, two in flight
-    // (separately named so that no index into them can become dynamic)
+    // Two register stages with the raw global data of one K step each; the loop
+    // is unrolled by two so that they alternate roles without register moves.
     uint4 ra0[APER], ra1[APER];
-    uint4 rb0[AWQ ? 1 : BPER], rb1[AWQ ? 1 : BPER];
-    uint32_t rw0[4] = {0, 0, 0, 0}, rw1[4] = {0, 0, 0, 0};
-    uint32_t rz0 = 0, rz1 = 0;
+    uint4 rb0[BPER], rb1[BPER];
+    uint32_t rw0[S::RPT], rw1[S::RPT];
+    uint32_t pz0 = 0, pz1 = 0, ps0 = 0, ps1 = 0;  // zero word and scale of the parameter column
 
-#define MOE_LOAD(RA, RB, RW, RZ, KT)                                                          \
+#define MOE_LOAD(RA, RB, RW, PZ, PS, KT)                                                      \
     do {                                                                                      \
-        const int k0_ = (KT) * kBK;                                                           \
-        _Pragma("unroll") for (int i = 0; i < APER; ++i) RA[i] =                              \
-            *reinterpret_cast<const uint4*>(asrc[i] + k0_);                                   \
-        if (!AWQ) {                                                                           \
-            _Pragma("unroll") for (int i = 0; i < BPER; ++i) RB[i] =                          \
-                *reinterpret_cast<const uint4*>(bsrc[i] + k0_);                               \
-        } else {                                                                              \
+        const int kt_ = (KT), k0_ = kt_ * kBK;                                                \
+        if (AWQ) {                                                                            \
+            PZ = (uint32_t)zsrc[(size_t)kt_ * OW];                                            \
+            PS = (uint32_t)ssrc[(size_t)kt_ * NOUT];                                          \
             _Pragma("unroll") for (int i = 0; i < S::RPT; ++i) RW[i] =                        \
                 (uint32_t)wsrc[(size_t)(k0_ + i) * OW];                                       \
-            RZ = (uint32_t)zsrc[(size_t)(KT) * OW];                                           \
-            RB[0] = *reinterpret_cast<const uint4*>(ssrc + (size_t)(KT) * NOUT);              \
+        } else {                                                                              \
+            _Pragma("unroll") for (int i = 0; i < BPER; ++i) RB[i] =                          \
+                *reinterpret_cast<const uint4*>(bsrc[i] + k0_);                               \
+        }                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < APER; ++i) RA[i] =                              \
+            *reinterpret_cast<const uint4*>(asrc[i] + k0_);                                   \
+    } while (0)
+    // (s, -(16 + z) s) of this thread's parameter column, for the step in PZ/PS
+#define MOE_PARAMS(PZ, PS, BUF)                                                               \
+    do {                                                                                      \
+        if (AWQ && tid < kBN) {                                                               \
+            const float s_ = f16_to_f32((PS) & 0xFFFFu);                                      \
+            const float z_ = (float)(((PZ) >> (4 * pnib)) & 15u);                             \
+            Ps[BUF][tid] = make_float2(s_, -(16.0f + z_) * s_);                               \
         }                                                                                     \
     } while (0)
 
-    // stage 0 holds the step being written to LDS next, stage 1 the step in flight;
-    // they swap by value each step (register moves, no addressable arrays).  The
-    // loop body has no branches (loads past the end repeat the last step, and
-    // the spare LDS stage absorbs the last store), so the whole step is one
-    // scheduling region.
-    MOE_LOAD(ra0, rb0, rw0, rz0, 0);
-    store_stage<MODE, AWQ, BM>(ra0, rb0, rw0, rz0, As[0], Bs[0], tid);
-    MOE_LOAD(ra1, rb1, rw1, rz1, (nk > 1 ? 1 : 0));
+    // prologue: steps 0 and 1 in registers, their parameters in LDS, step 0 in LDS
+    MOE_LOAD(ra0, rb0, rw0, pz0, ps0, 0);
+    MOE_LOAD(ra1, rb1, rw1, pz1, ps1, 1);
+    MOE_PARAMS(pz0, ps0, 0);
+    MOE_PARAMS(pz1, ps1, 1);
     __syncthreads();
+    store_stage<MODE, AWQ, BM>(ra0, rb0, rw0, Ps[0], As[0], Bs[0], tid);
+    __syncthreads();
+    // Loads past the end repeat the last step; the spare LDS stage absorbs the
+    // last stores.  No branches inside a step: one scheduling region.  Stage 0
+    // refills with step kt+2 while stage 1 (step kt+1) is stored; the stages then
+    // swap by value (register moves; unrolling instead makes the compiler merge
+    // the two halves and address the stages in memory).
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        MOE_LOAD(ra0, rb0, rw0, rz0, min(kt + 2, nk - 1));  // stage 0 is free: its step is in LDS
+        MOE_LOAD(ra0, rb0, rw0, pz0, ps0, min(kt + 2, nk - 1));
         bf16x8_t af[TM], bfr[TN];
         read_frags<MODE, AWQ, BM>(As[cur], Bs[cur], af, bfr, wm, wn, lane);
-        step_interleaved<MODE, AWQ, BM>(af, bfr, acc, ra1, rb1, rw1, rz1, As[cur ^ 1], Bs[cur ^ 1], tid);
+        step_interleaved<MODE, AWQ, BM>(af, bfr, acc, ra1, rb1, rw1, Ps[cur ^ 1], As[cur ^ 1], Bs[cur ^ 1], tid);
+        MOE_PARAMS(pz0, ps0, cur);  // parameters of step kt+2 (table cur held step kt's)
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < APER; ++i) { const uint4 t = ra0[i]; ra0[i] = ra1[i]; ra1[i] = t; }
 #pragma unroll
-        for (int i = 0; i < (AWQ ? 1 : BPER); ++i) { const uint4 t = rb0[i]; rb0[i] = rb1[i]; rb1[i] = t; }
+        for (int i = 0; i < BPER; ++i) { const uint4 t = rb0[i]; rb0[i] = rb1[i]; rb1[i] = t; }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { const uint32_t t = rw0[i]; rw0[i] = rw1[i]; rw1[i] = t; }
-        { const uint32_t t = rz0; rz0 = rz1; rz1 = t; }
+        for (int i = 0; i < S::RPT; ++i) { const uint32_t t = rw0[i]; rw0[i] = rw1[i]; rw1[i] = t; }
+        { const uint32_t t = pz0; pz0 = pz1; pz1 = t; }
+        { const uint32_t t = ps0; ps0 = ps1; ps1 = t; }
     }
 #undef MOE_LOAD
+#undef MOE_PARAMS
 
     // ---- epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile
     const int rbase = m0 + wm * S::MW + 4 * (lane / 16);
