@@ -463,7 +463,7 @@ static int max_tiles(int P, int E, int BM) { return (P + BM - 1) / BM + E; }
 static int pick_bm(int P, int E) {
     const int active = P < E ? P : E;
     const int avg = active > 0 ? P / active : 0;
-    return avg >= 192 ? 256 : (avg >= 96 ? 128 : 64);
+    return avg >= 128 ? 256 : (avg >= 96 ? 128 : 64);
 }
 
 static size_t tiles_bytes(int P, int E) {

@@ -47,7 +47,7 @@ __device__ __forceinline__ void awq_gemv_groups(const int32_t* __restrict__ qw,
             for (int i = 0; i < RCH; ++i) acc[j][i] = 0.0f;
         const int32_t* wp = qw + (size_t)g * 32 * OW + c;
         const int lg = g - g_base;
-#pragma unroll 4
+#pragma unroll
         for (int q = 0; q < 16; ++q) {
             const uint32_t w0 = (uint32_t)wp[(size_t)(2 * q) * OW];
             const uint32_t w1 = (uint32_t)wp[(size_t)(2 * q + 1) * OW];
@@ -506,8 +506,10 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, float* part, hipStream_t
 
 hipError_t launch_gemv(const GroupedArgs& a, void* ws, hipStream_t s) {
     float* part = static_cast<float*>(ws);
-    if (!a.offsets && a.T > 4) return launch_gemv_rch<8>(a, part, s);
-    return launch_gemv_rch<4>(a, part, s);
+    // rows per pass: the shared expert sees every token; a routed expert at
+    // decode sees one or two, so two rows per pass keeps registers low
+    if (!a.offsets && a.T > 2) return a.awq ? launch_gemv_rch<4>(a, part, s) : launch_gemv_rch<8>(a, part, s);
+    return launch_gemv_rch<2>(a, part, s);
 }
 
 }  // namespace moe
