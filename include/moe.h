@@ -163,7 +163,9 @@ moe_status moe_combine(const void *rows, int32_t rows_dtype, const int32_t *pair
  * T*(k+1) pairs), topk_idx / topk_logit are [T][k+1].  token_valid
  * (nullable = all valid) is [T] uint8.  stat_sum (fp32 [E]) and stat_count
  * (uint32 [E]) are ADDED to, so batches accumulate; each expert's additions
- * are summed in a fixed order (ascending pair id) and added once per call.
+ * are summed in a fixed order (64 strided partial sums over the expert's rows
+ * in grouped order, then a fixed tree) and added once per call, so results
+ * are reproducible.
  */
 moe_status moe_refill_score(const float *rows, const int32_t *expert_offsets,
                             const int32_t *sorted_pair, const int32_t *pair_to_row,

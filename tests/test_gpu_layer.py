@@ -111,7 +111,8 @@ def check_refill(gpu, ref, keep):
 
 @pytest.mark.parametrize("T,H,F,E,k,keep,batches", [(2048, 256, 128, 64, 10, 32, 1),   # MFMA rows
                                                     (300, 256, 128, 64, 4, 40, 3),     # additive batches
-                                                    (96, 2560, 640, 512, 10, 256, 1)])  # full geometry
+                                                    (96, 2560, 640, 512, 10, 256, 1),   # full geometry
+                                                    (256, 256, 128, 512, 10, 384, 1)])  # keep 384 of 512
 def test_refill_matches_oracle(T, H, F, E, k, keep, batches):
     moe = require_gpu()
     w = workloads.scaled(workloads.get("refill_bf16"), T=T, H=H, F=F, Fs=F, E=E, k=k, keep=keep)
@@ -119,3 +120,28 @@ def test_refill_matches_oracle(T, H, F, E, k, keep, batches):
     gpu = _gpu_refill(moe, d, w, keep, batches)
     ref = _oracle_refill(d, w, keep)
     check_refill(gpu, ref, keep)
+
+
+# ----------------------------------------------------------------------------- E384of512 budget
+
+def test_pruned_e384_layer_matches_oracle():
+    """Keep 384 of 512 AWQ experts (the other released budget): slice, route over
+    384 logits (6 per lane) and run the layer."""
+    moe = require_gpu()
+    w = workloads.scaled(workloads.get("pruned_awq"), T=64, E=384, E_base=512)
+    d = workloads.generate(w, seed=3, device="cuda")
+    keep = d["keep_idx"]
+    assert keep.numel() == 384
+    wr, bank = moe.prune_slice(keep.cuda(), d["router"], d["experts"])
+    y, mid = moe.moe_layer(d["x"], wr, w.k, bank, d["shared"], keep_intermediates=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(wr), bits(d["router"])[keep.numpy()])
+    ref_y, ref_idx, ref_g = oracle_layer_sparse(d["x"], wr, w.k, bank, d["shared"])
+    np.testing.assert_array_equal(mid["idx"].cpu().numpy(), ref_idx)
+    np.testing.assert_allclose(mid["gate"].cpu().numpy(), ref_g, rtol=1e-5, atol=1e-7)
+    # the pruned layer is the base layer with the dropped experts masked out
+    base_l, _ = O.router_logits(bits(d["x"]), bits(d["router"]))
+    masked = np.full_like(base_l, -np.inf)
+    masked[:, keep.numpy()] = base_l[:, keep.numpy()]
+    np.testing.assert_array_equal(keep.numpy()[ref_idx], O.rank(masked, w.k))
+    check_close(y.float().cpu().numpy(), ref_y, "E384 layer")

@@ -23,7 +23,8 @@ def _wl(T, H, E, F=128, fmt="bf16", Fs=None):
 @pytest.mark.parametrize("T,H,E,k,extra", [(64, 256, 16, 2, 0), (16, 2560, 512, 10, 0),
                                            (16, 2560, 512, 10, 1), (300, 512, 100, 7, 1),
                                            (3, 64, 1, 1, 0), (70, 128, 1024, 10, 1),
-                                           (33, 256, 65, 64, 0)])
+                                           (33, 256, 65, 64, 0), (40, 2560, 384, 10, 1),
+                                           (200, 512, 384, 10, 0)])
 def test_route_matches_oracle(T, H, E, k, extra):
     moe = require_gpu()
     w = _wl(T, H, E)
