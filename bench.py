@@ -2,8 +2,8 @@
 """Throughput of the MoE feed-forward layer on one MI355X.
 
 A step is one pass of the whole layer over one batch of seeded synthetic
-input resident in HBM: route -> permute -> routed experts -> shared expert ->
-combine (for the Refill-RMS workload: route with the 11th expert -> permute ->
+input resident in HBM: route -> permute -> routed experts -> combine, with the
+shared expert on a second stream beside them (for the Refill-RMS workload: route with the 11th expert -> permute ->
 routed experts (fp32 rows) -> refill score -> keep-set).  Steps cycle through
 several independently generated weight copies so that the weights do not stay
 in the 256 MB on-die cache between steps.
@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the oracle CPU-baseline sample (0 disables it)")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--graph", choices=["on", "off"], default="off",
+                   help="replay each step from HIP graphs ([route, permute], [routed experts], "
+                        "[combine]; the shared expert stays on its side stream)")
     return p.parse_args()
 
 
@@ -91,6 +94,9 @@ def main():
     torch.cuda.synchronize()
     ws = moe.Workspace(dev)
     stream = torch.cuda.current_stream()
+    # the shared expert needs only x: it runs on a second stream (default
+    # priority) beside routing and the routed experts, with its own workspace
+    side, side_ws = torch.cuda.Stream(dev), moe.Workspace(dev)
 
     if w.refill:
         stats = [(torch.zeros(w.E, dtype=torch.float32, device=dev),
@@ -109,14 +115,22 @@ def main():
             moe.refill_score(rows, off, sp, p2r, idx, tl, s, c, ws=ws)
             moe.refill_finalize(s, c, w.H, w.keep)
             return idx
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            s = moe.grouped_ffn(x, 1, d["shared"], ws=side_ws)
         idx, tl, gate, _ = moe.route(x, d["router"], w.k, ws=ws)
         off, sp, p2r = moe.permute(idx, w.E, ws=ws)
         if ev: ev[0].record(stream)
         rows = moe.grouped_ffn(x, w.k, d["experts"], off, sp, ws=ws)
         if ev: ev[1].record(stream)
-        s = moe.grouped_ffn(x, 1, d["shared"], ws=ws)
+        stream.wait_stream(side)
+        s.record_stream(stream)
         moe.combine(rows, p2r, gate, s)
         return idx
+
+    use_graph = args.graph == "on"
+    if use_graph:
+        step = graph_steps(moe, w, sets, ws, side, side_ws, stream, step)
 
     for i in range(args.warmup):
         step(i)
@@ -175,13 +189,56 @@ def main():
               "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
                          "experts_base": w.E_base or w.E, "top_k": w.k, "expert_width": w.F,
                          "shared_width": w.Fs, "weights": w.fmt, "weight_copies": copies,
-                         "touched_experts": n_touched},
+                         "touched_experts": n_touched, "hip_graphs": use_graph},
               "roofline": roof}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, sets[0], args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def graph_steps(moe, w, sets, ws, side, side_ws, stream, eager_step):
+    """Steps replayed from HIP graphs, one set per weight copy: [route, permute],
+    [routed experts], [combine] captured separately so that the HIP events
+    around the routed call are recorded between replays.  The shared expert
+    runs on the side stream as in the eager step.  Capture happens after an
+    eager pass, so every workspace already has its final size."""
+    import torch
+    for i in range(len(sets)):
+        eager_step(i)
+    torch.cuda.synchronize()
+    graphs = []
+    for d in sets:
+        x = d["x"]
+        if w.refill:
+            raise ValueError("the Refill-RMS pass is not replayed from graphs")
+        s_buf = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=x.device)
+        g1, g2, g3 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1):
+            idx, tl, gate, _ = moe.route(x, d["router"], w.k, ws=ws)
+            off, sp, p2r = moe.permute(idx, w.E, ws=ws)
+        with torch.cuda.graph(g2):
+            rows = moe.grouped_ffn(x, w.k, d["experts"], off, sp, ws=ws)
+        with torch.cuda.graph(g3):
+            y = moe.combine(rows, p2r, gate, s_buf)
+        graphs.append((g1, g2, g3, s_buf, (idx, tl, gate, off, sp, p2r, rows, y)))
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        d = sets[i % len(sets)]
+        g1, g2, g3, s_buf, keep = graphs[i % len(sets)]
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            moe.grouped_ffn(d["x"], 1, d["shared"], ws=side_ws, rows=s_buf)
+        g1.replay()
+        if ev: ev[0].record(stream)
+        g2.replay()
+        if ev: ev[1].record(stream)
+        stream.wait_stream(side)
+        g3.replay()
+        return keep[0]
+    return step
 
 
 def cpu_baseline(w, d, seconds):

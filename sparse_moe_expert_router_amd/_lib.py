@@ -265,13 +265,31 @@ def router_norm_keep(w_router, keep: int):
 # ----------------------------------------------------------------------------- layer
 
 def moe_layer(x, w_router, k: int, bank: dict, shared: dict | None = None, shared_scale=None,
-              ws=None, keep_intermediates: bool = False):
-    """The MoE feed-forward layer: route -> permute -> routed experts -> shared expert -> combine."""
+              ws=None, keep_intermediates: bool = False, shared_stream=None, shared_ws=None):
+    """The MoE feed-forward layer: route -> permute -> routed experts -> shared expert -> combine.
+
+    With `shared_stream` (a torch.cuda.Stream) the shared expert, which needs
+    only x, runs on that stream beside routing and the routed experts, with its
+    own workspace `shared_ws`; the combine waits for it."""
     E = w_router.shape[0]
+    main = torch.cuda.current_stream(x.device)
+    s = None
+    if shared is not None and shared_stream is not None:
+        if shared_ws is None:  # calls on different streams need different workspaces
+            key = (str(x.device), shared_stream.cuda_stream)
+            shared_ws = _default_ws.setdefault(key, Workspace(x.device))
+        shared_stream.wait_stream(main)
+        with torch.cuda.stream(shared_stream):
+            s = grouped_ffn(x, 1, shared, ws=shared_ws)
+        x.record_stream(shared_stream)
     idx, tl, gate, _ = route(x, w_router, k, ws=ws)
     off, sp, p2r = permute(idx, E, ws=ws)
     rows = grouped_ffn(x, k, bank, off, sp, ws=ws)
-    s = grouped_ffn(x, 1, shared, ws=ws) if shared is not None else None
+    if shared is not None and shared_stream is None:
+        s = grouped_ffn(x, 1, shared, ws=ws)
+    elif s is not None:
+        main.wait_stream(shared_stream)
+        s.record_stream(main)
     y = combine(rows, p2r, gate, s, shared_scale)
     if keep_intermediates:
         return y, dict(idx=idx, topk_logit=tl, gate=gate, offsets=off, sorted_pair=sp,

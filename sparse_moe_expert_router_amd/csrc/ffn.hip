@@ -18,7 +18,9 @@ static bool use_gemm(int P, int E, int H, int F) {
 // kGemmMinRows rows per expert) needs at most its size at that bound.
 size_t ffn_ws_bytes(int T, int k, int E, int H, int F) {
     const long P = (long)T * k;
-    const long Pg = P < (long)kGemmMinRows * E ? P : (long)kGemmMinRows * E;
+    // shapes the GEMM does not take stream every row through the GEMV
+    const bool gemm_ok = F % 128 == 0 && H % 256 == 0;
+    const long Pg = (gemm_ok && P >= (long)kGemmMinRows * E) ? (long)kGemmMinRows * E : P;
     const size_t g1 = gemv_ws_bytes((int)Pg, H, F, 1), g0 = gemv_ws_bytes((int)Pg, H, F, 0);
     size_t need = g1 > g0 ? g1 : g0;
     if (F % 128 == 0 && H % 256 == 0 && P >= (long)kGemmMinRows * E) {

@@ -466,6 +466,15 @@ static int pick_bm(int P, int E) {
     return avg >= 128 ? 256 : (avg >= 96 ? 128 : 64);
 }
 
+// Row tile of a single dense product (the shared expert, the router's
+// screening pass): the largest tile that still gives every compute unit a
+// workgroup, with `ncol` column tiles.
+static int pick_bm_dense(int M, int ncol) {
+    if ((long)((M + 255) / 256) * ncol >= 256) return 256;
+    if ((long)((M + 127) / 128) * ncol >= 256) return 128;
+    return 64;
+}
+
 static size_t tiles_bytes(int P, int E) {
     return (((size_t)(1 + 2 * max_tiles(P, E, 64)) * sizeof(int32_t)) + 255) & ~(size_t)255;
 }
@@ -491,7 +500,7 @@ static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t*
 
 hipError_t launch_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
     const int E = a.offsets ? a.E : 1;
-    const int BM = pick_bm(a.P, E);
+    const int BM = a.offsets ? pick_bm(a.P, E) : pick_bm_dense(a.P, a.F / (kBN / 2));
     const int mt = max_tiles(a.P, E, BM);
     int32_t* tiles = static_cast<int32_t*>(ws);
     uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + tiles_bytes(a.P, E));
@@ -521,7 +530,7 @@ hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t
     a.down.w = B;
     a.out_f32 = 1;
     a.rows = C;
-    const int BM = pick_bm(M, 1);
+    const int BM = pick_bm_dense(M, N / kBN);
     const int mt = max_tiles(M, 1, BM);
     int32_t* tiles = static_cast<int32_t*>(ws);
     uint16_t* Ain = const_cast<uint16_t*>(A);

@@ -27,10 +27,71 @@ __device__ __forceinline__ int row_token(const int32_t* sorted_pair, int k, int 
     return sorted_pair ? sorted_pair[r] / k : r;
 }
 
+constexpr bool kAwqPrefetch = false;  // next group's words in flight during the current group
+
+// Registers of one group of one word column: 32 code words (input rows
+// 32g..32g+31), the packed zero word and the 8 fp16 scales.
+struct AwqGroupRegs {
+    uint32_t w[32];
+    uint32_t z;
+    uint4 s;
+};
+
+__device__ __forceinline__ void awq_load_group(const int32_t* __restrict__ qw,
+                                               const int32_t* __restrict__ qz,
+                                               const uint16_t* __restrict__ sc, int O, int OW, int c,
+                                               int g, AwqGroupRegs& r) {
+    const int32_t* wp = qw + (size_t)g * 32 * OW + c;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) r.w[q] = (uint32_t)wp[(size_t)q * OW];
+    r.z = (uint32_t)qz[(size_t)g * OW + c];
+    r.s = *reinterpret_cast<const uint4*>(sc + (size_t)g * O + 8 * c);
+}
+
+template <int RCH>
+__device__ __forceinline__ void awq_group_dot(const AwqGroupRegs& r, const uint32_t* xs, int npairs,
+                                              const float* xsum, int ngroups, int lg,
+                                              float (&res)[8][RCH]) {
+    float acc[8][RCH];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < RCH; ++i) acc[j][i] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const uint32_t w0 = r.w[2 * q], w1 = r.w[2 * q + 1];
+        uint32_t v[8];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            // bytes: [w0.b, 0, w1.b, 0]
+            const uint32_t t = __builtin_amdgcn_perm(w1, w0, 0x0C000C00u | b | ((4u + b) << 16));
+            v[2 * b] = (t & 0x000F000Fu) | 0x43004300u;
+            v[2 * b + 1] = ((t >> 4) & 0x000F000Fu) | 0x43004300u;
+        }
+#pragma unroll
+        for (int i = 0; i < RCH; ++i) {
+            const uint32_t xp = xs[i * npairs + lg * 16 + q];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j][i] = dot2_bf16(v[j], xp, acc[j][i]);
+        }
+    }
+    const uint32_t sw[4] = {r.s.x, r.s.y, r.s.z, r.s.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int col = kAwqNib[j];
+        const float s = f16_to_f32((sw[col / 2] >> (16 * (col % 2))) & 0xFFFFu);
+        const float zc = 128.0f + (float)((r.z >> (4 * j)) & 15u);
+#pragma unroll
+        for (int i = 0; i < RCH; ++i)
+            res[j][i] = fmaf(s, fmaf(-zc, xsum[i * ngroups + lg], acc[j][i]), res[j][i]);
+    }
+}
+
 // Accumulate the AWQ GEMV of groups [g_begin, g_end) stepping by g_step for one
 // word column c of a projection (I inputs, OW = O/8 words per input row).
 // xs: activation pairs [RCH][npairs] (row pairs relative to group g_base),
 // xsum: [RCH][ngroups] group sums.  res[j][i]: column 8c + kAwqNib[j], row i.
+// The next group's words are in flight while the current one is computed.
 template <int RCH>
 __device__ __forceinline__ void awq_gemv_groups(const int32_t* __restrict__ qw,
                                                 const int32_t* __restrict__ qz,
@@ -39,44 +100,22 @@ __device__ __forceinline__ void awq_gemv_groups(const int32_t* __restrict__ qw,
                                                 int g_step, const uint32_t* xs, int npairs,
                                                 const float* xsum, int ngroups,
                                                 float (&res)[8][RCH]) {
-    for (int g = g_begin; g < g_end; g += g_step) {
-        float acc[8][RCH];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int i = 0; i < RCH; ++i) acc[j][i] = 0.0f;
-        const int32_t* wp = qw + (size_t)g * 32 * OW + c;
-        const int lg = g - g_base;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const uint32_t w0 = (uint32_t)wp[(size_t)(2 * q) * OW];
-            const uint32_t w1 = (uint32_t)wp[(size_t)(2 * q + 1) * OW];
-            uint32_t v[8];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                // bytes: [w0.b, 0, w1.b, 0]
-                const uint32_t t = __builtin_amdgcn_perm(w1, w0, 0x0C000C00u | b | ((4u + b) << 16));
-                v[2 * b] = (t & 0x000F000Fu) | 0x43004300u;
-                v[2 * b + 1] = ((t >> 4) & 0x000F000Fu) | 0x43004300u;
-            }
-#pragma unroll
-            for (int i = 0; i < RCH; ++i) {
-                const uint32_t xp = xs[i * npairs + lg * 16 + q];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j][i] = dot2_bf16(v[j], xp, acc[j][i]);
-            }
+    if (g_begin >= g_end) return;
+    if constexpr (kAwqPrefetch) {
+        AwqGroupRegs cur, nxt;
+        awq_load_group(qw, qz, sc, O, OW, c, g_begin, cur);
+        int g = g_begin;
+        for (; g + g_step < g_end; g += g_step) {
+            awq_load_group(qw, qz, sc, O, OW, c, g + g_step, nxt);
+            awq_group_dot<RCH>(cur, xs, npairs, xsum, ngroups, g - g_base, res);
+            cur = nxt;
         }
-        const uint32_t zw = (uint32_t)qz[(size_t)g * OW + c];
-        const uint4 s4 = *reinterpret_cast<const uint4*>(sc + (size_t)g * O + 8 * c);
-        const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int col = kAwqNib[j];
-            const float s = f16_to_f32((sw[col / 2] >> (16 * (col % 2))) & 0xFFFFu);
-            const float zc = 128.0f + (float)((zw >> (4 * j)) & 15u);
-#pragma unroll
-            for (int i = 0; i < RCH; ++i)
-                res[j][i] = fmaf(s, fmaf(-zc, xsum[i * ngroups + lg], acc[j][i]), res[j][i]);
+        awq_group_dot<RCH>(cur, xs, npairs, xsum, ngroups, g - g_base, res);
+    } else {
+        for (int g = g_begin; g < g_end; g += g_step) {
+            AwqGroupRegs cur;
+            awq_load_group(qw, qz, sc, O, OW, c, g, cur);
+            awq_group_dot<RCH>(cur, xs, npairs, xsum, ngroups, g - g_base, res);
         }
     }
 }
@@ -191,28 +230,67 @@ __global__ __launch_bounds__(512) void awq_gateup_kernel(GroupedArgs a, int KS, 
 // ---------------------------------------------------------------------------
 constexpr int kBfChunkK = 2048;
 
-template <int R>
-__device__ __forceinline__ void bf16_rows_dot(const uint16_t* __restrict__ W, int H, int k0, int nv,
-                                              int c0, int wave, int sub, int l16, const uint4* xs,
-                                              float (&acc)[4][8]) {
+// Dot products of NR weight rows (16-byte vectors, 16 lanes per row, vector
+// v of a row at rows[n][v]) with R activation rows staged in LDS (xs[i*xstride
+// + v]).  U vectors of every row are loaded before any is used, so NR*U loads
+// per lane are in flight.
+template <int R, int NR, int U, int RA>
+__device__ __forceinline__ void bf16_stream_dot(const uint4* const (&rows)[NR], int nv, int l16,
+                                                const uint4* xs, int xstride, float (&acc)[4][RA]) {
+    int v = l16;
+    for (; v + 16 * (U - 1) < nv; v += 16 * U) {
+        uint4 w[U][NR];
 #pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {
-        const int col = c0 + (wave % 2) * 16 + ps * 4 + sub;
-        const uint4* wr = reinterpret_cast<const uint4*>(W + (size_t)col * H + k0);
-        for (int v = l16; v < nv; v += 16) {
-            const uint4 w = wr[v];
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int n = 0; n < NR; ++n) w[u][n] = rows[n][v + 16 * u];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                const uint4 xv = xs[i * (kBfChunkK / 8) + v];
-                float t = acc[ps][i];
-                t = dot2_bf16(w.x, xv.x, t);
-                t = dot2_bf16(w.y, xv.y, t);
-                t = dot2_bf16(w.z, xv.z, t);
-                t = dot2_bf16(w.w, xv.w, t);
-                acc[ps][i] = t;
+                const uint4 xv = xs[i * xstride + v + 16 * u];
+#pragma unroll
+                for (int n = 0; n < NR; ++n) {
+                    float t = acc[n][i];
+                    t = dot2_bf16(w[u][n].x, xv.x, t);
+                    t = dot2_bf16(w[u][n].y, xv.y, t);
+                    t = dot2_bf16(w[u][n].z, xv.z, t);
+                    t = dot2_bf16(w[u][n].w, xv.w, t);
+                    acc[n][i] = t;
+                }
+            }
+    }
+    for (; v < nv; v += 16) {
+        uint4 w[NR];
+#pragma unroll
+        for (int n = 0; n < NR; ++n) w[n] = rows[n][v];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const uint4 xv = xs[i * xstride + v];
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                float t = acc[n][i];
+                t = dot2_bf16(w[n].x, xv.x, t);
+                t = dot2_bf16(w[n].y, xv.y, t);
+                t = dot2_bf16(w[n].z, xv.z, t);
+                t = dot2_bf16(w[n].w, xv.w, t);
+                acc[n][i] = t;
             }
         }
     }
+}
+
+template <int R, int RA>
+__device__ __forceinline__ void bf16_rows_dot(const uint16_t* __restrict__ W, int H, int k0, int nv,
+                                              int c0, int wave, int sub, int l16, const uint4* xs,
+                                              float (&acc)[4][RA]) {
+    const uint4* rows[4];
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+        const int col = c0 + (wave % 2) * 16 + ps * 4 + sub;
+        rows[ps] = reinterpret_cast<const uint4*>(W + (size_t)col * H + k0);
+    }
+    bf16_stream_dot<R, 4, 2>(rows, nv, l16, xs, kBfChunkK / 8, acc);
 }
 
 template <int RCH>
@@ -233,11 +311,11 @@ __global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, int KS,
     const uint16_t* W = (mat ? a.up.w : a.gate.w) + (size_t)e * F * H;
     for (int rc = r0; rc < r1; rc += RCH) {
         const int nr = min(RCH, r1 - rc);
-        float acc[4][8];
+        float acc[4][RCH];
 #pragma unroll
         for (int ps = 0; ps < 4; ++ps)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[ps][i] = 0.0f;
+            for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
         for (int k0 = kb; k0 < ke; k0 += kBfChunkK) {
             const int kl = min(kBfChunkK, ke - k0), nv = kl / 8;
             __syncthreads();
@@ -249,7 +327,7 @@ __global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, int KS,
             __syncthreads();
             auto body = [&](auto rtag) {
                 constexpr int R = decltype(rtag)::value;
-                bf16_rows_dot<R>(W, H, k0, nv, c0, wave, sub, l16, xs, acc);
+                bf16_rows_dot<R, RCH>(W, H, k0, nv, c0, wave, sub, l16, xs, acc);
             };
             dispatch_rows<RCH>(nr, body);
         }
@@ -273,11 +351,47 @@ __global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, int KS,
     }
 }
 
-// SwiGLU of the reduced gate/up partials for rows [rc, rc+nr) into LDS as
-// bf16 pairs h2[RCH][F/2] (the product rounded to bf16 once).
+// SwiGLU of the gate/up partials summed over the KS input splits: one bf16
+// pair (the product rounded once) per thread, h[r][F/2].
+__device__ __forceinline__ uint32_t swiglu_pair(const float* __restrict__ part, int KS, int P, int F,
+                                                int r, int f) {
+    float hv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        float g = 0.0f, up = 0.0f;
+        for (int ks = 0; ks < KS; ++ks) {
+            const float* pp = part + ((size_t)ks * P + r) * (2 * F);
+            g += pp[f + u];
+            up += pp[F + f + u];
+        }
+        hv[u] = silu(g) * up;
+    }
+    return pack_bf16x2(hv[0], hv[1]);
+}
+
+// With several input splits the SwiGLU is formed once per row here, instead of
+// in every down-projection workgroup that reads the row.
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restrict__ part, int KS,
+                                                            int P, int F, uint32_t* __restrict__ h) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)P * (F / 2)) return;
+    const int r = (int)(i / (F / 2)), f = 2 * (int)(i % (F / 2));
+    h[i] = swiglu_pair(part, KS, P, F, r, f);
+}
+
+// Rows [rc, rc+nr) of h into LDS as bf16 pairs h2[RCH][F/2]: copied from hsrc
+// when the SwiGLU was formed by swiglu_reduce_kernel, else formed here.
 template <int RCH>
-__device__ __forceinline__ void stage_swiglu(const float* __restrict__ part, int KS, int P, int F,
-                                             int rc, int nr, uint32_t* h2) {
+__device__ __forceinline__ void stage_swiglu(const float* __restrict__ part,
+                                             const uint32_t* __restrict__ hsrc, int KS, int P,
+                                             int F, int rc, int nr, uint32_t* h2) {
+    if (hsrc) {
+        for (int it = threadIdx.x; it < RCH * (F / 2); it += blockDim.x) {
+            const int i = it / (F / 2);
+            h2[it] = i < nr ? hsrc[(size_t)(rc + i) * (F / 2) + it % (F / 2)] : 0u;
+        }
+        return;
+    }
     for (int it = threadIdx.x; it < RCH * (F / 2); it += blockDim.x) {
         const int i = it / (F / 2), f = 2 * (it % (F / 2));
         float hv[2] = {0.0f, 0.0f};
@@ -302,7 +416,8 @@ __device__ __forceinline__ void stage_swiglu(const float* __restrict__ part, int
 // ---------------------------------------------------------------------------
 template <int RCH>
 __global__ __launch_bounds__(512) void awq_down_kernel(GroupedArgs a, int KS, int OWC,
-                                                       const float* __restrict__ part) {
+                                                       const float* __restrict__ part,
+                                                       const uint32_t* __restrict__ hsrc) {
     __shared__ uint32_t xs[RCH * kGemvMaxKPairs];
     __shared__ float xsum[RCH * 64];
     extern __shared__ float red[];  // [RCH][8*OWC]
@@ -319,7 +434,7 @@ __global__ __launch_bounds__(512) void awq_down_kernel(GroupedArgs a, int KS, in
     for (int rc = r0; rc < r1; rc += RCH) {
         const int nr = min(RCH, r1 - rc);
         __syncthreads();
-        stage_swiglu<RCH>(part, KS, a.P, F, rc, nr, xs);
+        stage_swiglu<RCH>(part, hsrc, KS, a.P, F, rc, nr, xs);
         __syncthreads();
         stage_group_sums<RCH>(xs, npairs, G, xsum);
         __syncthreads();
@@ -349,34 +464,21 @@ __global__ __launch_bounds__(512) void awq_down_kernel(GroupedArgs a, int KS, in
 // bf16 down: grid (expert slot, H/(16*npass) row chunks); block 256; 16 lanes
 // per weight row; each WG covers 16*npass output rows.
 // ---------------------------------------------------------------------------
-template <int R, int NPASS>
+template <int R, int NPASS, int RA>
 __device__ __forceinline__ void bf16_down_dot(const uint16_t* __restrict__ W, int F, int o0,
                                               int wave, int sub, int l16, const uint4* hv,
-                                              float (&acc)[4][8]) {
-    const int nv = F / 8;
+                                              float (&acc)[4][RA]) {
+    const uint4* rows[NPASS];
 #pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-        const int o = o0 + ps * 16 + wave * 4 + sub;
-        const uint4* wr = reinterpret_cast<const uint4*>(W + (size_t)o * F);
-        for (int v = l16; v < nv; v += 16) {
-            const uint4 w = wr[v];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const uint4 xv = hv[i * (F / 8) + v];
-                float t = acc[ps][i];
-                t = dot2_bf16(w.x, xv.x, t);
-                t = dot2_bf16(w.y, xv.y, t);
-                t = dot2_bf16(w.z, xv.z, t);
-                t = dot2_bf16(w.w, xv.w, t);
-                acc[ps][i] = t;
-            }
-        }
-    }
+    for (int ps = 0; ps < NPASS; ++ps)
+        rows[ps] = reinterpret_cast<const uint4*>(W + (size_t)(o0 + ps * 16 + wave * 4 + sub) * F);
+    bf16_stream_dot<R, NPASS, (NPASS >= 4 ? 2 : 4)>(rows, F / 8, l16, hv, F / 8, acc);
 }
 
 template <int RCH, int NPASS>
 __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
-                                                        const float* __restrict__ part) {
+                                                        const float* __restrict__ part,
+                                                        const uint32_t* __restrict__ hsrc) {
     constexpr int npass = NPASS;
     __shared__ uint32_t h2[RCH * kGemvMaxKPairs];
     __shared__ float outv[64][RCH];
@@ -393,16 +495,16 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
     for (int rc = r0; rc < r1; rc += RCH) {
         const int nr = min(RCH, r1 - rc);
         __syncthreads();
-        stage_swiglu<RCH>(part, KS, a.P, F, rc, nr, h2);
+        stage_swiglu<RCH>(part, hsrc, KS, a.P, F, rc, nr, h2);
         __syncthreads();
-        float acc[4][8];
+        float acc[4][RCH];
 #pragma unroll
         for (int ps = 0; ps < 4; ++ps)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[ps][i] = 0.0f;
+            for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
         auto body = [&](auto rtag) {
             constexpr int R = decltype(rtag)::value;
-            bf16_down_dot<R, NPASS>(W, F, o0, wave, sub, l16, hv, acc);
+            bf16_down_dot<R, NPASS, RCH>(W, F, o0, wave, sub, l16, hv, acc);
         };
         dispatch_rows<RCH>(nr, body);
 #pragma unroll
@@ -449,12 +551,20 @@ int gemv_ksplit(const GroupedArgs& a) {
     return ks;
 }
 
+static size_t part_bytes(int P, int F, int ks) {
+    return ((size_t)ks * P * 2 * F * sizeof(float) + 255) & ~(size_t)255;
+}
+
 size_t gemv_ws_bytes(int P, int H, int F, int awq) {
-    if (!awq) return (size_t)8 * P * 2 * F * sizeof(float);  // at most 8 splits
-    GroupedArgs a{};
-    a.H = H;
-    a.awq = awq;
-    return (size_t)gemv_ksplit(a) * P * 2 * F * sizeof(float);
+    int ks = 8;  // at most 8 splits for bf16
+    if (awq) {
+        GroupedArgs a{};
+        a.H = H;
+        a.awq = awq;
+        ks = gemv_ksplit(a);
+    }
+    // partial sums, then h [P][F] bf16
+    return part_bytes(P, F, ks) + (size_t)P * F * sizeof(uint16_t);
 }
 
 static int down_owc(int OW) {
@@ -474,42 +584,59 @@ static int row_phases(int OW) {
 }
 
 template <int RCH>
-static hipError_t launch_gemv_rch(const GroupedArgs& a, float* part, hipStream_t s) {
+static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s) {
     const int slots = a.offsets ? (a.P < a.E ? a.P : a.E) : 1;
     const int F = a.F, H = a.H;
+    const int KS = gemv_ksplit(a);
+    float* part = static_cast<float*>(ws);
+    uint32_t* hbuf = nullptr;
+    if (KS > 1) hbuf = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + part_bytes(a.P, F, KS));
     if (a.awq) {
-        const int KS = gemv_ksplit(a);
+      if constexpr (RCH <= 2) {
         const int OW = F / 8;
         const int RP = row_phases(OW);
         const size_t red_bytes = (size_t)RCH * F * sizeof(float);
         hipLaunchKernelGGL(awq_gateup_kernel<RCH>, dim3(slots, 2 * KS), dim3(OW * RP), red_bytes, s,
                            a, KS, part);
+        if (hbuf) {
+            const long pairs = (long)a.P * (F / 2);
+            hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
+                               s, (const float*)part, KS, a.P, F, hbuf);
+        }
         const int OWd = H / 8, OWC = down_owc(OWd);
         const int RPd = row_phases(OWC);
         hipLaunchKernelGGL(awq_down_kernel<RCH>, dim3(slots, OWd / OWC), dim3(OWC * RPd),
                            (size_t)RCH * 8 * OWC * sizeof(float), s, a, KS, OWC,
-                           (const float*)part);
+                           (const float*)part, (const uint32_t*)hbuf);
+      } else {
+        return hipErrorInvalidValue;  // AWQ takes at most two rows per pass
+      }
     } else {
-        const int KS = gemv_ksplit(a);
         hipLaunchKernelGGL(bf16_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS,
                            part);
+        if (hbuf) {
+            const long pairs = (long)a.P * (F / 2);
+            hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
+                               s, (const float*)part, KS, a.P, F, hbuf);
+        }
         // rows per down workgroup: 64, or 16 when few experts are active
         if ((long)slots * (H / 64) >= 1024)
             hipLaunchKernelGGL((bf16_down_kernel<RCH, 4>), dim3(slots, H / 64), dim3(256), 0, s, a, KS,
-                               (const float*)part);
+                               (const float*)part, (const uint32_t*)hbuf);
         else
             hipLaunchKernelGGL((bf16_down_kernel<RCH, 1>), dim3(slots, H / 16), dim3(256), 0, s, a, KS,
-                               (const float*)part);
+                               (const float*)part, (const uint32_t*)hbuf);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GroupedArgs& a, void* ws, hipStream_t s) {
-    float* part = static_cast<float*>(ws);
-    // rows per pass: the shared expert sees every token; a routed expert at
-    // decode sees one or two, so two rows per pass keeps registers low
-    if (!a.offsets && a.T > 2) return a.awq ? launch_gemv_rch<4>(a, part, s) : launch_gemv_rch<8>(a, part, s);
-    return launch_gemv_rch<2>(a, part, s);
+    // rows per pass: a bf16 shared expert sees every token (all of a decode
+    // batch in one pass); a routed expert at decode sees one or two, and the
+    // AWQ kernels keep two rows per pass to hold the next group's words in
+    // registers
+    if (!a.offsets && a.T > 2 && !a.awq) return launch_gemv_rch<16>(a, ws, s);
+    return launch_gemv_rch<2>(a, ws, s);
 }
 
 }  // namespace moe

@@ -15,12 +15,57 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Exact logits.  One wave per expert row; lanes split the hidden dimension;
-// a tile of up to 16 tokens is staged in LDS in chunks of kChunk columns.
-// grid = (ceil(E / kWavesPerWg), ceil(T / 16)), block = 64 * kWavesPerWg.
+// a tile of up to 16 tokens is staged in LDS in chunks of kLogitChunk
+// columns (one chunk at H = 2560).  Each lane loads its whole share of the
+// router row before the tile is staged, so the row streams in while the
+// activations are copied.
+// grid = (ceil(E / kLogitWaves), ceil(T / 16)), block = 64 * kLogitWaves.
 // ---------------------------------------------------------------------------
 constexpr int kLogitTok = 16;
-constexpr int kLogitChunk = 1024;
-constexpr int kLogitWaves = 8;
+constexpr int kLogitChunk = 2560;
+constexpr int kLogitVecs = kLogitChunk / 8 / kWave;  // 16-byte vectors per lane per chunk
+constexpr int kLogitWaves = 4;
+
+// Sum a[0..15] over the 64 lanes of a wave.  Halving exchange: at each of the
+// first four steps a lane keeps half of its tokens and adds its partner's
+// share of them; the last two steps add single values.  Afterwards lane L
+// holds the total of token ((L >> 2) & 15) reordered as tok_of_lane() says.
+__device__ __forceinline__ double wave_reduce16(double (&a)[kLogitTok], int lane) {
+    double b[8], c[4], d[2], e;
+    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double send = h5 ? a[j] : a[j + 8];
+        const double keep = h5 ? a[j + 8] : a[j];
+        b[j] = keep + shfl_xor_f64(send, 32);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const double send = h4 ? b[j] : b[j + 4];
+        const double keep = h4 ? b[j + 4] : b[j];
+        c[j] = keep + shfl_xor_f64(send, 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const double send = h3 ? c[j] : c[j + 2];
+        const double keep = h3 ? c[j + 2] : c[j];
+        d[j] = keep + shfl_xor_f64(send, 8);
+    }
+    {
+        const double send = h2 ? d[0] : d[1];
+        const double keep = h2 ? d[1] : d[0];
+        e = keep + shfl_xor_f64(send, 4);
+    }
+    e += shfl_xor_f64(e, 2);
+    e += shfl_xor_f64(e, 1);
+    return e;
+}
+
+// Token held by lane L after wave_reduce16: bit 5 chose the upper 8, bit 4
+// the upper 4 of those, bit 3 the upper 2, bit 2 the upper one.
+__device__ __forceinline__ int tok_of_lane(int lane) {
+    return ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+}
 
 __global__ __launch_bounds__(kLogitWaves * kWave) void exact_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int E,
@@ -36,6 +81,14 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void exact_logits_kernel(
     for (int h0 = 0; h0 < H; h0 += kLogitChunk) {
         const int len = min(kLogitChunk, H - h0);  // multiple of 8
         const int vecs = len / 8;
+        uint4 w4[kLogitVecs];
+#pragma unroll
+        for (int j = 0; j < kLogitVecs; ++j) {
+            const int c = lane + j * kWave;
+            w4[j] = (e < E && c < vecs)
+                        ? *reinterpret_cast<const uint4*>(wr + (size_t)e * H + h0 + c * 8)
+                        : make_uint4(0, 0, 0, 0);
+        }
         __syncthreads();
         for (int v = threadIdx.x; v < kLogitTok * (kLogitChunk / 8); v += blockDim.x) {
             const int t = v / (kLogitChunk / 8), c = v % (kLogitChunk / 8);
@@ -45,40 +98,34 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void exact_logits_kernel(
             xs[v] = val;
         }
         __syncthreads();
-        if (e < E) {
-            for (int c = lane; c < vecs; c += kWave) {
-                const uint4 w4 = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + h0 + c * 8);
-                const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
-                double wd[8];
+#pragma unroll
+        for (int j = 0; j < kLogitVecs; ++j) {
+            const int c = lane + j * kWave;
+            if (c >= vecs) break;
+            const uint32_t ww[4] = {w4[j].x, w4[j].y, w4[j].z, w4[j].w};
+            double wd[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                wd[2 * i] = (double)bf16_to_f32(ww[i] & 0xFFFFu);
+                wd[2 * i + 1] = (double)bf16_to_f32(ww[i] >> 16);
+            }
+#pragma unroll
+            for (int t = 0; t < kLogitTok; ++t) {
+                const uint4 x4 = xs[t * (kLogitChunk / 8) + c];
+                const uint32_t xx[4] = {x4.x, x4.y, x4.z, x4.w};
+                double a = acc[t];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    wd[2 * i] = (double)bf16_to_f32(ww[i] & 0xFFFFu);
-                    wd[2 * i + 1] = (double)bf16_to_f32(ww[i] >> 16);
+                    a = fma(wd[2 * i], (double)bf16_to_f32(xx[i] & 0xFFFFu), a);
+                    a = fma(wd[2 * i + 1], (double)bf16_to_f32(xx[i] >> 16), a);
                 }
-#pragma unroll
-                for (int t = 0; t < kLogitTok; ++t) {
-                    const uint4 x4 = xs[t * (kLogitChunk / 8) + c];
-                    const uint32_t xx[4] = {x4.x, x4.y, x4.z, x4.w};
-                    double a = acc[t];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        a = fma(wd[2 * i], (double)bf16_to_f32(xx[i] & 0xFFFFu), a);
-                        a = fma(wd[2 * i + 1], (double)bf16_to_f32(xx[i] >> 16), a);
-                    }
-                    acc[t] = a;
-                }
+                acc[t] = a;
             }
         }
     }
-    if (e >= E) return;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-#pragma unroll
-        for (int t = 0; t < kLogitTok; ++t) acc[t] += shfl_xor_f64(acc[t], m);
-    }
-#pragma unroll
-    for (int t = 0; t < kLogitTok; ++t)
-        if (lane == t && t0 + t < T) logits[(size_t)(t0 + t) * E + e] = (float)acc[t];
+    const double tot = wave_reduce16(acc, lane);
+    const int t = t0 + tok_of_lane(lane);
+    if (e < E && (lane & 3) == 0 && t < T) logits[(size_t)t * E + e] = (float)tot;
 }
 
 hipError_t launch_exact_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E,

@@ -112,3 +112,11 @@ def test_workspace_sizes_monotone_in_tokens():
                   (moe.OP_REFILL_SCORE, 10)):
         sizes = [moe.workspace_bytes(op, T, k, 512, 2560, 640) for T in (16, 256, 4096, 32768)]
         assert sizes == sorted(sizes), (op, sizes)
+
+
+def test_streaming_workspace_covers_every_row_when_the_gemm_cannot_run():
+    # width 96 is not a multiple of the GEMM's 128-column tile, so every row of
+    # every expert goes through the streaming kernels: the workspace keeps growing
+    sizes = [moe.workspace_bytes(moe.OP_GROUPED_FFN, T, 2, 8, 256, 96) for T in (100, 1000, 10000)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    assert sizes[2] >= 9 * sizes[1]

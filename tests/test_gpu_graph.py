@@ -1,0 +1,35 @@
+"""The layer replayed from a HIP graph: every replay, with eager work and
+synchronisation between replays, gives the eager result bit for bit."""
+import pytest
+import torch
+
+import workloads
+from tests.gpu_helpers import require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,side_stream", [("tiny_bf16", False), ("decode_awq", True)])
+def test_layer_graph_replays_match_eager(name, side_stream):
+    moe = require_gpu()
+    w = workloads.get(name)
+    d = workloads.generate(w, device="cuda")
+    other = workloads.generate(w, seed=7, device="cuda")
+    ws, sws = moe.Workspace(), moe.Workspace()
+    side = torch.cuda.Stream() if side_stream else None
+    kw = dict(ws=ws, shared_stream=side, shared_ws=sws)
+    ref = moe.moe_layer(d["x"], d["router"], w.k, d["experts"], d["shared"], **kw).clone()
+    ref_other = moe.moe_layer(other["x"], other["router"], w.k, other["experts"], other["shared"],
+                              **kw).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y = moe.moe_layer(d["x"], d["router"], w.k, d["experts"], d["shared"], **kw)
+    for _ in range(3):
+        # eager work on the same workspaces between replays
+        y2 = moe.moe_layer(other["x"], other["router"], w.k, other["experts"], other["shared"], **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, ref_other)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)

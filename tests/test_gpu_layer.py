@@ -62,6 +62,20 @@ def test_layer_is_deterministic():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["decode_bf16", "tiny_bf16"])
+def test_layer_with_shared_expert_on_a_second_stream(name):
+    """The shared expert beside the routed path on its own stream gives the same bits."""
+    moe = require_gpu()
+    w = workloads.get(name)
+    d = workloads.generate(w, device="cuda")
+    ref = moe.moe_layer(d["x"], d["router"], w.k, d["experts"], d["shared"]).clone()
+    side = torch.cuda.Stream()
+    for _ in range(3):
+        y = moe.moe_layer(d["x"], d["router"], w.k, d["experts"], d["shared"], shared_stream=side)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+
+
 # ----------------------------------------------------------------------------- Refill-RMS
 
 def _gpu_refill(moe, d, w, keep, batches=1):

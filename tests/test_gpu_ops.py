@@ -143,7 +143,9 @@ def _random_routing(T, k, E, seed):
                                        (1100, 8, 2, 256, 128),    # 275 rows: 256-row tiles + tails
                                        (8, 4, 2, 2560, 640),      # full width, streaming
                                        (16, 512, 10, 2560, 640),  # decode geometry, streaming
-                                       (100, 4, 2, 2560, 640)])   # full width, MFMA
+                                       (100, 4, 2, 2560, 640),    # full width, MFMA
+                                       (400, 8, 2, 256, 96)])     # width the MFMA path does not take:
+                                                                  # 100 rows per expert streamed
 def test_grouped_ffn_matches_oracle(fmt, T, E, k, H, F):
     moe = require_gpu()
     w = _wl(T, H, E, F=F, fmt=fmt)
