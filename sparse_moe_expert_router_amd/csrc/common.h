@@ -38,6 +38,16 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// (a & m) | c as one v_and_or_b32.  A VOP3 instruction on gfx9 takes no
+// literal operand, so with both constants written as literals the compiler
+// falls back to a separate AND and OR; here the mask travels in a VGPR and
+// the constant in an SGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "s"(c));
+    return r;
+}
+
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
 // Which group of a segmented list (offsets[0..n], non-decreasing) holds item `i`:

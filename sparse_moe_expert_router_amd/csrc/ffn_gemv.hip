@@ -65,8 +65,8 @@ __device__ __forceinline__ void awq_group_dot(const AwqGroupRegs& r, const uint3
         for (int b = 0; b < 4; ++b) {
             // bytes: [w0.b, 0, w1.b, 0]
             const uint32_t t = __builtin_amdgcn_perm(w1, w0, 0x0C000C00u | b | ((4u + b) << 16));
-            v[2 * b] = (t & 0x000F000Fu) | 0x43004300u;
-            v[2 * b + 1] = ((t >> 4) & 0x000F000Fu) | 0x43004300u;
+            v[2 * b] = and_or(t, 0x000F000Fu, 0x43004300u);
+            v[2 * b + 1] = and_or(t >> 4, 0x000F000Fu, 0x43004300u);
         }
 #pragma unroll
         for (int i = 0; i < RCH; ++i) {
@@ -415,7 +415,7 @@ __device__ __forceinline__ void stage_swiglu(const float* __restrict__ part,
 // AWQ down: grid (expert slot, OW/OWC column chunks); block = OWC * RP.
 // ---------------------------------------------------------------------------
 template <int RCH>
-__global__ __launch_bounds__(512) void awq_down_kernel(GroupedArgs a, int KS, int OWC,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void awq_down_kernel(GroupedArgs a, int KS, int OWC,
                                                        const float* __restrict__ part,
                                                        const uint32_t* __restrict__ hsrc) {
     __shared__ uint32_t xs[RCH * kGemvMaxKPairs];
