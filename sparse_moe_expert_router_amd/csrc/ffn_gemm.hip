@@ -83,10 +83,18 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
     if (e == 1023) tiles[0] = scan[1023];
 }
 
-__device__ __forceinline__ int xcd_remap(int p, int G) {
-    const int q = G / kXcd, r = G % kXcd;
-    const int x = p % kXcd, i = p / kXcd;
-    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+// Workgroup b runs on XCD b % 8.  The grid is an upper bound on the work (the
+// tile count is only known on the device); the `total` real work items are
+// split into 8 contiguous ranges, XCD x taking range x with its lowest-numbered
+// workgroups, so every XCD gets an equal share and the surplus workgroups of
+// every XCD exit.  Returns -1 for a surplus workgroup.  Needs gridDim a
+// multiple of 8 and at least total rounded up to a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+    const int q = (total + kXcd - 1) / kXcd;
+    const int x = b % kXcd, i = b / kXcd;
+    if (i >= q) return -1;
+    const int l = x * q + i;
+    return l < total ? l : -1;
 }
 
 // Packing order {0,2,4,6,1,3,5,7}: nibble j holds column awq_perm(j) of its word.
@@ -271,9 +279,9 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kBK];
     __shared__ __attribute__((aligned(16))) float2 Ps[2][kBN];  // AWQ (s, -(16 + z) s) per column
 
-    const int l = xcd_remap(blockIdx.x, gridDim.x);
+    const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
+    if (l < 0) return;
     const int tile = l / NT, nt = l % NT;
-    if (tile >= tiles[0]) return;
     const int e = tiles[1 + 2 * tile];
     const int m0 = tiles[2 + 2 * tile];
     const int m1 = a.offsets ? min(m0 + BM, (int)a.offsets[e + 1]) : min(m0 + BM, a.P);
@@ -459,6 +467,9 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
 // ---------------------------------------------------------------------------
 static int max_tiles(int P, int E, int BM) { return (P + BM - 1) / BM + E; }
 
+// Grid for `mt` row tiles x `nt` column tiles: a multiple of the XCD count.
+static dim3 gemm_grid(int mt, int nt) { return dim3((unsigned)(((long)mt * nt + kXcd - 1) / kXcd * kXcd)); }
+
 // Row tile from the average rows per non-empty expert.
 static int pick_bm(int P, int E) {
     const int active = P < E ? P : E;
@@ -486,14 +497,14 @@ static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t*
                            hipStream_t s) {
     const int NT1 = a.F / (kBN / 2), NT2 = a.H / kBN;
     if (a.awq) {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, true, BM>), dim3(mt * NT1), dim3(GemmShape<BM>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, true, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, true, BM>), dim3(mt * NT2), dim3(GemmShape<BM>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, true, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT2);
     } else {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, false, BM>), dim3(mt * NT1), dim3(GemmShape<BM>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, false, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, BM>), dim3(mt * NT2), dim3(GemmShape<BM>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT2);
     }
 }
@@ -538,13 +549,13 @@ hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t
                        tiles);
     const int NT = N / kBN;
     if (BM == 256)
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 256>), dim3(mt * NT), dim3(GemmShape<256>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 256>), gemm_grid(mt, NT), dim3(GemmShape<256>::NT), 0,
                            s, a, tiles, Ain, NT);
     else if (BM == 128)
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 128>), dim3(mt * NT), dim3(GemmShape<128>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 128>), gemm_grid(mt, NT), dim3(GemmShape<128>::NT), 0,
                            s, a, tiles, Ain, NT);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 64>), dim3(mt * NT), dim3(GemmShape<64>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 64>), gemm_grid(mt, NT), dim3(GemmShape<64>::NT), 0,
                            s, a, tiles, Ain, NT);
     return hipGetLastError();
 }
