@@ -48,7 +48,14 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
     return r;
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+// silu(a) = a / (1 + e^-a) with the hardware base-2 exponential and
+// reciprocal (v_exp_f32, v_rcp_f32, each within about one ulp): a few ulp of
+// fp32 in all, far below the bf16 rounding that every caller applies to
+// silu(gate) * up.  Large negative a gives e^-a = inf and a * 0 = -0.
+__device__ __forceinline__ float silu(float a) {
+    const float e = __builtin_amdgcn_exp2f(-a * 1.4426950408889634f);  // log2(e)
+    return a * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // Which group of a segmented list (offsets[0..n], non-decreasing) holds item `i`:
 // the largest g with offsets[g] <= i, restricted to non-empty groups.

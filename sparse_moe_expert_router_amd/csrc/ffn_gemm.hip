@@ -50,6 +50,15 @@ constexpr int kXcd = 8;
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
+// Orders a wave's own LDS accesses (writes by some lanes, then reads by
+// others): LDS instructions of one wave complete in issue order, so only the
+// compiler must be kept from moving them across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
 // Tile table: tiles[0] = number of tiles, then pairs (expert, first row).
 // ---------------------------------------------------------------------------
@@ -425,40 +434,74 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
 #undef MOE_LOAD
 #undef MOE_PARAMS
 
-    // ---- epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile
-    const int rbase = m0 + wm * S::MW + 4 * (lane / 16);
+    // ---- epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile.
+    // Each wave passes its tile through a private 8 KB LDS region (the stages
+    // are free after one block barrier) as fp32, 16 rows at a time; row
+    // strides of 64 + 4 (32 + 4) floats put the four lane groups' rows on
+    // different banks.  It then writes whole 16-byte vectors of a row.  The
+    // region is the wave's own, so only the wave's LDS accesses need ordering.
+    __syncthreads();
+    float* st = reinterpret_cast<float*>(
+        NTHR / kWave > 4 ? (wave < 4 ? reinterpret_cast<char*>(&As[0][0]) + wave * 8192
+                                     : reinterpret_cast<char*>(&Bs[0][0]) + (wave - 4) * 8192)
+                         : reinterpret_cast<char*>(&Bs[0][0]) + wave * 8192);
+    const int wrow = m0 + wm * S::MW;  // first row of the wave tile
     if (MODE == MODE_GATEUP) {
+        constexpr int HC = S::NW / 2, LD = HC + 4;  // 32 h columns per wave
+        const int hcol = n0 + wn * HC;
 #pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
+        for (int mi = 0; mi < TM; ++mi) {
 #pragma unroll
-            for (int nj = 0; nj < TN / 2; ++nj) {
-                const int col = n0 + wn * (S::NW / 2) + nj * 16 + lane % 16;
+            for (int nj = 0; nj < TN / 2; ++nj)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = rbase + mi * 16 + r;
-                    if (row < m1) {
-                        const float g = acc[mi][nj][r], u = acc[mi][nj + TN / 2][r];
-                        hbuf[(size_t)row * F + col] = (uint16_t)f32_to_bf16_bits(silu(g) * u);
-                    }
-                }
-            }
+                for (int r = 0; r < 4; ++r)
+                    st[(4 * (lane / 16) + r) * LD + nj * 16 + lane % 16] = silu(acc[mi][nj][r]) * acc[mi][nj + TN / 2][r];
+            wave_lds_sync();
+            const int rr = lane / 4, ch = lane % 4;  // 16 rows x 4 chunks of 8 columns
+            const float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
+            const float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
+            const int row = wrow + mi * 16 + rr;
+            if (row < m1)
+                *reinterpret_cast<uint4*>(&hbuf[(size_t)row * F + hcol + ch * 8]) =
+                    make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
+                               pack_bf16x2(v1.z, v1.w));
+            wave_lds_sync();
+        }
     } else {
+        constexpr int LD = S::NW + 4;  // 64 output columns per wave
+        const int ocol = n0 + wn * S::NW;
 #pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
+        for (int mi = 0; mi < TM; ++mi) {
 #pragma unroll
-            for (int nj = 0; nj < TN; ++nj) {
-                const int col = n0 + wn * S::NW + nj * 16 + lane % 16;
+            for (int nj = 0; nj < TN; ++nj)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = rbase + mi * 16 + r;
-                    if (row < m1) {
-                        const float v = acc[mi][nj][r];
-                        const size_t o = (size_t)row * H + col;
-                        if (a.out_f32) static_cast<float*>(a.rows)[o] = v;
-                        else static_cast<uint16_t*>(a.rows)[o] = (uint16_t)f32_to_bf16_bits(v);
-                    }
+                for (int r = 0; r < 4; ++r) st[(4 * (lane / 16) + r) * LD + nj * 16 + lane % 16] = acc[mi][nj][r];
+            wave_lds_sync();
+            if (a.out_f32) {
+                float* out = static_cast<float*>(a.rows);
+#pragma unroll
+                for (int pass = 0; pass < 4; ++pass) {  // 4 rows x 16 chunks of 4 floats
+                    const int rr = pass * 4 + lane / 16, ch = lane % 16;
+                    const int row = wrow + mi * 16 + rr;
+                    const float4 v = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 4]);
+                    if (row < m1) *reinterpret_cast<float4*>(&out[(size_t)row * H + ocol + ch * 4]) = v;
+                }
+            } else {
+                uint16_t* out = static_cast<uint16_t*>(a.rows);
+#pragma unroll
+                for (int pass = 0; pass < 2; ++pass) {  // 8 rows x 8 chunks of 8 values
+                    const int rr = pass * 8 + lane / 8, ch = lane % 8;
+                    const int row = wrow + mi * 16 + rr;
+                    const float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
+                    const float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
+                    if (row < m1)
+                        *reinterpret_cast<uint4*>(&out[(size_t)row * H + ocol + ch * 8]) =
+                            make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w),
+                                       pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w));
                 }
             }
+            wave_lds_sync();
+        }
     }
 }
 
