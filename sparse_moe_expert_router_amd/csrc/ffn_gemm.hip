@@ -521,11 +521,11 @@ static int pick_bm(int P, int E) {
 }
 
 // Row tile of a single dense product (the shared expert, the router's
-// screening pass): the largest tile that still gives every compute unit a
-// workgroup, with `ncol` column tiles.
+// screening pass): the largest tile that still gives every compute unit two
+// workgroups, with `ncol` column tiles.
 static int pick_bm_dense(int M, int ncol) {
-    if ((long)((M + 255) / 256) * ncol >= 256) return 256;
-    if ((long)((M + 127) / 128) * ncol >= 256) return 128;
+    if ((long)((M + 255) / 256) * ncol >= 512) return 256;
+    if ((long)((M + 127) / 128) * ncol >= 512) return 128;
     return 64;
 }
 

@@ -282,12 +282,81 @@ __device__ __forceinline__ float wave_exact_logit(const uint16_t* __restrict__ x
     return (float)acc;
 }
 
+// Exact fp32 logits of four (token, expert) pairs at once: lane group
+// g = lane / 16 takes expert e_g (e_g < 0: none) and 16 lanes split the
+// hidden dimension; fp64 FMAs, a 16-lane tree, one rounding.  Every lane
+// returns its group's logit.
+__device__ __forceinline__ float quad_exact_logit(const uint16_t* __restrict__ xr,
+                                                  const uint16_t* __restrict__ wr, int H, int e_g) {
+    const int l16 = threadIdx.x % 16;
+    double acc = 0.0;
+    if (e_g >= 0) {
+        const uint4* wv = reinterpret_cast<const uint4*>(wr + (size_t)e_g * H);
+        const uint4* xv = reinterpret_cast<const uint4*>(xr);
+        for (int c = l16; c < H / 8; c += 16) {
+            const uint4 x4 = xv[c];
+            const uint4 w4 = wv[c];
+            const uint32_t xx[4] = {x4.x, x4.y, x4.z, x4.w};
+            const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc = fma((double)bf16_to_f32(xx[i] & 0xFFFFu), (double)bf16_to_f32(ww[i] & 0xFFFFu), acc);
+                acc = fma((double)bf16_to_f32(xx[i] >> 16), (double)bf16_to_f32(ww[i] >> 16), acc);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) acc += shfl_xor_f64(acc, m);
+    return (float)acc;
+}
+
+// Rank-ordered top K of n <= 64 distinct 64-bit keys held one per lane
+// (lanes >= n hold nothing): each lane counts the keys above its own through
+// the wave's LDS copy.  Writes the experts and logits of ranks < K and, with
+// gate, the renormalised gates of ranks < k.
+__device__ __forceinline__ void rank_emit(uint64_t key, int n, uint64_t* kbuf, float* lbuf, int K,
+                                          int k, int32_t* idx, float* topk_logit, float* gate,
+                                          size_t t) {
+    const int lane = threadIdx.x % kWave;
+    if (lane < n) kbuf[lane] = key;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int rank = kWave;
+    if (lane < n) {
+        rank = 0;
+        for (int i = 0; i < n; ++i) rank += kbuf[i] > key;
+    }
+    const int e = (int)(~(uint32_t)key);
+    const float l = float_from_order_key((uint32_t)(key >> 32));
+    if (rank < K) {
+        idx[t * K + rank] = e;
+        if (topk_logit) topk_logit[t * K + rank] = l;
+    }
+    if (gate) {
+        // the selected logits move to lane = rank, so that the gates are
+        // summed in the same order as the per-token top-k kernel sums them
+        if (rank < k) lbuf[rank] = l;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float my_l = lane < k ? lbuf[lane] : 0.0f;
+        const float l0 = lbuf[0];
+        const float p = lane < k ? expf(my_l - l0) : 0.0f;
+        const float z = wave_sum_f32(p);
+        if (lane < k) gate[t * k + lane] = p / z;
+    }
+}
+
 template <int VPL>
 __global__ __launch_bounds__(256) void route_refine_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ la,
     const double* __restrict__ wnorm, int T, int H, int E, int K, int k, int32_t* __restrict__ idx,
     float* __restrict__ topk_logit, float* __restrict__ gate) {
     __shared__ int cand[4][kWave];
+    __shared__ double lmax[4][kWave];
+    __shared__ uint64_t kbuf[4][kWave];
+    __shared__ float lbuf[4][kWave];
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
     const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;  // whole wave; no block barrier below
@@ -296,9 +365,15 @@ __global__ __launch_bounds__(256) void route_refine_kernel(
 
     // ||x_t|| (fp64) and the bound factor
     double xs = 0.0;
-    for (int h = lane; h < H; h += kWave) {
-        const double v = (double)bf16_to_f32(xr[h]);
-        xs = fma(v, v, xs);
+    for (int c = lane; c < H / 8; c += kWave) {
+        const uint4 x4 = reinterpret_cast<const uint4*>(xr)[c];
+        const uint32_t xx[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double a = (double)bf16_to_f32(xx[i] & 0xFFFFu), b = (double)bf16_to_f32(xx[i] >> 16);
+            xs = fma(a, a, xs);
+            xs = fma(b, b, xs);
+        }
     }
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) xs += shfl_xor_f64(xs, m);
@@ -307,6 +382,7 @@ __global__ __launch_bounds__(256) void route_refine_kernel(
     const double dabs = (double)H * ldexp(1.0, -100);
 
     double lo[VPL], hi[VPL];
+    double mylo = -INFINITY;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         const int e = v * kWave + lane;
@@ -319,32 +395,25 @@ __global__ __launch_bounds__(256) void route_refine_kernel(
             lo[v] = -INFINITY;
             hi[v] = -INFINITY;
         }
+        mylo = fmax(mylo, lo[v]);
     }
-    // K-th largest lower bound (K rounds of a wave max, removing one entry each)
-    double tau = 0.0;
-    {
-        double tmp[VPL];
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) tmp[v] = lo[v];
-        for (int r = 0; r < K; ++r) {
-            double best = -INFINITY;
-            int bi = 0x7FFFFFFF;
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) {
-                const int e = v * kWave + lane;
-                if (tmp[v] > best || (tmp[v] == best && e < bi)) { best = tmp[v]; bi = e; }
-            }
-#pragma unroll
-            for (int m = 1; m < kWave; m <<= 1) {
-                const double ob = __shfl_xor(best, m, kWave);
-                const int oi = __shfl_xor(bi, m, kWave);
-                if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-            }
-#pragma unroll
-            for (int v = 0; v < VPL; ++v)
-                if (v * kWave + lane == bi) tmp[v] = -INFINITY;
-            tau = best;
+    // tau: the K-th largest of the 64 lanes' largest lower bounds.  At least K
+    // lower bounds (those K lane maxima) reach it, so it does not exceed the
+    // K-th largest lower bound, and every expert that can be in the exact top
+    // K has an upper bound >= tau.
+    double tau = -INFINITY;
+    if (K <= kWave) {
+        lmax[wv][lane] = mylo;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        int rank = 0;
+        for (int i = 0; i < kWave; ++i) {
+            const double o = lmax[wv][i];
+            rank += (o > mylo) || (o == mylo && i < lane);
         }
+        const uint64_t hit = __ballot(rank == K - 1);
+        tau = lmax[wv][__ffsll((long long)hit) - 1];
     }
     // candidates: hi >= tau
     int ncand = 0;
@@ -361,42 +430,27 @@ __global__ __launch_bounds__(256) void route_refine_kernel(
         }
         ncand += n;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (ncand > kWave) overflow = true;
 
-    uint64_t key = 0;  // this lane's candidate (or nothing)
     if (!overflow) {
+        // exact logits of the candidates, four at a time; candidate j's logit
+        // ends in lane j
         float mine = 0.0f;
-        for (int j = 0; j < ncand; ++j) {
-            const int e = cand[wv][j];
-            const float l = wave_exact_logit(xr, wr + (size_t)e * H, H);
-            if (lane == j) mine = l;
-        }
-        if (lane < ncand) {
-            const int e = cand[wv][lane];
-            key = ((uint64_t)float_order_key(mine) << 32) | (uint32_t)(~e);
-        }
-        int my_e = 0;
-        float my_l = 0.0f;
-        for (int r = 0; r < K; ++r) {
-            const uint64_t best = wave_max_u64(key);
-            const int e = (int)(~(uint32_t)best);
-            if (key == best) key = 0;
-            if (lane == r) {
-                my_e = e;
-                my_l = float_from_order_key((uint32_t)(best >> 32));
+        for (int j0 = 0; j0 < ncand; j0 += 4) {
+            const int j = j0 + lane / 16;
+            const float l = quad_exact_logit(xr, wr, H, j < ncand ? cand[wv][j] : -1);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float lg = __shfl(l, g * 16, kWave);
+                if (lane == j0 + g) mine = lg;
             }
         }
-        if (lane < K) {
-            idx[(size_t)t * K + lane] = my_e;
-            if (topk_logit) topk_logit[(size_t)t * K + lane] = my_l;
-        }
-        if (gate) {
-            const float l0 = __shfl(my_l, 0, kWave);
-            const float p = lane < k ? expf(my_l - l0) : 0.0f;
-            const float z = wave_sum_f32(p);
-            if (lane < k) gate[(size_t)t * k + lane] = p / z;
-        }
+        uint64_t key = 0;
+        if (lane < ncand) key = ((uint64_t)float_order_key(mine) << 32) | (uint32_t)(~cand[wv][lane]);
+        rank_emit(key, ncand, kbuf[wv], lbuf[wv], K, k, idx, topk_logit, gate, (size_t)t);
         return;
     }
     // fallback: every logit of this token exactly (kept in the owning lane's
