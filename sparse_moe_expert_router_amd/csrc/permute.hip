@@ -14,7 +14,7 @@
 
 namespace moe {
 
-constexpr int kPermChunk = 2048;     // pairs per block in the multi-block path
+constexpr int kPermChunk = 512;      // pairs per block in the multi-block path
 constexpr int kSmallPairs = 4096;    // single-workgroup path up to this many pairs
 
 // Expert ids outside [0, E) are clamped so that every row stays inside the buffers.
@@ -109,34 +109,61 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
 }
 
 // Pass 2 (one block of 1024): counts[b][e] becomes the first row of block b's
-// pairs of expert e; offsets[] gets the expert boundaries.
+// pairs of expert e; offsets[] gets the expert boundaries.  Thread (s, e)
+// covers a contiguous segment s of the blocks for expert e (S = 1024 / E
+// segments), reading eight counts at a time so that their loads overlap.
+constexpr int kScanUnroll = 8;
+
 __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ counts, int nb,
                                                             int E, int P,
                                                             int32_t* __restrict__ offsets) {
-    __shared__ int tot[1024];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < E) {
-        for (int b = 0; b < nb; ++b) {
-            const int c = counts[(size_t)b * E + e];
-            counts[(size_t)b * E + e] = run;
-            run += c;
-        }
+    __shared__ int seg_tot[1024];  // [s][e]
+    __shared__ int tot[1024];      // expert totals, then their exclusive scan
+    const int S = 1024 / E;        // E <= 1024
+    const int s = threadIdx.x / E, e = threadIdx.x % E;
+    const bool on = s < S;
+    const int b0 = on ? (int)((long)nb * s / S) : 0, b1 = on ? (int)((long)nb * (s + 1) / S) : 0;
+    // 1. this segment's total
+    int sum = 0;
+    for (int b = b0; b < b1; b += kScanUnroll) {
+        int c[kScanUnroll];
+#pragma unroll
+        for (int u = 0; u < kScanUnroll; ++u) c[u] = b + u < b1 ? counts[(size_t)(b + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanUnroll; ++u) sum += c[u];
     }
-    tot[e] = e < E ? run : 0;
+    seg_tot[threadIdx.x] = on ? sum : 0;
+    __syncthreads();
+    // 2. expert totals and their exclusive scan (ascending expert)
+    const int t = threadIdx.x;
+    int run = 0;
+    if (t < E)
+        for (int q = 0; q < S; ++q) run += seg_tot[q * E + t];
+    tot[t] = t < E ? run : 0;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-        int v = e >= off ? tot[e - off] : 0;
+        const int v = t >= off ? tot[t - off] : 0;
         __syncthreads();
-        tot[e] += v;
+        tot[t] += v;
         __syncthreads();
     }
-    const int base = tot[e] - (e < E ? run : 0);
-    if (e < E) {
-        offsets[e] = base;
-        for (int b = 0; b < nb; ++b) counts[(size_t)b * E + e] += base;
+    if (t < E) offsets[t] = tot[t] - run;
+    if (t == 0) offsets[E] = P;
+    // 3. first row of each block's pairs: expert base + earlier segments + earlier blocks
+    if (on) {
+        int r = tot[e];  // inclusive: minus expert e's own total gives its base
+        for (int q = 0; q < S; ++q) r -= seg_tot[q * E + e] * (q >= s);
+        for (int b = b0; b < b1; b += kScanUnroll) {
+            int c[kScanUnroll];
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; ++u) c[u] = b + u < b1 ? counts[(size_t)(b + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; ++u) {
+                if (b + u < b1) counts[(size_t)(b + u) * E + e] = r;
+                r += c[u];
+            }
+        }
     }
-    if (e == 0) offsets[E] = P;
 }
 
 // Pass 3: one wave per block scatters its chunk in order.
