@@ -7,8 +7,9 @@ from ._lib import (EXPORTS, LIB_PATH, OP_GROUPED_FFN, OP_PERMUTE, OP_REFILL_SCOR
                    OUT_BF16, OUT_F32, MoeError, Workspace, combine, grouped_ffn, lib, moe_layer,
                    permute, prune_slice, refill_finalize, refill_score, route, router_norm_keep,
                    workspace_bytes)
+from .calibration import RefillCalibration
 
 __all__ = ["EXPORTS", "LIB_PATH", "OP_GROUPED_FFN", "OP_PERMUTE", "OP_REFILL_SCORE", "OP_ROUTE",
            "OUT_BF16", "OUT_F32", "MoeError", "Workspace", "combine", "grouped_ffn", "lib",
            "moe_layer", "permute", "prune_slice", "refill_finalize", "refill_score", "route",
-           "router_norm_keep", "workspace_bytes"]
+           "router_norm_keep", "workspace_bytes", "RefillCalibration"]
