@@ -40,6 +40,12 @@
  *              Refill-RMS); "rows" are expert outputs in grouped order:
  *              row r holds the output of pair sorted_pair[r].
  *  bf16 experts: gate, up [E][F][H]; down [E][H][F]  (row per output feature)
+ *  FP8 experts:  codes [E][O][I] uint8, OCP FP8 E4M3 (bias 7, max 448, no
+ *                infinities, S.1111.111 = NaN); block_scales [E][O/128][I/128]
+ *                fp32; w[e][o][i] = e4m3(codes[e][o][i]) * block_scales[e][o/128][i/128]
+ *                (the optional FP8 draft of the AWQ-g32 card stores routed
+ *                experts in E4M3 with explicit block scales; the 128 x 128
+ *                block is this library's reading).  I and O multiples of 128.
  *  AWQ experts:  for a projection with input dim I and output dim O
  *                  qweight [E][I][O/8] int32, qzeros [E][I/32][O/8] int32,
  *                  scales [E][I/32][O] fp16;
@@ -65,7 +71,7 @@ typedef enum {
     MOE_ERR_HIP = 5          /* a HIP call failed; see moe_last_hip_error()   */
 } moe_status;
 
-typedef enum { MOE_W_BF16 = 0, MOE_W_AWQ_G32 = 1 } moe_wfmt;
+typedef enum { MOE_W_BF16 = 0, MOE_W_AWQ_G32 = 1, MOE_W_FP8_BLOCK = 2 } moe_wfmt;
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_dtype;
 
 /* One projection of a bank of experts, input dim in_dim, output dim out_dim. */
@@ -76,6 +82,8 @@ typedef struct {
     const int32_t *qweight;   /* AWQ:  [E][in][out/8]                         */
     const int32_t *qzeros;    /* AWQ:  [E][in/32][out/8]                      */
     const uint16_t *scales;   /* AWQ:  [E][in/32][out] fp16                   */
+    const uint8_t *codes;     /* FP8:  [E][out][in] E4M3 (OCP)                */
+    const float *block_scales;/* FP8:  [E][out/128][in/128] fp32              */
 } moe_proj;
 
 /* A bank of SwiGLU experts: gate, up: hidden -> inter; down: inter -> hidden.

@@ -30,7 +30,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-BF16, AWQ = 0, 1
+BF16, AWQ, FP8 = 0, 1, 2
 
 
 def build(verbose: bool = False) -> str:
@@ -47,7 +47,8 @@ def build(verbose: bool = False) -> str:
 class _Proj(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("in_dim", ctypes.c_int32), ("out_dim", ctypes.c_int32),
                 ("w", ctypes.c_void_p), ("qweight", ctypes.c_void_p),
-                ("qzeros", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+                ("qzeros", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("bscales", ctypes.c_void_p)]
 
 
 class _Bank(ctypes.Structure):
@@ -77,6 +78,8 @@ def _load():
     lib.oracle_permute.argtypes = [P, i64, i64, i64, P, P, P]
     lib.oracle_proj_weight.restype = ctypes.c_double
     lib.oracle_proj_weight.argtypes = [ctypes.POINTER(_Proj), i64, i64, i64]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
     lib.oracle_pair_outputs.restype = None
     lib.oracle_pair_outputs.argtypes = [P, i64, i64, P, ctypes.POINTER(_Bank), P]
     lib.oracle_shared_outputs.restype = None
@@ -111,23 +114,26 @@ def _ptr(a):
 class Proj:
     """One projection of a bank of experts, as raw arrays (see moe_oracle.c for layouts)."""
 
-    def __init__(self, fmt, in_dim, out_dim, w=None, qweight=None, qzeros=None, scales=None):
+    def __init__(self, fmt, in_dim, out_dim, w=None, qweight=None, qzeros=None, scales=None,
+                 codes=None, bscales=None):
         self.fmt, self.in_dim, self.out_dim = fmt, int(in_dim), int(out_dim)
         self.w = None if w is None else _c(w, np.uint16)
         self.qweight = None if qweight is None else _c(qweight, np.int32)
         self.qzeros = None if qzeros is None else _c(qzeros, np.int32)
         self.scales = None if scales is None else _c(scales, np.uint16)
+        self.codes = None if codes is None else _c(codes, np.uint8)
+        self.bscales = None if bscales is None else _c(bscales, np.float32)
 
     def _struct(self):
         return _Proj(self.fmt, self.in_dim, self.out_dim, _ptr(self.w), _ptr(self.qweight),
-                     _ptr(self.qzeros), _ptr(self.scales))
+                     _ptr(self.qzeros), _ptr(self.scales), _ptr(self.codes), _ptr(self.bscales))
 
     def take(self, experts) -> "Proj":
         """Expert-granular slice (used by tests to pass only the experts they need)."""
         experts = np.asarray(experts, dtype=np.int64)
         pick = (lambda a: None if a is None else a[experts])
         return Proj(self.fmt, self.in_dim, self.out_dim, pick(self.w), pick(self.qweight),
-                    pick(self.qzeros), pick(self.scales))
+                    pick(self.qzeros), pick(self.scales), pick(self.codes), pick(self.bscales))
 
 
 class Bank:
@@ -156,6 +162,11 @@ def bank_from_tensors(d: dict, prefix: str = "") -> Bank:
                     Proj(BF16, H, F, w=d[prefix + "gate"]),
                     Proj(BF16, H, F, w=d[prefix + "up"]),
                     Proj(BF16, F, H, w=d[prefix + "down"]))
+    if fmt == "fp8":
+        E, F, H = d[prefix + "gate_codes"].shape
+        mk = lambda n, i, o: Proj(FP8, i, o, codes=d[prefix + n + "_codes"],
+                                  bscales=d[prefix + n + "_bscales"])
+        return Bank(E, H, F, mk("gate", H, F), mk("up", H, F), mk("down", F, H))
     E, H, F8 = d[prefix + "gate_qweight"].shape
     F = F8 * 8
     mk = lambda n, i, o: Proj(AWQ, i, o, qweight=d[prefix + n + "_qweight"],
@@ -212,6 +223,11 @@ def permute(idx: np.ndarray, E: int):
     pair_to_row = np.empty(T * k, np.int32)
     _load().oracle_permute(_ptr(ix), T, k, E, _ptr(offsets), _ptr(sorted_pair), _ptr(pair_to_row))
     return offsets, sorted_pair, pair_to_row
+
+
+def e4m3_value(code: int) -> float:
+    """Exact value of an OCP FP8 E4M3 code."""
+    return float(_load().oracle_e4m3_value(int(code)))
 
 
 def proj_weight(p: Proj, e: int, o: int, i: int) -> float:

@@ -19,6 +19,9 @@
  *  [AWQ]   "Qwen3.8-Flash-Next-AWQ-g32" card, sections "Checkpoint" and
  *          "Calibration": asymmetric W4A16, group 32, integer zero points,
  *          FP16 scales, codes clip(round(w/scale + zero), 0, 15), GEMM packing.
+ *  [FP8]   "Qwen3.8-Flash-Next-AWQ-g32" card, "Optional FP8 MTP": routed
+ *          experts stored in FP8 E4M3 with explicit block scales (the
+ *          128 x 128 block and fp32 scales are this oracle's reading).
  *  [RAZOR] "Qwen3.8-Flash-Next-RAZOR-65B-A6B-E256of512" card, section
  *          "Selection and calibration": Refill-RMS saliency, RMS conditional on
  *          the tokens routed to each expert, additive statistics, keep-set in
@@ -351,7 +354,7 @@ void oracle_permute(const int32_t *idx, int64_t T, int64_t k, int64_t E,
 /* O5/O6: one SwiGLU expert, bf16 or AWQ W4 weights                           */
 /* ------------------------------------------------------------------------- */
 
-enum { ORA_BF16 = 0, ORA_AWQ = 1 };
+enum { ORA_BF16 = 0, ORA_AWQ = 1, ORA_FP8 = 2 };
 
 /* One projection of a bank of experts (out x in per expert). */
 typedef struct {
@@ -361,6 +364,8 @@ typedef struct {
     const int32_t *qweight;  /* awq:  [E][in][out/8]                */
     const int32_t *qzeros;   /* awq:  [E][in/32][out/8]             */
     const uint16_t *scales;  /* awq:  [E][in/32][out] fp16          */
+    const uint8_t *codes;    /* fp8:  [E][out][in] E4M3              */
+    const float *bscales;    /* fp8:  [E][out/128][in/128] fp32      */
 } ora_proj;
 
 typedef struct {
@@ -375,12 +380,42 @@ static int awq_nibble_of_column(int c8)
     return (c8 % 2 == 0) ? c8 / 2 : 4 + c8 / 2;
 }
 
+/* OCP FP8 E4M3 code to its exact value: sign bit, 4 exponent bits with bias
+ * 7, 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); exponent
+ * field 15 with mantissa 7 is NaN (there are no infinities, so 448 is the
+ * largest finite magnitude). */
+static double e4m3_value(uint8_t c)
+{
+    int sign = c >> 7, ex = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (ex == 15 && m == 7)
+        return NAN;
+    if (ex == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, ex - 7);
+    return sign ? -v : v;
+}
+
+/* Exported for the tests: the value of every E4M3 code. */
+double oracle_e4m3_value(int code)
+{
+    return e4m3_value((uint8_t)code);
+}
+
 /* Weight W[e][o][i] of a projection, decoded to an exact double.
- * AWQ: w = (q - z) * s, q and z integers in 0..15, s fp16 ([AWQ]). */
+ * AWQ: w = (q - z) * s, q and z integers in 0..15, s fp16 ([AWQ]).
+ * FP8: w = e4m3(code) * block scale of the 128 x 128 block holding (o, i),
+ * the product of a 4-bit and a 24-bit significand, exact in double. */
 static double proj_weight(const ora_proj *p, int64_t e, int64_t o, int64_t i)
 {
     if (p->fmt == ORA_BF16)
         return bf16_value(p->w[(e * p->out_dim + o) * p->in_dim + i]);
+    if (p->fmt == ORA_FP8) {
+        int64_t ob = p->out_dim / 128, ib = p->in_dim / 128;
+        double s = (double)p->bscales[(e * ob + o / 128) * ib + i / 128];
+        return e4m3_value(p->codes[(e * p->out_dim + o) * p->in_dim + i]) * s;
+    }
     int64_t words = p->out_dim / 8, groups = p->in_dim / 32;
     int nib = awq_nibble_of_column((int)(o % 8));
     uint32_t qw = (uint32_t)p->qweight[(e * p->in_dim + i) * words + o / 8];

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 OP_ROUTE, OP_PERMUTE, OP_GROUPED_FFN, OP_REFILL_SCORE = 0, 1, 2, 3
-W_BF16, W_AWQ = 0, 1
+W_BF16, W_AWQ, W_FP8 = 0, 1, 2
 OUT_BF16, OUT_F32 = 0, 1
 
 EXPORTS = ["moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_refill_score",
@@ -37,7 +37,8 @@ class MoeError(RuntimeError):
 class _Proj(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("in_dim", ctypes.c_int32), ("out_dim", ctypes.c_int32),
                 ("w", ctypes.c_void_p), ("qweight", ctypes.c_void_p),
-                ("qzeros", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+                ("qzeros", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("block_scales", ctypes.c_void_p)]
 
 
 class _Experts(ctypes.Structure):
@@ -133,8 +134,13 @@ def experts_struct(bank: dict):
     fmt = bank["fmt"]
     if fmt == "bf16":
         E, F, H = bank["gate"].shape
-        mk = lambda t, i, o: _Proj(W_BF16, i, o, t.data_ptr(), None, None, None)
+        mk = lambda t, i, o: _Proj(W_BF16, i, o, t.data_ptr(), None, None, None, None, None)
         return _Experts(E, H, F, mk(bank["gate"], H, F), mk(bank["up"], H, F), mk(bank["down"], F, H))
+    if fmt == "fp8":
+        E, F, H = bank["gate_codes"].shape
+        mk = lambda n, i, o: _Proj(W_FP8, i, o, None, None, None, None, bank[n + "_codes"].data_ptr(),
+                                   bank[n + "_bscales"].data_ptr())
+        return _Experts(E, H, F, mk("gate", H, F), mk("up", H, F), mk("down", F, H))
     E, H, F8 = bank["gate_qweight"].shape
     F = F8 * 8
     mk = lambda n, i, o: _Proj(W_AWQ, i, o, None, bank[n + "_qweight"].data_ptr(),
@@ -145,6 +151,8 @@ def experts_struct(bank: dict):
 def bank_dims(bank: dict):
     if bank["fmt"] == "bf16":
         E, F, H = bank["gate"].shape
+    elif bank["fmt"] == "fp8":
+        E, F, H = bank["gate_codes"].shape
     else:
         E, H, F8 = bank["gate_qweight"].shape
         F = F8 * 8

@@ -48,6 +48,13 @@ bool proj_ok(const moe_proj& p, int fmt, int in_dim, int out_dim, int E, moe_sta
             *st = MOE_ERR_UNSUPPORTED;
             return false;
         }
+    } else if (fmt == MOE_W_FP8_BLOCK) {
+        if (!p.codes || !p.block_scales) { *st = MOE_ERR_NULL; return false; }
+        if (in_dim % 128 || out_dim % 128) { *st = MOE_ERR_UNSUPPORTED; return false; }
+        if (!aligned16(p.codes) || ((uintptr_t)p.block_scales % 4)) {
+            *st = MOE_ERR_UNSUPPORTED;
+            return false;
+        }
     } else {
         *st = MOE_ERR_UNSUPPORTED;
         return false;
@@ -221,6 +228,14 @@ moe_status moe_prune_slice(const int32_t* keep_idx, int32_t n_keep, const uint16
         if (sp[m]->fmt == MOE_W_BF16) {
             st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->w, const_cast<uint16_t*>(dp[m]->w),
                                                      in * out * sizeof(uint16_t), s));
+            if (st != MOE_OK) return st;
+        } else if (sp[m]->fmt == MOE_W_FP8_BLOCK) {
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->codes,
+                                                     const_cast<uint8_t*>(dp[m]->codes), in * out, s));
+            if (st != MOE_OK) return st;
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->block_scales,
+                                                     const_cast<float*>(dp[m]->block_scales),
+                                                     (in / 128) * (out / 128) * sizeof(float), s));
             if (st != MOE_OK) return st;
         } else {
             st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->qweight,

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 from scipy.special import softmax
 
-from tests import awq_ref
+from tests import awq_ref, fp8_ref
 from tests.helpers import bf16_bits_to_f64, f32_to_bf16_bits, random_bf16
 
 import oracle as O
@@ -41,6 +41,8 @@ def _awq_bank(rng, E, H, F, pow2_scales=False):
 def _dense(p: O.Proj) -> np.ndarray:
     if p.fmt == O.BF16:
         return bf16_bits_to_f64(p.w)
+    if p.fmt == O.FP8:
+        return fp8_ref.dequant_dense(p.codes, p.bscales)
     return awq_ref.dequant_dense(p.qweight, p.qzeros, p.scales)
 
 

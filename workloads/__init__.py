@@ -10,6 +10,8 @@ Value recipe (shared by every workload):
   * AWQ W4A16 g32 experts: every 4-bit code and zero point uniform in 0..15
     (a uniformly random int32 word has 8 independent uniform nibbles), fp16
     scales |N(0, 0.002)| + 1e-4 drawn in fp32 then rounded to fp16;
+  * FP8 block-scaled experts: N(0, 0.02) weights in fp32, per 128 x 128 block
+    scale = largest |w| / 448, codes = w / scale rounded to E4M3;
   * the pruned workload's keep-set: a seeded random choice of 256 of the 512
     base experts, listed in ascending index order.
 Each tensor draws from its own torch.Generator, seeded from (seed, copy,
@@ -58,6 +60,9 @@ WORKLOADS = {
     "decode_bf16": Workload("decode_bf16", T=16, H=2560, E=512, k=10, F=640, Fs=640, fmt="bf16"),
     # same geometry, AWQ W4A16 g32 routed experts, decode and prefill batches
     "decode_awq": Workload("decode_awq", T=16, H=2560, E=512, k=10, F=640, Fs=640, fmt="awq"),
+    # same geometry, FP8 E4M3 routed experts with 128 x 128 block scales
+    "decode_fp8": Workload("decode_fp8", T=16, H=2560, E=512, k=10, F=640, Fs=640, fmt="fp8"),
+    "prefill_fp8": Workload("prefill_fp8", T=4096, H=2560, E=512, k=10, F=640, Fs=640, fmt="fp8"),
     "prefill_awq": Workload("prefill_awq", T=4096, H=2560, E=512, k=10, F=640, Fs=640, fmt="awq"),
     # 256 of 512 experts kept; one packed row of 32768 tokens
     "pruned_awq": Workload("pruned_awq", T=32768, H=2560, E=256, k=10, F=640, Fs=640, fmt="awq",
@@ -155,9 +160,32 @@ def expert_bank(w: Workload, seed: int = 0, device="cpu", copy: int = 0, E: int 
                                            device)
             out[name + "_scales"] = _scales((E, i // 32, o), _gen(device, seed, copy, tid, 3),
                                             device)
+        elif fmt == "fp8":
+            assert o % 128 == 0 and i % 128 == 0
+            out[name + "_codes"], out[name + "_bscales"] = _fp8_blocks(
+                (E, o, i), _gen(device, seed, copy, tid, 4), device)
         else:
             raise ValueError(fmt)
     return out
+
+
+def _fp8_blocks(shape, g, device, chunk_rows=16):
+    """FP8 E4M3 codes and 128 x 128 block scales of N(0, 0.02) weights: each
+    block's scale is its largest |w| / 448 (the largest finite E4M3 value),
+    the codes are w / scale rounded to E4M3 by torch's conversion."""
+    E, O, I = shape
+    codes = torch.empty(shape, dtype=torch.uint8, device=device)
+    scales = torch.empty((E, O // 128, I // 128), dtype=torch.float32, device=device)
+    for e0 in range(0, E, chunk_rows):
+        n = min(chunk_rows, E - e0)
+        w = torch.randn((n, O, I), generator=g, device=device, dtype=torch.float32) * 0.02
+        blk = w.view(n, O // 128, 128, I // 128, 128)
+        amax = blk.abs().amax(dim=(2, 4))
+        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (blk / sc[:, :, None, :, None]).to(torch.float8_e4m3fn)
+        codes[e0:e0 + n] = q.view(torch.uint8).view(n, O, I)
+        scales[e0:e0 + n] = sc
+    return codes, scales
 
 
 def shared_bank(w: Workload, seed: int = 0, device="cpu", copy: int = 0) -> dict:
