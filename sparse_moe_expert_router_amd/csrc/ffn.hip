@@ -40,6 +40,7 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
     a.E = f.E;
     a.P = f.T * f.k;
     a.awq = f.ex->gate.fmt == MOE_W_AWQ_G32;
+    a.fp8 = f.ex->gate.fmt == MOE_W_FP8_BLOCK;
     a.offsets = f.offsets;
     a.sorted_pair = f.sorted_pair;
     auto pj = [](const moe_proj& p) {
@@ -48,6 +49,8 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
         d.qweight = p.qweight;
         d.qzeros = p.qzeros;
         d.scales = p.scales;
+        d.codes = p.codes;
+        d.bscales = p.block_scales;
         return d;
     };
     a.gate = pj(f.ex->gate);

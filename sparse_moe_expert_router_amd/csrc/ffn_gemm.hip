@@ -181,19 +181,44 @@ __device__ __forceinline__ void awq_split(const uint32_t (&rw)[RPT], uint32_t (&
     }
 }
 
+// FP8 B tile: a thread's chunk q (< BPER/2) is B-column q/2, inputs
+// 16*(q%2)..+15 of the step: 16 E4M3 codes, widened two at a time
+// (v_cvt_pk_f32_fp8), times the block scale, rounded to bf16 and stored as the
+// column's two 8-input LDS chunks.
+__device__ __forceinline__ void fp8_store_chunk(uint4 c, float sc, uint16_t* Bs, int q) {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], true);
+        o[2 * i] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+        o[2 * i + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+    }
+    const int bc = q / 2, kh = q % 2;
+    *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh)]) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh + 1)]) = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // Registers of one K step -> LDS stage (A chunks; bf16 B chunks or dequantised AWQ words).
-template <int MODE, bool AWQ, int BM>
+template <int MODE, int WF, int BM>
 __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APER],
                                             const uint4 (&rb)[GemmShape<BM>::BPER],
                                             const uint32_t (&rw)[GemmShape<BM>::RPT], const float2* Ps,
                                             uint16_t* As, uint16_t* Bs, int tid) {
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32 or FP8
+    (void)FP8;
     using S = GemmShape<BM>;
 #pragma unroll
     for (int i = 0; i < S::APER; ++i) {
         const int q = tid + i * S::NT;
         *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[i];
     }
-    if (!AWQ) {
+    if (FP8) {
+#pragma unroll
+        for (int i = 0; i < S::BPER / 2; ++i)
+            fp8_store_chunk(rb[i], __uint_as_float(rw[i]), Bs, tid + i * S::NT);
+    } else if (!AWQ) {
 #pragma unroll
         for (int i = 0; i < S::BPER; ++i) {
             const int q = tid + i * S::NT;
@@ -212,11 +237,13 @@ __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APE
 }
 
 // MFMA operand fragments of one K step from an LDS stage.
-template <int MODE, bool AWQ, int BM>
+template <int MODE, int WF, int BM>
 __device__ __forceinline__ void read_frags(const uint16_t* As, const uint16_t* Bs,
                                            bf16x8_t (&af)[GemmShape<BM>::TM],
                                            bf16x8_t (&bfr)[GemmShape<BM>::TN], int wm, int wn,
                                            int lane) {
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32 or FP8
+    (void)FP8;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
 #pragma unroll
@@ -236,7 +263,7 @@ __device__ __forceinline__ void read_frags(const uint16_t* As, const uint16_t* B
 // bf16 B chunks or one dequantised AWQ column) are cut into 8 slices, each
 // followed by 1/8 of this step's MFMAs; scheduling barriers keep the slices
 // in order, so that the VALU and LDS work issues while earlier MFMAs execute.
-template <int MODE, bool AWQ, int BM>
+template <int MODE, int WF, int BM>
 __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<BM>::TM],
                                                  const bf16x8_t (&bfr)[GemmShape<BM>::TN],
                                                  f32x4_t (&acc)[GemmShape<BM>::TM][GemmShape<BM>::TN],
@@ -244,6 +271,8 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
                                                  const uint4 (&rb)[GemmShape<BM>::BPER],
                                                  const uint32_t (&rw)[GemmShape<BM>::RPT],
                                                  const float2* Ps, uint16_t* As, uint16_t* Bs, int tid) {
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32 or FP8
+    (void)FP8;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
     constexpr int NM = TM * TN;  // MFMAs this step
@@ -262,7 +291,9 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
             const int q = tid + j * S::NT;
             *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[j];
         }
-        if (!AWQ) {
+        if (FP8) {
+            if (j < S::BPER / 2) fp8_store_chunk(rb[j], __uint_as_float(rw[j]), Bs, tid + j * S::NT);
+        } else if (!AWQ) {
             if (j < S::BPER) {
                 const int q = tid + j * S::NT;
                 *reinterpret_cast<uint4*>(&Bs[lds_off(q / 4, q % 4)]) = rb[j];
@@ -278,10 +309,12 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
     }
 }
 
-template <int MODE, bool AWQ, int BM>
+template <int MODE, int WF, int BM>
 __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(GroupedArgs a,
                                                                const int32_t* __restrict__ tiles,
                                                                uint16_t* __restrict__ hbuf, int NT) {
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32 or FP8
+    (void)FP8;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN, APER = S::APER, BPER = S::BPER, NTHR = S::NT;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
@@ -322,12 +355,27 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
     // threads < 256 also fetch one column's zero word and scale for the
     // per-step parameter table.
     const uint16_t* bsrc[BPER];
+    const uint8_t* fsrc[BPER / 2 > 0 ? BPER / 2 : 1];   // FP8 code chunks
+    const float* fscl[BPER / 2 > 0 ? BPER / 2 : 1];     // their block-scale rows
     const int32_t* wsrc = nullptr;
     const int32_t* zsrc = nullptr;
     const uint16_t* ssrc = nullptr;
     int pnib = 0;  // nibble of the parameter column in its zero word
     const int OW = NOUT / 8;
-    if (!AWQ) {
+    if (FP8) {
+#pragma unroll
+        for (int i = 0; i < BPER / 2; ++i) {
+            const int q = tid + i * NTHR;
+            const int bc = q / 2, kh = q % 2;
+            const bool upm = MODE == MODE_GATEUP && bc >= kBN / 2;
+            // select by value (a reference into the kernel-argument struct would force a stack copy)
+            const uint8_t* codes = MODE == MODE_DOWN ? a.down.codes : (upm ? a.up.codes : a.gate.codes);
+            const float* bsc = MODE == MODE_DOWN ? a.down.bscales : (upm ? a.up.bscales : a.gate.bscales);
+            const int col = MODE == MODE_GATEUP ? n0 + bc % (kBN / 2) : n0 + bc;
+            fsrc[i] = codes + (size_t)e * NOUT * K + (size_t)col * K + kh * 16;
+            fscl[i] = bsc + ((size_t)e * (NOUT / 128) + col / 128) * (K / 128);
+        }
+    } else if (!AWQ) {
 #pragma unroll
         for (int i = 0; i < BPER; ++i) {
             const int q = tid + i * NTHR;
@@ -384,6 +432,11 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
             PS = (uint32_t)ssrc[(size_t)kt_ * NOUT];                                          \
             _Pragma("unroll") for (int i = 0; i < S::RPT; ++i) RW[i] =                        \
                 (uint32_t)wsrc[(size_t)(k0_ + i) * OW];                                       \
+        } else if (FP8) {                                                                     \
+            _Pragma("unroll") for (int i = 0; i < BPER / 2; ++i) {                            \
+                RB[i] = *reinterpret_cast<const uint4*>(fsrc[i] + k0_);                       \
+                RW[i] = __float_as_uint(fscl[i][k0_ >> 7]);                                   \
+            }                                                                                 \
         } else {                                                                              \
             _Pragma("unroll") for (int i = 0; i < BPER; ++i) RB[i] =                          \
                 *reinterpret_cast<const uint4*>(bsrc[i] + k0_);                               \
@@ -407,7 +460,7 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
     MOE_PARAMS(pz0, ps0, 0);
     MOE_PARAMS(pz1, ps1, 1);
     __syncthreads();
-    store_stage<MODE, AWQ, BM>(ra0, rb0, rw0, Ps[0], As[0], Bs[0], tid);
+    store_stage<MODE, WF, BM>(ra0, rb0, rw0, Ps[0], As[0], Bs[0], tid);
     __syncthreads();
     // Loads past the end repeat the last step; the spare LDS stage absorbs the
     // last stores.  No branches inside a step: one scheduling region.  Stage 0
@@ -418,8 +471,8 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
         const int cur = kt & 1;
         MOE_LOAD(ra0, rb0, rw0, pz0, ps0, min(kt + 2, nk - 1));
         bf16x8_t af[TM], bfr[TN];
-        read_frags<MODE, AWQ, BM>(As[cur], Bs[cur], af, bfr, wm, wn, lane);
-        step_interleaved<MODE, AWQ, BM>(af, bfr, acc, ra1, rb1, rw1, Ps[cur ^ 1], As[cur ^ 1], Bs[cur ^ 1], tid);
+        read_frags<MODE, WF, BM>(As[cur], Bs[cur], af, bfr, wm, wn, lane);
+        step_interleaved<MODE, WF, BM>(af, bfr, acc, ra1, rb1, rw1, Ps[cur ^ 1], As[cur ^ 1], Bs[cur ^ 1], tid);
         MOE_PARAMS(pz0, ps0, cur);  // parameters of step kt+2 (table cur held step kt's)
         __syncthreads();
 #pragma unroll
@@ -539,15 +592,20 @@ template <int BM>
 static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int mt,
                            hipStream_t s) {
     const int NT1 = a.F / (kBN / 2), NT2 = a.H / kBN;
-    if (a.awq) {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, true, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
+    if (a.fp8) {
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, 2, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, true, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 2, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
+                           s, a, tiles, hbuf, NT2);
+    } else if (a.awq) {
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, 1, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
+                           s, a, tiles, hbuf, NT1);
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 1, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT2);
     } else {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, false, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, 0, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 0, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT2);
     }
 }
@@ -592,13 +650,13 @@ hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t
                        tiles);
     const int NT = N / kBN;
     if (BM == 256)
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 256>), gemm_grid(mt, NT), dim3(GemmShape<256>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 0, 256>), gemm_grid(mt, NT), dim3(GemmShape<256>::NT), 0,
                            s, a, tiles, Ain, NT);
     else if (BM == 128)
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 128>), gemm_grid(mt, NT), dim3(GemmShape<128>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 0, 128>), gemm_grid(mt, NT), dim3(GemmShape<128>::NT), 0,
                            s, a, tiles, Ain, NT);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, false, 64>), gemm_grid(mt, NT), dim3(GemmShape<64>::NT), 0,
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 0, 64>), gemm_grid(mt, NT), dim3(GemmShape<64>::NT), 0,
                            s, a, tiles, Ain, NT);
     return hipGetLastError();
 }

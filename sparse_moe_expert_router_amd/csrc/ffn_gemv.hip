@@ -351,6 +351,134 @@ __global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, int KS,
     }
 }
 
+// ---------------------------------------------------------------------------
+// FP8 E4M3 experts with 128 x 128 block scales (AWQ-g32 card, "Optional FP8
+// MTP": routed experts in E4M3 with explicit block scales).  Same mapping as
+// the bf16 kernels, 16 lanes per weight row, but a 16-byte vector holds 16
+// weights: v_cvt_pk_f32_fp8 widens two codes at a time (every E4M3 value is
+// exactly a bf16 value), v_cvt_pk_bf16_f32 packs them and v_dot2_f32_bf16
+// takes the activation pairs; the vector's dot product is scaled by its
+// block's scale (a vector never crosses a 128-input block).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fp8_to_bf16x8(uint4 c, uint32_t (&o)[8]) {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], true);
+        o[2 * i] = pack_bf16x2(lo[0], lo[1]);
+        o[2 * i + 1] = pack_bf16x2(hi[0], hi[1]);
+    }
+}
+
+// Dot products of NR FP8 weight rows (row n: codes rows[n], scales srow[n]
+// per 128-input block, first input k0) with R activation rows in LDS
+// (xs[i * xstride + v], 8 bf16 per uint4, input 8v relative to k0).
+template <int R, int NR, int RA>
+__device__ __forceinline__ void fp8_stream_dot(const uint4* const (&rows)[NR], const float* const (&srow)[NR],
+                                               int k0, int nv, int l16, const uint4* xs, int xstride,
+                                               float (&acc)[4][RA]) {
+    for (int v = l16; v < nv; v += 16) {  // v: 16-input vector
+        uint4 w[NR];
+        float sc[NR];
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            w[n] = rows[n][v];
+            sc[n] = srow[n][(k0 + 16 * v) >> 7];
+        }
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            uint32_t wb[8];
+            fp8_to_bf16x8(w[n], wb);
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint4 x0 = xs[i * xstride + 2 * v], x1 = xs[i * xstride + 2 * v + 1];
+                float t = 0.0f;
+                t = dot2_bf16(wb[0], x0.x, t);
+                t = dot2_bf16(wb[1], x0.y, t);
+                t = dot2_bf16(wb[2], x0.z, t);
+                t = dot2_bf16(wb[3], x0.w, t);
+                t = dot2_bf16(wb[4], x1.x, t);
+                t = dot2_bf16(wb[5], x1.y, t);
+                t = dot2_bf16(wb[6], x1.z, t);
+                t = dot2_bf16(wb[7], x1.w, t);
+                acc[n][i] = fmaf(sc[n], t, acc[n][i]);
+            }
+        }
+    }
+}
+
+// FP8 gate/up: grid (expert slot, F/32 column chunks, KS input splits);
+// block 256 (4 waves).  Waves 0,1: gate columns c0..c0+31, waves 2,3: up.
+template <int RCH>
+__global__ __launch_bounds__(256) void fp8_gateup_kernel(GroupedArgs a, int KS, float* __restrict__ part) {
+    __shared__ uint4 xs[RCH * kBfChunkK / 8];
+    __shared__ float outv[64][RCH];
+    int r0, r1;
+    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    if (!a.offsets) { r0 = 0; r1 = a.T; }
+    if (e < 0) return;
+    const int H = a.H, F = a.F;
+    const int ks = blockIdx.z;
+    // input split on 16-weight vectors
+    const int kb = (int)((long)H / 16 * ks / KS) * 16, ke = (int)((long)H / 16 * (ks + 1) / KS) * 16;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int sub = lane / 16, l16 = lane % 16;
+    const int c0 = blockIdx.y * 32;
+    const int mat = wave / 2;
+    const ProjDev& pj = mat ? a.up : a.gate;
+    const uint8_t* W = pj.codes + (size_t)e * F * H;
+    const float* S = pj.bscales + (size_t)e * (F / 128) * (H / 128);
+    for (int rc = r0; rc < r1; rc += RCH) {
+        const int nr = min(RCH, r1 - rc);
+        float acc[4][RCH];
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
+        for (int k0 = kb; k0 < ke; k0 += kBfChunkK) {
+            const int kl = min(kBfChunkK, ke - k0), nx = kl / 8;
+            __syncthreads();
+            for (int it = threadIdx.x; it < nr * nx; it += blockDim.x) {
+                const int i = it / nx, v = it % nx;
+                const int t = row_token(a.sorted_pair, a.k, rc + i);
+                xs[i * (kBfChunkK / 8) + v] = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + k0)[v];
+            }
+            __syncthreads();
+            const uint4* rows[4];
+            const float* srow[4];
+#pragma unroll
+            for (int ps = 0; ps < 4; ++ps) {
+                const int col = c0 + (wave % 2) * 16 + ps * 4 + sub;
+                rows[ps] = reinterpret_cast<const uint4*>(W + (size_t)col * H + k0);
+                srow[ps] = S + (size_t)(col / 128) * (H / 128);
+            }
+            auto body = [&](auto rtag) {
+                constexpr int R = decltype(rtag)::value;
+                fp8_stream_dot<R, 4, RCH>(rows, srow, k0, kl / 16, l16, xs, kBfChunkK / 8, acc);
+            };
+            dispatch_rows<RCH>(nr, body);
+        }
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) {
+                float v = acc[ps][i];
+                v += __shfl_xor(v, 1, kWave);
+                v += __shfl_xor(v, 2, kWave);
+                v += __shfl_xor(v, 4, kWave);
+                v += __shfl_xor(v, 8, kWave);
+                if (l16 == 0) outv[wave * 16 + ps * 4 + sub][i] = v;
+            }
+        __syncthreads();
+        for (int it = threadIdx.x; it < 64 * nr; it += blockDim.x) {
+            const int o = it % 64, i = it / 64;
+            const int m = o / 32, col = c0 + o % 32;
+            part[((size_t)ks * a.P + rc + i) * (2 * F) + m * F + col] = outv[o][i];
+        }
+    }
+}
+
 // SwiGLU of the gate/up partials summed over the KS input splits: one bf16
 // pair (the product rounded once) per thread, h[r][F/2].
 __device__ __forceinline__ uint32_t swiglu_pair(const float* __restrict__ part, int KS, int P, int F,
@@ -475,7 +603,8 @@ __device__ __forceinline__ void bf16_down_dot(const uint16_t* __restrict__ W, in
     bf16_stream_dot<R, NPASS, (NPASS >= 4 ? 2 : 4)>(rows, F / 8, l16, hv, F / 8, acc);
 }
 
-template <int RCH, int NPASS>
+// The down projection of bf16 experts, or (FP8) of FP8 experts.
+template <int RCH, int NPASS, bool FP8 = false>
 __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
                                                         const float* __restrict__ part,
                                                         const uint32_t* __restrict__ hsrc) {
@@ -504,7 +633,21 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
             for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
         auto body = [&](auto rtag) {
             constexpr int R = decltype(rtag)::value;
-            bf16_down_dot<R, NPASS, RCH>(W, F, o0, wave, sub, l16, hv, acc);
+            if constexpr (FP8) {
+                const uint4* rows[NPASS];
+                const float* srow[NPASS];
+                const uint8_t* C = a.down.codes + (size_t)e * H * F;
+                const float* S = a.down.bscales + (size_t)e * (H / 128) * (F / 128);
+#pragma unroll
+                for (int ps = 0; ps < NPASS; ++ps) {
+                    const int o = o0 + ps * 16 + wave * 4 + sub;
+                    rows[ps] = reinterpret_cast<const uint4*>(C + (size_t)o * F);
+                    srow[ps] = S + (size_t)(o / 128) * (F / 128);
+                }
+                fp8_stream_dot<R, NPASS, RCH>(rows, srow, 0, F / 16, l16, hv, F / 8, acc);
+            } else {
+                bf16_down_dot<R, NPASS, RCH>(W, F, o0, wave, sub, l16, hv, acc);
+            }
         };
         dispatch_rows<RCH>(nr, body);
 #pragma unroll
@@ -611,6 +754,19 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s)
       } else {
         return hipErrorInvalidValue;  // AWQ takes at most two rows per pass
       }
+    } else if (a.fp8) {
+        hipLaunchKernelGGL(fp8_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS, part);
+        if (hbuf) {
+            const long pairs = (long)a.P * (F / 2);
+            hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
+                               s, (const float*)part, KS, a.P, F, hbuf);
+        }
+        if ((long)slots * (H / 64) >= 1024)
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4, true>), dim3(slots, H / 64), dim3(256), 0, s, a, KS,
+                               (const float*)part, (const uint32_t*)hbuf);
+        else
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1, true>), dim3(slots, H / 16), dim3(256), 0, s, a, KS,
+                               (const float*)part, (const uint32_t*)hbuf);
     } else {
         hipLaunchKernelGGL(bf16_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS,
                            part);
@@ -635,7 +791,8 @@ hipError_t launch_gemv(const GroupedArgs& a, void* ws, hipStream_t s) {
     // batch in one pass); a routed expert at decode sees one or two, and the
     // AWQ kernels keep two rows per pass to hold the next group's words in
     // registers
-    if (!a.offsets && a.T > 2 && !a.awq) return launch_gemv_rch<16>(a, ws, s);
+    if (!a.offsets && a.T > 2 && !a.awq && !a.fp8) return launch_gemv_rch<16>(a, ws, s);
+    if (!a.offsets && a.T > 2 && a.fp8) return launch_gemv_rch<8>(a, ws, s);
     return launch_gemv_rch<2>(a, ws, s);
 }
 

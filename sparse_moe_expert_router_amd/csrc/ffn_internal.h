@@ -14,12 +14,15 @@ struct ProjDev {
     const int32_t* qweight;   // awq  [E][in][out/8]
     const int32_t* qzeros;    // awq  [E][in/32][out/8]
     const uint16_t* scales;   // awq  [E][in/32][out] fp16
+    const uint8_t* codes;     // fp8  [E][out][in] E4M3
+    const float* bscales;     // fp8  [E][out/128][in/128]
 };
 
 struct GroupedArgs {
     const uint16_t* x;          // [T][H] bf16
     int T, k, H, F, E, P;       // P = T*k rows
-    int awq;                    // 1: AWQ g32, 0: bf16
+    int awq;                    // 1: AWQ g32, 0: bf16 or fp8
+    int fp8;                    // 1: FP8 E4M3 with 128 x 128 block scales
     const int32_t* offsets;     // [E+1] or nullptr (identity: E == 1, row r = token r)
     const int32_t* sorted_pair; // [P] or nullptr
     ProjDev gate, up, down;
