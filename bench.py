@@ -267,7 +267,7 @@ def cpu_baseline(w, d, seconds):
         used = np.unique(idx)
         import torch
         sel = torch.as_tensor(used, dtype=torch.long, device=d["x"].device)
-        bank = O.bank_from_tensors({k: (v if isinstance(v, str) else workloads.bits(v.index_select(0, sel)))
+        bank = O.bank_from_tensors({k: (v if isinstance(v, (str, float)) else workloads.bits(v.index_select(0, sel)))
                                     for k, v in d["experts"].items()})
         local = np.searchsorted(used, idx).astype(np.int32)
         if w.refill:

@@ -30,7 +30,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-BF16, AWQ, FP8 = 0, 1, 2
+BF16, AWQ, FP8, NVFP4 = 0, 1, 2, 3
 
 
 def build(verbose: bool = False) -> str:
@@ -48,7 +48,8 @@ class _Proj(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("in_dim", ctypes.c_int32), ("out_dim", ctypes.c_int32),
                 ("w", ctypes.c_void_p), ("qweight", ctypes.c_void_p),
                 ("qzeros", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("codes", ctypes.c_void_p), ("bscales", ctypes.c_void_p)]
+                ("codes", ctypes.c_void_p), ("bscales", ctypes.c_void_p),
+                ("gscales", ctypes.c_void_p), ("wglobal", ctypes.c_void_p), ("aglobal", ctypes.c_float)]
 
 
 class _Bank(ctypes.Structure):
@@ -80,6 +81,14 @@ def _load():
     lib.oracle_proj_weight.argtypes = [ctypes.POINTER(_Proj), i64, i64, i64]
     lib.oracle_e4m3_value.restype = ctypes.c_double
     lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
+    lib.oracle_e2m1_value.restype = ctypes.c_double
+    lib.oracle_e2m1_value.argtypes = [ctypes.c_int]
+    lib.oracle_e2m1_round.restype = ctypes.c_int
+    lib.oracle_e2m1_round.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_round.restype = ctypes.c_int
+    lib.oracle_e4m3_round.argtypes = [ctypes.c_float]
+    lib.oracle_nvfp4_quantize.restype = None
+    lib.oracle_nvfp4_quantize.argtypes = [P, i64, ctypes.c_float, P]
     lib.oracle_pair_outputs.restype = None
     lib.oracle_pair_outputs.argtypes = [P, i64, i64, P, ctypes.POINTER(_Bank), P]
     lib.oracle_shared_outputs.restype = None
@@ -115,8 +124,11 @@ class Proj:
     """One projection of a bank of experts, as raw arrays (see moe_oracle.c for layouts)."""
 
     def __init__(self, fmt, in_dim, out_dim, w=None, qweight=None, qzeros=None, scales=None,
-                 codes=None, bscales=None):
+                 codes=None, bscales=None, gscales=None, wglobal=None, aglobal=1.0):
         self.fmt, self.in_dim, self.out_dim = fmt, int(in_dim), int(out_dim)
+        self.gscales = None if gscales is None else _c(gscales, np.uint8)
+        self.wglobal = None if wglobal is None else _c(wglobal, np.float32)
+        self.aglobal = float(np.float32(aglobal))
         self.w = None if w is None else _c(w, np.uint16)
         self.qweight = None if qweight is None else _c(qweight, np.int32)
         self.qzeros = None if qzeros is None else _c(qzeros, np.int32)
@@ -126,14 +138,16 @@ class Proj:
 
     def _struct(self):
         return _Proj(self.fmt, self.in_dim, self.out_dim, _ptr(self.w), _ptr(self.qweight),
-                     _ptr(self.qzeros), _ptr(self.scales), _ptr(self.codes), _ptr(self.bscales))
+                     _ptr(self.qzeros), _ptr(self.scales), _ptr(self.codes), _ptr(self.bscales),
+                     _ptr(self.gscales), _ptr(self.wglobal), self.aglobal)
 
     def take(self, experts) -> "Proj":
         """Expert-granular slice (used by tests to pass only the experts they need)."""
         experts = np.asarray(experts, dtype=np.int64)
         pick = (lambda a: None if a is None else a[experts])
         return Proj(self.fmt, self.in_dim, self.out_dim, pick(self.w), pick(self.qweight),
-                    pick(self.qzeros), pick(self.scales), pick(self.codes), pick(self.bscales))
+                    pick(self.qzeros), pick(self.scales), pick(self.codes), pick(self.bscales),
+                    pick(self.gscales), pick(self.wglobal), self.aglobal)
 
 
 class Bank:
@@ -162,6 +176,14 @@ def bank_from_tensors(d: dict, prefix: str = "") -> Bank:
                     Proj(BF16, H, F, w=d[prefix + "gate"]),
                     Proj(BF16, H, F, w=d[prefix + "up"]),
                     Proj(BF16, F, H, w=d[prefix + "down"]))
+    if fmt == "nvfp4":
+        E, F, H2 = d[prefix + "gate_fp4"].shape
+        H = H2 * 2
+        mk = lambda n, i, o, ga: Proj(NVFP4, i, o, codes=d[prefix + n + "_fp4"],
+                                      gscales=d[prefix + n + "_fp4scales"],
+                                      wglobal=d[prefix + n + "_wglobal"], aglobal=ga)
+        ga_gu, ga_dn = float(d[prefix + "act_global_gu"]), float(d[prefix + "act_global_down"])
+        return Bank(E, H, F, mk("gate", H, F, ga_gu), mk("up", H, F, ga_gu), mk("down", F, H, ga_dn))
     if fmt == "fp8":
         E, F, H = d[prefix + "gate_codes"].shape
         mk = lambda n, i, o: Proj(FP8, i, o, codes=d[prefix + n + "_codes"],
@@ -223,6 +245,27 @@ def permute(idx: np.ndarray, E: int):
     pair_to_row = np.empty(T * k, np.int32)
     _load().oracle_permute(_ptr(ix), T, k, E, _ptr(offsets), _ptr(sorted_pair), _ptr(pair_to_row))
     return offsets, sorted_pair, pair_to_row
+
+
+def e2m1_value(code: int) -> float:
+    return float(_load().oracle_e2m1_value(int(code)))
+
+
+def e2m1_round(v: float) -> int:
+    return int(_load().oracle_e2m1_round(float(np.float32(v))))
+
+
+def e4m3_round(f: float) -> int:
+    return int(_load().oracle_e4m3_round(float(np.float32(f))))
+
+
+def nvfp4_quantize(v, ga: float) -> np.ndarray:
+    """NVFP4 quantisation of fp32 values in groups of 16 (see moe_oracle.c);
+    returns e2m1(code) * block scale, without the global factor ga."""
+    a = _c(v, np.float32)
+    out = np.empty(a.shape, np.float64)
+    _load().oracle_nvfp4_quantize(_ptr(a), a.size, float(np.float32(ga)), _ptr(out))
+    return out
 
 
 def e4m3_value(code: int) -> float:

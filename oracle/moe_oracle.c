@@ -22,6 +22,10 @@
  *  [FP8]   "Qwen3.8-Flash-Next-AWQ-g32" card, "Optional FP8 MTP": routed
  *          experts stored in FP8 E4M3 with explicit block scales (the
  *          128 x 128 block and fp32 scales are this oracle's reading).
+ *  [NVFP4] "cleyesode/Qwen3.8-Flash-Next-RAZOR-96B-A6B-NVFP4" card, precision
+ *          table: routed experts NVFP4 W4A4, group 16, FP8 block scales,
+ *          FP32 global scales (layouts and the activation recipe are this
+ *          oracle's reading).
  *  [RAZOR] "Qwen3.8-Flash-Next-RAZOR-65B-A6B-E256of512" card, section
  *          "Selection and calibration": Refill-RMS saliency, RMS conditional on
  *          the tokens routed to each expert, additive statistics, keep-set in
@@ -354,7 +358,7 @@ void oracle_permute(const int32_t *idx, int64_t T, int64_t k, int64_t E,
 /* O5/O6: one SwiGLU expert, bf16 or AWQ W4 weights                           */
 /* ------------------------------------------------------------------------- */
 
-enum { ORA_BF16 = 0, ORA_AWQ = 1, ORA_FP8 = 2 };
+enum { ORA_BF16 = 0, ORA_AWQ = 1, ORA_FP8 = 2, ORA_NVFP4 = 3 };
 
 /* One projection of a bank of experts (out x in per expert). */
 typedef struct {
@@ -365,7 +369,11 @@ typedef struct {
     const int32_t *qzeros;   /* awq:  [E][in/32][out/8]             */
     const uint16_t *scales;  /* awq:  [E][in/32][out] fp16          */
     const uint8_t *codes;    /* fp8:  [E][out][in] E4M3              */
+                             /* nvfp4: [E][out][in/2], two E2M1 codes */
     const float *bscales;    /* fp8:  [E][out/128][in/128] fp32      */
+    const uint8_t *gscales;  /* nvfp4: [E][out][in/16] E4M3          */
+    const float *wglobal;    /* nvfp4: [E] fp32 weight global scale  */
+    float aglobal;           /* nvfp4: activation global scale       */
 } ora_proj;
 
 typedef struct {
@@ -403,6 +411,91 @@ double oracle_e4m3_value(int code)
     return e4m3_value((uint8_t)code);
 }
 
+/* ---- NVFP4 ([NVFP4]: routed experts W4A4, FP4 values in groups of 16 with
+ * FP8 E4M3 block scales and FP32 global scales). */
+
+/* E2M1 code (sign bit 3, exponent bits 2..1 with bias 1, mantissa bit 0) to
+ * its value; exponent field 0 is subnormal: 0 or 0.5. */
+static double e2m1_value(int c)
+{
+    int sign = (c >> 3) & 1, ex = (c >> 1) & 3, m = c & 1;
+    double v = ex == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, ex - 1);
+    return sign ? -v : v;
+}
+
+/* Nearest E2M1 code to v (fp32), ties to the even code, magnitudes above 6
+ * saturating to 6; a result of magnitude 0 is +0. */
+static int e2m1_round(float v)
+{
+    static const float grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    float a = fabsf(v);
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        float dc = fabsf(a - grid[c]), db = fabsf(a - grid[best]);
+        if (dc < db || (dc == db && (c & 1) == 0))
+            best = c;
+    }
+    return (best != 0 && v < 0.0f) ? (best | 8) : best;
+}
+
+/* Nearest E4M3 code to f >= 0 (fp32), ties to even, saturating at 448:
+ * the value grid is 2^-9 * k for k < 8 (subnormal) and (8 + m) * 2^(e - 10)
+ * for exponent field e in 1..15 (the top code 15/7 excluded). */
+static int e4m3_round(float f)
+{
+    if (!(f > 0.0f))
+        return 0;
+    if (f >= 448.0f)
+        return 0x7E;
+    double x = (double)f;  /* exact */
+    int e = 0;
+    frexp(x, &e);          /* x = r * 2^e, r in [0.5, 1) */
+    int ex = e - 1 + 7;    /* exponent field if normal */
+    double step = ex >= 1 ? ldexp(1.0, ex - 7 - 3) : ldexp(1.0, -9);
+    double k = x / step;   /* exact: a power-of-two division */
+    double kf = floor(k);
+    double r = k - kf;
+    double kr = (r > 0.5 || (r == 0.5 && fmod(kf, 2.0) != 0.0)) ? kf + 1.0 : kf;
+    if (ex < 1) {          /* subnormal: k in [0, 8] */
+        int ki = (int)kr;
+        return ki >= 8 ? 0x08 : ki;  /* 8 * 2^-9 = 2^-6: exponent 1, mantissa 0 */
+    }
+    int ki = (int)kr;      /* in [8, 16] */
+    if (ki == 16) { ki = 8; ex += 1; }
+    if (ex > 15 || (ex == 15 && ki - 8 == 7))
+        return 0x7E;
+    return (ex << 3) | (ki - 8);
+}
+
+/* Exported for the tests. */
+double oracle_e2m1_value(int code) { return e2m1_value(code); }
+int oracle_e2m1_round(float v) { return e2m1_round(v); }
+int oracle_e4m3_round(float f) { return e4m3_round(f); }
+
+/* NVFP4 quantisation of n values (n a multiple of 16) with activation
+ * global scale ga, every decision in fp32: per group of 16, the block scale
+ * code is the E4M3 rounding of amax / (6 * ga); with block scale s, each
+ * value's code is the E2M1 rounding of v / (s * ga).  out[i] receives
+ * e2m1(code) * s (exact), i.e. the value without the global factor ga. */
+void oracle_nvfp4_quantize(const float *v, int64_t n, float ga, double *out)
+{
+    for (int64_t g = 0; g < n; g += 16) {
+        float amax = 0.0f;
+        for (int i = 0; i < 16; ++i)
+            amax = fmaxf(amax, fabsf(v[g + i]));
+        float sf = amax / (6.0f * ga);
+        double s = e4m3_value((uint8_t)e4m3_round(sf));
+        for (int i = 0; i < 16; ++i) {
+            if (s == 0.0) {
+                out[g + i] = 0.0;
+            } else {
+                float d = (float)s * ga;
+                out[g + i] = e2m1_value(e2m1_round(v[g + i] / d)) * s;
+            }
+        }
+    }
+}
+
 /* Weight W[e][o][i] of a projection, decoded to an exact double.
  * AWQ: w = (q - z) * s, q and z integers in 0..15, s fp16 ([AWQ]).
  * FP8: w = e4m3(code) * block scale of the 128 x 128 block holding (o, i),
@@ -415,6 +508,12 @@ static double proj_weight(const ora_proj *p, int64_t e, int64_t o, int64_t i)
         int64_t ob = p->out_dim / 128, ib = p->in_dim / 128;
         double s = (double)p->bscales[(e * ob + o / 128) * ib + i / 128];
         return e4m3_value(p->codes[(e * p->out_dim + o) * p->in_dim + i]) * s;
+    }
+    if (p->fmt == ORA_NVFP4) {
+        uint8_t byte = p->codes[(e * p->out_dim + o) * (p->in_dim / 2) + i / 2];
+        int c = (i % 2) ? (byte >> 4) : (byte & 15);
+        double s = e4m3_value(p->gscales[(e * p->out_dim + o) * (p->in_dim / 16) + i / 16]);
+        return e2m1_value(c) * s * (double)p->wglobal[e];
     }
     int64_t words = p->out_dim / 8, groups = p->in_dim / 32;
     int nib = awq_nibble_of_column((int)(o % 8));
@@ -446,21 +545,52 @@ static void expert_forward(const ora_bank *b, int64_t e, const double *x, double
 {
     int64_t H = b->hidden, F = b->inter;
     double *h = (double *)malloc((size_t)F * sizeof(double));
+    const double *xin = x;
+    double *xq = NULL;
+    double ga_in = 1.0, ga_h = 1.0;
+    if (b->gate.fmt == ORA_NVFP4) {
+        /* W4A4: the input is quantised once for gate and up (shared
+         * activation global scale of the gate/up pair) */
+        float *xf = (float *)malloc((size_t)H * sizeof(float));
+        xq = (double *)malloc((size_t)H * sizeof(double));
+        for (int64_t i = 0; i < H; ++i)
+            xf[i] = (float)x[i];  /* bf16 values: exact */
+        oracle_nvfp4_quantize(xf, H, b->gate.aglobal, xq);
+        free(xf);
+        xin = xq;
+        ga_in = (double)b->gate.aglobal;
+        ga_h = (double)b->down.aglobal;
+    }
     for (int64_t f = 0; f < F; ++f) {
         double a = 0.0, u = 0.0;
         for (int64_t i = 0; i < H; ++i) {
-            a += proj_weight(&b->gate, e, f, i) * x[i];
-            u += proj_weight(&b->up, e, f, i) * x[i];
+            a += proj_weight(&b->gate, e, f, i) * xin[i];
+            u += proj_weight(&b->up, e, f, i) * xin[i];
         }
-        h[f] = silu(a) * u;
+        h[f] = silu(a * ga_in) * (u * ga_in);
+    }
+    const double *hin = h;
+    double *hq = NULL;
+    if (b->gate.fmt == ORA_NVFP4) {
+        /* the down projection's input is quantised too; its decisions are
+         * taken on h rounded to fp32 */
+        float *hf = (float *)malloc((size_t)F * sizeof(float));
+        hq = (double *)malloc((size_t)F * sizeof(double));
+        for (int64_t f = 0; f < F; ++f)
+            hf[f] = (float)h[f];
+        oracle_nvfp4_quantize(hf, F, b->down.aglobal, hq);
+        free(hf);
+        hin = hq;
     }
     for (int64_t o = 0; o < H; ++o) {
         double s = 0.0;
         for (int64_t f = 0; f < F; ++f)
-            s += proj_weight(&b->down, e, o, f) * h[f];
-        out[o] = s;
+            s += proj_weight(&b->down, e, o, f) * hin[f];
+        out[o] = s * ga_h;
     }
     free(h);
+    free(xq);
+    free(hq);
 }
 
 static void x_row(const uint16_t *x, int64_t t, int64_t H, double *xd)

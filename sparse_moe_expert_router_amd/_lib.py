@@ -250,7 +250,9 @@ def prune_slice(keep_idx, w_router, bank: dict):
     H = w_router.shape[1] if w_router is not None else bank_dims(bank)[1]
     out = {"fmt": bank["fmt"]}
     for name, t in bank.items():
-        if name != "fmt":
+        if name == "fmt" or isinstance(t, float):
+            out[name] = t
+        else:
             out[name] = torch.empty((n,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
     wr2 = None
     if w_router is not None:

@@ -33,7 +33,7 @@ def oracle_bank(bank: dict, experts=None) -> O.Bank:
     sel = None if experts is None else torch.as_tensor(np.asarray(experts), dtype=torch.long)
     d = {}
     for name, t in bank.items():
-        if name == "fmt":
+        if name == "fmt" or isinstance(t, float):
             d[name] = t
         else:
             tt = t if sel is None else t.index_select(0, sel.to(t.device))

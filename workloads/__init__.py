@@ -12,6 +12,9 @@ Value recipe (shared by every workload):
     scales |N(0, 0.002)| + 1e-4 drawn in fp32 then rounded to fp16;
   * FP8 block-scaled experts: N(0, 0.02) weights in fp32, per 128 x 128 block
     scale = largest |w| / 448, codes = w / scale rounded to E4M3;
+  * NVFP4 experts: uniform E2M1 codes, E4M3 group scales with values in
+    [0.5, 4], weight global scales 0.004 * (1 + U(0, 0.1)) per expert and
+    activation global scales 0.002;
   * the pruned workload's keep-set: a seeded random choice of 256 of the 512
     base experts, listed in ascending index order.
 Each tensor draws from its own torch.Generator, seeded from (seed, copy,
@@ -63,6 +66,10 @@ WORKLOADS = {
     # same geometry, FP8 E4M3 routed experts with 128 x 128 block scales
     "decode_fp8": Workload("decode_fp8", T=16, H=2560, E=512, k=10, F=640, Fs=640, fmt="fp8"),
     "prefill_fp8": Workload("prefill_fp8", T=4096, H=2560, E=512, k=10, F=640, Fs=640, fmt="fp8"),
+    # NVFP4 W4A4 routed experts (group 16, E4M3 group scales, fp32 global scales)
+    "decode_nvfp4": Workload("decode_nvfp4", T=16, H=2560, E=512, k=10, F=640, Fs=640, fmt="nvfp4"),
+    "prefill_nvfp4": Workload("prefill_nvfp4", T=4096, H=2560, E=512, k=10, F=640, Fs=640,
+                              fmt="nvfp4"),
     "prefill_awq": Workload("prefill_awq", T=4096, H=2560, E=512, k=10, F=640, Fs=640, fmt="awq"),
     # 256 of 512 experts kept; one packed row of 32768 tokens
     "pruned_awq": Workload("pruned_awq", T=32768, H=2560, E=256, k=10, F=640, Fs=640, fmt="awq",
@@ -164,8 +171,25 @@ def expert_bank(w: Workload, seed: int = 0, device="cpu", copy: int = 0, E: int 
             assert o % 128 == 0 and i % 128 == 0
             out[name + "_codes"], out[name + "_bscales"] = _fp8_blocks(
                 (E, o, i), _gen(device, seed, copy, tid, 4), device)
+        elif fmt == "nvfp4":
+            assert i % 32 == 0
+            g = _gen(device, seed, copy, tid, 5)
+            # two uniform E2M1 codes per byte (all 16 codes, -0 included)
+            out[name + "_fp4"] = torch.randint(0, 256, (E, o, i // 2), generator=g, device=device,
+                                               dtype=torch.int64).to(torch.uint8)
+            # E4M3 block scales with values in [0.5, 4] (codes 0x30..0x48)
+            out[name + "_fp4scales"] = torch.randint(0x30, 0x49, (E, o, i // 16), generator=g,
+                                                     device=device, dtype=torch.int64).to(torch.uint8)
+            # weight global scale per expert: 0.004 * (1 + U(0, 0.1))
+            out[name + "_wglobal"] = (0.004 * (1.0 + 0.1 * torch.rand(E, generator=g, device=device,
+                                                                       dtype=torch.float32)))
         else:
             raise ValueError(fmt)
+    if fmt == "nvfp4":
+        # static activation global scales (the inputs' largest magnitudes are
+        # about 6 * 448 * scale): one for the gate/up input, one for down's
+        out["act_global_gu"] = 0.002
+        out["act_global_down"] = 0.002
     return out
 
 
@@ -230,4 +254,4 @@ def bits(t: torch.Tensor):
 
 def bank_numpy(bank: dict) -> dict:
     """Numpy bit patterns of an expert-bank dict (for the oracle)."""
-    return {k: (v if isinstance(v, str) else bits(v)) for k, v in bank.items()}
+    return {k: (v if isinstance(v, (str, float)) else bits(v)) for k, v in bank.items()}
