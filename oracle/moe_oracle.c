@@ -430,6 +430,8 @@ static int e2m1_round(float v)
     static const float grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
     float a = fabsf(v);
     int best = 0;
+    if (a > 6.0f)  /* saturation; past 2^22 the fp32 distances below would tie */
+        return v < 0.0f ? 15 : 7;
     for (int c = 1; c < 8; ++c) {
         float dc = fabsf(a - grid[c]), db = fabsf(a - grid[best]);
         if (dc < db || (dc == db && (c & 1) == 0))

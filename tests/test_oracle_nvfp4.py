@@ -55,7 +55,9 @@ def _e2m1_round_ref(v):
 def test_e2m1_round_against_midpoint_thresholds():
     rng = np.random.default_rng(31)
     vals = np.concatenate([rng.uniform(-8, 8, 4000), rng.uniform(-1, 1, 2000),
-                           np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 100.0])])
+                           np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 100.0]),
+                           # saturation far beyond 6, where fp32 distances to the grid tie
+                           np.array([2.0**22, 2.0**22 + 1, 7.4e7, 1e30, 3.4e38, np.inf])])
     vals = np.concatenate([vals, -vals]).astype(np.float32)
     for v in vals:
         assert O.e2m1_round(v) == _e2m1_round_ref(float(v)), v
