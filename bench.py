@@ -36,6 +36,8 @@ def expert_bytes(w, fmt):
         return 2 * n
     if fmt == "fp8":  # one byte per weight + an fp32 scale per 128 x 128 block
         return n + 4 * (n // (128 * 128))
+    if fmt == "nvfp4":  # 4-bit codes + an E4M3 scale per 16 weights + 3 fp32 global scales
+        return n // 2 + n // 16 + 3 * 4
     # AWQ g32: 4-bit codes + fp16 scale per (group, column) + 4-bit zero per (group, column)
     return n // 2 + 2 * (n // 32) + (n // 32) // 2
 
@@ -53,8 +55,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_bf16",
-                   help="tiny_bf16, decode_bf16, decode_awq, decode_fp8, prefill_awq, prefill_fp8, "
-                        "pruned_awq, refill_bf16")
+                   help="tiny_bf16, decode_bf16, decode_awq, decode_fp8, decode_nvfp4, prefill_awq, "
+                        "prefill_fp8, prefill_nvfp4, pruned_awq, refill_bf16")
     p.add_argument("--copies", type=int, default=0, help="weight copies to cycle (0: auto)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the oracle CPU-baseline sample (0 disables it)")
@@ -187,7 +189,8 @@ def main():
     result = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
               "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-              "dtype": {"bf16": "bf16", "awq": "w4a16_g32/bf16", "fp8": "w8a16_e4m3_block128/bf16"}[w.fmt],
+              "dtype": {"bf16": "bf16", "awq": "w4a16_g32/bf16", "fp8": "w8a16_e4m3_block128/bf16",
+                        "nvfp4": "w4a4_nvfp4_g16/bf16"}[w.fmt],
               "data": "synthetic (seeded)",
               "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
                          "experts_base": w.E_base or w.E, "top_k": w.k, "expert_width": w.F,

@@ -46,6 +46,24 @@
  *                (the optional FP8 draft of the AWQ-g32 card stores routed
  *                experts in E4M3 with explicit block scales; the 128 x 128
  *                block is this library's reading).  I and O multiples of 128.
+ *  NVFP4 experts (W4A4; the NVFP4 release card's precision table: group
+ *                16, FP8 block scales, FP32 global scales; the layouts and the
+ *                activation recipe below are this library's reading):
+ *                codes [E][O][I/2]: byte j holds inputs 2j (bits 0..3) and
+ *                2j+1 (bits 4..7) as E2M1 (sign bit 3, exponent bits 2..1
+ *                with bias 1, mantissa bit 0); group_scales [E][O][I/16] E4M3;
+ *                global_scale [E] fp32:
+ *                  w[e][o][i] = e2m1 * e4m3(group_scales[e][o][i/16]) * global_scale[e].
+ *                Every input row of every projection is quantised the same
+ *                way, per 16 consecutive inputs, all in fp32: with g =
+ *                act_scale, the group's scale code is the E4M3 rounding
+ *                (nearest, ties to even, saturating at 448) of amax / (6 g);
+ *                with s its value, each input v becomes the E2M1 rounding
+ *                (nearest, ties to even, saturating at 6) of v / (s g); the
+ *                projection then sees e2m1 * s * g.  Gate and up share their
+ *                input and must carry the same act_scale; the down
+ *                projection's input (the SwiGLU product) is quantised with
+ *                down.act_scale.  I and O multiples of 32.
  *  AWQ experts:  for a projection with input dim I and output dim O
  *                  qweight [E][I][O/8] int32, qzeros [E][I/32][O/8] int32,
  *                  scales [E][I/32][O] fp16;
@@ -71,7 +89,7 @@ typedef enum {
     MOE_ERR_HIP = 5          /* a HIP call failed; see moe_last_hip_error()   */
 } moe_status;
 
-typedef enum { MOE_W_BF16 = 0, MOE_W_AWQ_G32 = 1, MOE_W_FP8_BLOCK = 2 } moe_wfmt;
+typedef enum { MOE_W_BF16 = 0, MOE_W_AWQ_G32 = 1, MOE_W_FP8_BLOCK = 2, MOE_W_NVFP4 = 3 } moe_wfmt;
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_dtype;
 
 /* One projection of a bank of experts, input dim in_dim, output dim out_dim. */
@@ -83,7 +101,12 @@ typedef struct {
     const int32_t *qzeros;    /* AWQ:  [E][in/32][out/8]                      */
     const uint16_t *scales;   /* AWQ:  [E][in/32][out] fp16                   */
     const uint8_t *codes;     /* FP8:  [E][out][in] E4M3 (OCP)                */
+                              /* NVFP4: [E][out][in/2] two E2M1 codes a byte  */
     const float *block_scales;/* FP8:  [E][out/128][in/128] fp32              */
+    const uint8_t *group_scales; /* NVFP4: [E][out][in/16] E4M3               */
+    const float *global_scale;   /* NVFP4: [E] fp32 weight global scale       */
+    float act_scale;             /* NVFP4: global scale of this projection's
+                                    input activations (host value, > 0)       */
 } moe_proj;
 
 /* A bank of SwiGLU experts: gate, up: hidden -> inter; down: inter -> hidden.
@@ -94,7 +117,8 @@ typedef struct {
 } moe_experts;
 
 /* Operation ids for moe_workspace_bytes(). */
-enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_FFN = 2, MOE_OP_REFILL_SCORE = 3 };
+enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_FFN = 2, MOE_OP_REFILL_SCORE = 3,
+       MOE_OP_GROUPED_FFN_NVFP4 = 4 /* grouped FFN of an NVFP4 bank (adds the quantised input) */ };
 
 /*
  * Router: logits, softmax, top-k, renormalised gates.
@@ -137,8 +161,14 @@ moe_status moe_permute(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E,
  * expert applied to every token (the shared expert): rows[t] = expert(x[t]),
  * and k must be 1.  `ex` is a HOST pointer to a struct of device pointers.
  * rows is [T*k][H] of out_dtype.  Intermediates: fp32 accumulation, the
- * SwiGLU product rounded to bf16 before the down projection.
- * AWQ requires hidden % 32 == 0 and inter % 32 == 0.
+ * SwiGLU product rounded to bf16 before the down projection (NVFP4: x and
+ * the SwiGLU product are quantised as described under "NVFP4 experts").
+ * AWQ and NVFP4 require hidden % 32 == 0 and inter % 32 == 0, FP8 multiples
+ * of 128.  x, rows, ws and the bf16 / AWQ / FP8 / NVFP4 code arrays must be
+ * 16-byte aligned, FP8 block scales and NVFP4 global scales 4-byte aligned,
+ * NVFP4 group scales 2-byte aligned (MOE_ERR_UNSUPPORTED otherwise).  A bad
+ * NVFP4 act_scale (not in (0, 3e38)) or gate/up act_scales that differ give
+ * MOE_ERR_SHAPE.
  */
 moe_status moe_grouped_ffn(const uint16_t *x, int32_t T, int32_t k, const moe_experts *ex,
                            const int32_t *expert_offsets, const int32_t *sorted_pair,
@@ -216,9 +246,23 @@ moe_status moe_prune_slice(const int32_t *keep_idx, int32_t n_keep, const uint16
 moe_status moe_router_norm_keep(const uint16_t *w_router, int32_t E, int32_t H, int32_t keep,
                                 float *norm, int32_t *keep_idx, void *stream);
 
+/*
+ * NVFP4 activation quantisation (the recipe under "NVFP4 experts" above) of
+ * a [T][n] bf16 matrix, row by row in groups of 16 (n % 16 == 0): out[t][i]
+ * = e2m1(code) * s as bf16 (exact), without the global factor act_scale.
+ * moe_grouped_ffn applies it to NVFP4 banks by itself; this call exposes it
+ * for checking.  x and out are device pointers, 16-byte aligned, owned by
+ * the caller (out may not overlap x).  Errors: T < 0, n < 1 or act_scale not
+ * in (0, 3e38) -> MOE_ERR_SHAPE; n % 16 or misalignment ->
+ * MOE_ERR_UNSUPPORTED; a null pointer with T > 0 -> MOE_ERR_NULL.
+ */
+moe_status moe_nvfp4_quantize(const uint16_t *x, int32_t T, int32_t n, float act_scale,
+                              uint16_t *out, void *stream);
+
 /* Scratch bytes an operation needs (0 when none).  For MOE_OP_GROUPED_FFN,
- * k is the pairs per token and E the bank's expert count.  Sizes grow with T;
- * a workspace sized for the largest T of a run serves every smaller call. */
+ * k is the pairs per token and E the bank's expert count; an NVFP4 bank needs
+ * MOE_OP_GROUPED_FFN_NVFP4.  Sizes grow with T; a workspace sized for the
+ * largest T of a run serves every smaller call. */
 size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
 
 /* Static text for a status code. */

@@ -10,6 +10,12 @@ Expert banks are dicts of device tensors:
   awq : {"fmt": "awq", "gate_qweight": [E,H,F/8] int32, "gate_qzeros": [E,H/32,F/8] int32,
          "gate_scales": [E,H/32,F] fp16, and the same for "up_*" and "down_*"
          (down: [E,F,H/8], [E,F/32,H/8], [E,F/32,H])}
+  fp8 : {"fmt": "fp8", "gate_codes": [E,F,H] uint8 E4M3, "gate_bscales": [E,F/128,H/128] f32,
+         and the same for "up_*" and "down_*" (down: [E,H,F], [E,H/128,F/128])}
+  nvfp4: {"fmt": "nvfp4", "gate_fp4": [E,F,H/2] uint8 (two E2M1 codes, low nibble = even
+         input), "gate_fp4scales": [E,F,H/16] uint8 E4M3, "gate_wglobal": [E] f32, the same
+         for "up_*" and "down_*" (down: [E,H,F/2], [E,H,F/16], [E]), and the activation
+         global scales "act_global_gu" (gate and up inputs) and "act_global_down" (floats)}
 """
 from __future__ import annotations
 
@@ -21,13 +27,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-OP_ROUTE, OP_PERMUTE, OP_GROUPED_FFN, OP_REFILL_SCORE = 0, 1, 2, 3
-W_BF16, W_AWQ, W_FP8 = 0, 1, 2
+OP_ROUTE, OP_PERMUTE, OP_GROUPED_FFN, OP_REFILL_SCORE, OP_GROUPED_FFN_NVFP4 = 0, 1, 2, 3, 4
+W_BF16, W_AWQ, W_FP8, W_NVFP4 = 0, 1, 2, 3
 OUT_BF16, OUT_F32 = 0, 1
 
 EXPORTS = ["moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_refill_score",
            "moe_refill_finalize", "moe_prune_slice", "moe_router_norm_keep",
-           "moe_workspace_bytes", "moe_status_string", "moe_last_hip_error"]
+           "moe_nvfp4_quantize", "moe_workspace_bytes", "moe_status_string", "moe_last_hip_error"]
 
 
 class MoeError(RuntimeError):
@@ -38,7 +44,9 @@ class _Proj(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("in_dim", ctypes.c_int32), ("out_dim", ctypes.c_int32),
                 ("w", ctypes.c_void_p), ("qweight", ctypes.c_void_p),
                 ("qzeros", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("codes", ctypes.c_void_p), ("block_scales", ctypes.c_void_p)]
+                ("codes", ctypes.c_void_p), ("block_scales", ctypes.c_void_p),
+                ("group_scales", ctypes.c_void_p), ("global_scale", ctypes.c_void_p),
+                ("act_scale", ctypes.c_float)]
 
 
 class _Experts(ctypes.Structure):
@@ -68,6 +76,7 @@ def lib():
         "moe_refill_finalize": [P, P, i32, i32, i32, P, P, P, P],
         "moe_prune_slice": [P, i32, P, P, i32, ctypes.POINTER(_Experts), ctypes.POINTER(_Experts), P],
         "moe_router_norm_keep": [P, i32, i32, i32, P, P, P],
+        "moe_nvfp4_quantize": [P, i32, i32, ctypes.c_float, P, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -141,6 +150,14 @@ def experts_struct(bank: dict):
         mk = lambda n, i, o: _Proj(W_FP8, i, o, None, None, None, None, bank[n + "_codes"].data_ptr(),
                                    bank[n + "_bscales"].data_ptr())
         return _Experts(E, H, F, mk("gate", H, F), mk("up", H, F), mk("down", F, H))
+    if fmt == "nvfp4":
+        E, F, H2 = bank["gate_fp4"].shape
+        H = H2 * 2
+        ga = {"gate": bank["act_global_gu"], "up": bank["act_global_gu"], "down": bank["act_global_down"]}
+        mk = lambda n, i, o: _Proj(W_NVFP4, i, o, None, None, None, None, bank[n + "_fp4"].data_ptr(), None,
+                                   bank[n + "_fp4scales"].data_ptr(), bank[n + "_wglobal"].data_ptr(),
+                                   float(ga[n]))
+        return _Experts(E, H, F, mk("gate", H, F), mk("up", H, F), mk("down", F, H))
     E, H, F8 = bank["gate_qweight"].shape
     F = F8 * 8
     mk = lambda n, i, o: _Proj(W_AWQ, i, o, None, bank[n + "_qweight"].data_ptr(),
@@ -153,6 +170,9 @@ def bank_dims(bank: dict):
         E, F, H = bank["gate"].shape
     elif bank["fmt"] == "fp8":
         E, F, H = bank["gate_codes"].shape
+    elif bank["fmt"] == "nvfp4":
+        E, F, H2 = bank["gate_fp4"].shape
+        H = H2 * 2
     else:
         E, H, F8 = bank["gate_qweight"].shape
         F = F8 * 8
@@ -199,7 +219,8 @@ def grouped_ffn(x, k: int, bank: dict, offsets=None, sorted_pair=None, out_dtype
         rows = torch.empty((T * k, H), dtype=torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
                            device=dev)
     st = experts_struct(bank)
-    buf, n = _ws(ws, dev).get(workspace_bytes(OP_GROUPED_FFN, T, k, E, H, F))
+    op = OP_GROUPED_FFN_NVFP4 if bank["fmt"] == "nvfp4" else OP_GROUPED_FFN
+    buf, n = _ws(ws, dev).get(workspace_bytes(op, T, k, E, H, F))
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(_ptr(x), T, k, ctypes.byref(st), _ptr(offsets),
                                                     _ptr(sorted_pair), out_dtype, _ptr(rows),
                                                     _ptr(buf), n, _stream()))
@@ -261,6 +282,18 @@ def prune_slice(keep_idx, w_router, bank: dict):
     _check("moe_prune_slice", lib().moe_prune_slice(_ptr(keep_idx), n, _ptr(w_router), _ptr(wr2), H,
                                                     ctypes.byref(src), ctypes.byref(dst), _stream()))
     return wr2, out
+
+
+def nvfp4_quantize(x, act_scale: float, out=None):
+    """NVFP4 activation quantisation of bf16 x [T, n] (n % 16 == 0) under the
+    global scale act_scale: per 16 values the E4M3 block scale s and E2M1 codes,
+    returned as bf16 e2m1 * s (exact), the form the NVFP4 experts consume."""
+    T, n = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check("moe_nvfp4_quantize", lib().moe_nvfp4_quantize(_ptr(x), T, n, float(act_scale), _ptr(out),
+                                                          _stream()))
+    return out
 
 
 def router_norm_keep(w_router, keep: int):

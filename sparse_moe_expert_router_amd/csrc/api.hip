@@ -48,6 +48,14 @@ bool proj_ok(const moe_proj& p, int fmt, int in_dim, int out_dim, int E, moe_sta
             *st = MOE_ERR_UNSUPPORTED;
             return false;
         }
+    } else if (fmt == MOE_W_NVFP4) {
+        if (!p.codes || !p.group_scales || !p.global_scale) { *st = MOE_ERR_NULL; return false; }
+        if (in_dim % 32 || out_dim % 32) { *st = MOE_ERR_UNSUPPORTED; return false; }
+        if (!(p.act_scale > 0.0f) || !(p.act_scale < 3.0e38f)) { *st = MOE_ERR_SHAPE; return false; }
+        if (!aligned16(p.codes) || ((uintptr_t)p.group_scales % 2) || ((uintptr_t)p.global_scale % 4)) {
+            *st = MOE_ERR_UNSUPPORTED;
+            return false;
+        }
     } else if (fmt == MOE_W_FP8_BLOCK) {
         if (!p.codes || !p.block_scales) { *st = MOE_ERR_NULL; return false; }
         if (in_dim % 128 || out_dim % 128) { *st = MOE_ERR_UNSUPPORTED; return false; }
@@ -69,8 +77,11 @@ bool bank_ok(const moe_experts* ex, moe_status* st) {
     if (E < 1 || H < 1 || F < 1) { *st = MOE_ERR_SHAPE; return false; }
     if (E > kMaxE || H % 64 || F % 32 || H > 16384 || F > 2048) { *st = MOE_ERR_UNSUPPORTED; return false; }
     const int fmt = ex->gate.fmt;
-    return proj_ok(ex->gate, fmt, H, F, E, st) && proj_ok(ex->up, fmt, H, F, E, st) &&
-           proj_ok(ex->down, fmt, F, H, E, st);
+    if (!(proj_ok(ex->gate, fmt, H, F, E, st) && proj_ok(ex->up, fmt, H, F, E, st) &&
+          proj_ok(ex->down, fmt, F, H, E, st)))
+        return false;
+    if (fmt == MOE_W_NVFP4 && ex->gate.act_scale != ex->up.act_scale) { *st = MOE_ERR_SHAPE; return false; }
+    return true;
 }
 
 }  // namespace
@@ -135,7 +146,7 @@ moe_status moe_grouped_ffn(const uint16_t* x, int32_t T, int32_t k, const moe_ex
     if (!x || !rows) return MOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(rows)) return MOE_ERR_UNSUPPORTED;
     const int E = ex->num_experts, H = ex->hidden, F = ex->inter;
-    const size_t need = moe::ffn_ws_bytes(T, k, E, H, F);
+    const size_t need = moe::ffn_ws_bytes(T, k, E, H, F, ex->gate.fmt == MOE_W_NVFP4);
     if (ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (need && !ws) return MOE_ERR_NULL;
     if (!aligned16(ws)) return MOE_ERR_UNSUPPORTED;
@@ -229,6 +240,16 @@ moe_status moe_prune_slice(const int32_t* keep_idx, int32_t n_keep, const uint16
             st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->w, const_cast<uint16_t*>(dp[m]->w),
                                                      in * out * sizeof(uint16_t), s));
             if (st != MOE_OK) return st;
+        } else if (sp[m]->fmt == MOE_W_NVFP4) {
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->codes,
+                                                     const_cast<uint8_t*>(dp[m]->codes), in / 2 * out, s));
+            if (st != MOE_OK) return st;
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->group_scales,
+                                                     const_cast<uint8_t*>(dp[m]->group_scales), in / 16 * out, s));
+            if (st != MOE_OK) return st;
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->global_scale,
+                                                     const_cast<float*>(dp[m]->global_scale), sizeof(float), s));
+            if (st != MOE_OK) return st;
         } else if (sp[m]->fmt == MOE_W_FP8_BLOCK) {
             st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->codes,
                                                      const_cast<uint8_t*>(dp[m]->codes), in * out, s));
@@ -264,12 +285,24 @@ moe_status moe_router_norm_keep(const uint16_t* w_router, int32_t E, int32_t H, 
                                                    static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_nvfp4_quantize(const uint16_t* x, int32_t T, int32_t n, float act_scale, uint16_t* out,
+                              void* stream) {
+    if (T < 0 || n < 1) return MOE_ERR_SHAPE;
+    if (n % 16) return MOE_ERR_UNSUPPORTED;
+    if (!(act_scale > 0.0f) || !(act_scale < 3.0e38f)) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!x || !out) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_nvfp4_quantize(x, T, n, act_scale, out, static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
     if (T <= 0 || k <= 0 || E <= 0) return 0;
     switch (op) {
         case MOE_OP_ROUTE: return route_ws(T, E, H);
         case MOE_OP_PERMUTE: return moe::permute_ws_bytes(T, k, E);
-        case MOE_OP_GROUPED_FFN: return moe::ffn_ws_bytes(T, k, E, H, F);
+        case MOE_OP_GROUPED_FFN: return moe::ffn_ws_bytes(T, k, E, H, F, false);
+        case MOE_OP_GROUPED_FFN_NVFP4: return moe::ffn_ws_bytes(T, k, E, H, F, true);
         case MOE_OP_REFILL_SCORE: return moe::refill_ws_bytes(T, k);
         default: return 0;
     }

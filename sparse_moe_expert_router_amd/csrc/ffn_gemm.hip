@@ -26,12 +26,20 @@
 // bits), fma(m, s, c) = (q - z) * s exactly, then one RNE to bf16.  The four
 // rows of a column are contiguous in the K-major LDS tile: one 8-byte store.
 //
+// FP8 and NVFP4 B tiles are widened to bf16 on the way into LDS (both are
+// exact in bf16: an E4M3 code times its fp32 block scale is rounded once; an
+// E2M1 value times its E4M3 group scale has at most 6 significant bits).  For
+// NVFP4 the activations arrive quantised, the global factors (activation times
+// weight global scale) multiply the accumulators, and the gate/up epilogue
+// quantises h per 16 columns for the down pass.
+//
 // Tiles are enumerated per expert (ceil(rows / BM) each) by a small kernel;
 // workgroup ids are remapped so that each XCD (ids are dealt round-robin over
 // 8 XCDs) works on a contiguous range of tiles, the column tiles of one row
 // tile adjacent: the A rows and the expert's weights are then reused from that
 // XCD's L2.
 #include "ffn_internal.h"
+#include "nvfp4.h"
 
 namespace moe {
 
@@ -200,14 +208,38 @@ __device__ __forceinline__ void fp8_store_chunk(uint4 c, float sc, uint16_t* Bs,
     *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh + 1)]) = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// NVFP4 B tile: chunk q (< BPER/2) is B-column q/2, inputs 16*(q%2)..+15 of
+// the step: 16 E2M1 codes (8 bytes, low nibble first) and one E4M3 scale s;
+// each value e2m1 * s is exact in bf16.
+__device__ __forceinline__ void nvfp4_store_chunk(uint4 c, uint32_t sbyte, uint16_t* Bs, int q) {
+    const float sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)sbyte, false)[0];
+    const uint32_t cw[2] = {c.x, c.y};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], 1.0f, 0);
+        const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], 1.0f, 1);
+        const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], 1.0f, 2);
+        const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], 1.0f, 3);
+        o[4 * i + 0] = pack_bf16x2(v0[0] * sc, v0[1] * sc);
+        o[4 * i + 1] = pack_bf16x2(v1[0] * sc, v1[1] * sc);
+        o[4 * i + 2] = pack_bf16x2(v2[0] * sc, v2[1] * sc);
+        o[4 * i + 3] = pack_bf16x2(v3[0] * sc, v3[1] * sc);
+    }
+    const int bc = q / 2, kh = q % 2;
+    *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh)]) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh + 1)]) = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // Registers of one K step -> LDS stage (A chunks; bf16 B chunks or dequantised AWQ words).
 template <int MODE, int WF, int BM>
 __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APER],
                                             const uint4 (&rb)[GemmShape<BM>::BPER],
                                             const uint32_t (&rw)[GemmShape<BM>::RPT], const float2* Ps,
                                             uint16_t* As, uint16_t* Bs, int tid) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32 or FP8
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
     (void)FP8;
+    (void)NV4;
     using S = GemmShape<BM>;
 #pragma unroll
     for (int i = 0; i < S::APER; ++i) {
@@ -218,6 +250,9 @@ __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APE
 #pragma unroll
         for (int i = 0; i < S::BPER / 2; ++i)
             fp8_store_chunk(rb[i], __uint_as_float(rw[i]), Bs, tid + i * S::NT);
+    } else if (NV4) {
+#pragma unroll
+        for (int i = 0; i < S::BPER / 2; ++i) nvfp4_store_chunk(rb[i], rw[i], Bs, tid + i * S::NT);
     } else if (!AWQ) {
 #pragma unroll
         for (int i = 0; i < S::BPER; ++i) {
@@ -242,8 +277,9 @@ __device__ __forceinline__ void read_frags(const uint16_t* As, const uint16_t* B
                                            bf16x8_t (&af)[GemmShape<BM>::TM],
                                            bf16x8_t (&bfr)[GemmShape<BM>::TN], int wm, int wn,
                                            int lane) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32 or FP8
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
     (void)FP8;
+    (void)NV4;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
 #pragma unroll
@@ -271,8 +307,9 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
                                                  const uint4 (&rb)[GemmShape<BM>::BPER],
                                                  const uint32_t (&rw)[GemmShape<BM>::RPT],
                                                  const float2* Ps, uint16_t* As, uint16_t* Bs, int tid) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32 or FP8
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
     (void)FP8;
+    (void)NV4;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
     constexpr int NM = TM * TN;  // MFMAs this step
@@ -293,6 +330,8 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
         }
         if (FP8) {
             if (j < S::BPER / 2) fp8_store_chunk(rb[j], __uint_as_float(rw[j]), Bs, tid + j * S::NT);
+        } else if (NV4) {
+            if (j < S::BPER / 2) nvfp4_store_chunk(rb[j], rw[j], Bs, tid + j * S::NT);
         } else if (!AWQ) {
             if (j < S::BPER) {
                 const int q = tid + j * S::NT;
@@ -313,8 +352,9 @@ template <int MODE, int WF, int BM>
 __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(GroupedArgs a,
                                                                const int32_t* __restrict__ tiles,
                                                                uint16_t* __restrict__ hbuf, int NT) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32 or FP8
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
     (void)FP8;
+    (void)NV4;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN, APER = S::APER, BPER = S::BPER, NTHR = S::NT;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
@@ -357,6 +397,7 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
     const uint16_t* bsrc[BPER];
     const uint8_t* fsrc[BPER / 2 > 0 ? BPER / 2 : 1];   // FP8 code chunks
     const float* fscl[BPER / 2 > 0 ? BPER / 2 : 1];     // their block-scale rows
+    const uint8_t* gsrc[BPER / 2 > 0 ? BPER / 2 : 1];   // NVFP4: group-scale rows
     const int32_t* wsrc = nullptr;
     const int32_t* zsrc = nullptr;
     const uint16_t* ssrc = nullptr;
@@ -374,6 +415,18 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
             const int col = MODE == MODE_GATEUP ? n0 + bc % (kBN / 2) : n0 + bc;
             fsrc[i] = codes + (size_t)e * NOUT * K + (size_t)col * K + kh * 16;
             fscl[i] = bsc + ((size_t)e * (NOUT / 128) + col / 128) * (K / 128);
+        }
+    } else if (NV4) {
+#pragma unroll
+        for (int i = 0; i < BPER / 2; ++i) {
+            const int q = tid + i * NTHR;
+            const int bc = q / 2, kh = q % 2;
+            const bool upm = MODE == MODE_GATEUP && bc >= kBN / 2;
+            const uint8_t* codes = MODE == MODE_DOWN ? a.down.codes : (upm ? a.up.codes : a.gate.codes);
+            const uint8_t* gsc = MODE == MODE_DOWN ? a.down.gscales : (upm ? a.up.gscales : a.gate.gscales);
+            const int col = MODE == MODE_GATEUP ? n0 + bc % (kBN / 2) : n0 + bc;
+            fsrc[i] = codes + ((size_t)e * NOUT + col) * (K / 2) + kh * 8;
+            gsrc[i] = gsc + ((size_t)e * NOUT + col) * (K / 16) + kh;
         }
     } else if (!AWQ) {
 #pragma unroll
@@ -437,6 +490,12 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
                 RB[i] = *reinterpret_cast<const uint4*>(fsrc[i] + k0_);                       \
                 RW[i] = __float_as_uint(fscl[i][k0_ >> 7]);                                   \
             }                                                                                 \
+        } else if (NV4) {                                                                     \
+            _Pragma("unroll") for (int i = 0; i < BPER / 2; ++i) {                            \
+                const uint2 c_ = *reinterpret_cast<const uint2*>(fsrc[i] + (k0_ >> 1));       \
+                RB[i] = make_uint4(c_.x, c_.y, 0u, 0u);                                       \
+                RW[i] = gsrc[i][k0_ >> 4];                                                    \
+            }                                                                                 \
         } else {                                                                              \
             _Pragma("unroll") for (int i = 0; i < BPER; ++i) RB[i] =                          \
                 *reinterpret_cast<const uint4*>(bsrc[i] + k0_);                               \
@@ -499,6 +558,17 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
                                      : reinterpret_cast<char*>(&Bs[0][0]) + (wave - 4) * 8192)
                          : reinterpret_cast<char*>(&Bs[0][0]) + wave * 8192);
     const int wrow = m0 + wm * S::MW;  // first row of the wave tile
+    // NVFP4 global factors of the accumulators (1 for the other formats)
+    float cg = 1.0f, cu = 1.0f, cd = 1.0f;
+    if (NV4) {
+        if (MODE == MODE_GATEUP) {
+            cg = a.gate.act * a.gate.wglobal[e];
+            cu = a.gate.act * a.up.wglobal[e];
+        } else {
+            cd = a.down.act * a.down.wglobal[e];
+        }
+    }
+    (void)cd;
     if (MODE == MODE_GATEUP) {
         constexpr int HC = S::NW / 2, LD = HC + 4;  // 32 h columns per wave
         const int hcol = n0 + wn * HC;
@@ -508,11 +578,22 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
             for (int nj = 0; nj < TN / 2; ++nj)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    st[(4 * (lane / 16) + r) * LD + nj * 16 + lane % 16] = silu(acc[mi][nj][r]) * acc[mi][nj + TN / 2][r];
+                    st[(4 * (lane / 16) + r) * LD + nj * 16 + lane % 16] =
+                        silu(acc[mi][nj][r] * cg) * (acc[mi][nj + TN / 2][r] * cu);
             wave_lds_sync();
             const int rr = lane / 4, ch = lane % 4;  // 16 rows x 4 chunks of 8 columns
-            const float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
-            const float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
+            float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
+            float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
+            if (NV4) {  // groups of 16 h columns: chunk pairs (0,1), (2,3) of lanes 4i..4i+3
+                float am = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                                 fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+                am = fmaxf(am, __shfl_xor(am, 1, kWave));
+                const float qa = a.down.act, sc = nvfp4_group_scale(am, qa);
+                v0 = make_float4(nvfp4_qv(v0.x, sc, qa), nvfp4_qv(v0.y, sc, qa), nvfp4_qv(v0.z, sc, qa),
+                                 nvfp4_qv(v0.w, sc, qa));
+                v1 = make_float4(nvfp4_qv(v1.x, sc, qa), nvfp4_qv(v1.y, sc, qa), nvfp4_qv(v1.z, sc, qa),
+                                 nvfp4_qv(v1.w, sc, qa));
+            }
             const int row = wrow + mi * 16 + rr;
             if (row < m1)
                 *reinterpret_cast<uint4*>(&hbuf[(size_t)row * F + hcol + ch * 8]) =
@@ -528,7 +609,8 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
 #pragma unroll
             for (int nj = 0; nj < TN; ++nj)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) st[(4 * (lane / 16) + r) * LD + nj * 16 + lane % 16] = acc[mi][nj][r];
+                for (int r = 0; r < 4; ++r)
+                    st[(4 * (lane / 16) + r) * LD + nj * 16 + lane % 16] = NV4 ? acc[mi][nj][r] * cd : acc[mi][nj][r];
             wave_lds_sync();
             if (a.out_f32) {
                 float* out = static_cast<float*>(a.rows);
@@ -592,7 +674,12 @@ template <int BM>
 static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int mt,
                            hipStream_t s) {
     const int NT1 = a.F / (kBN / 2), NT2 = a.H / kBN;
-    if (a.fp8) {
+    if (a.nvfp4) {
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, 3, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
+                           s, a, tiles, hbuf, NT1);
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 3, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
+                           s, a, tiles, hbuf, NT2);
+    } else if (a.fp8) {
         hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, 2, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT1);
         hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 2, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,

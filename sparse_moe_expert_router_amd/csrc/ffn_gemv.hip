@@ -17,6 +17,7 @@
 // Threads own one word column (8 output columns) and whole groups, so the
 // zero/scale correction is paid once per group.
 #include "ffn_internal.h"
+#include "nvfp4.h"
 
 namespace moe {
 
@@ -479,10 +480,168 @@ __global__ __launch_bounds__(256) void fp8_gateup_kernel(GroupedArgs a, int KS, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4 experts (W4A4): the activations arrive quantised (e2m1 * block
+// scale, as bf16).  A 16-byte weight vector holds 32 E2M1 codes, inputs
+// 32v..32v+31 of one row, i.e. two groups of 16 with one E4M3 scale each.
+// v_cvt_scalef32_pk_f32_fp4 with scale 1 gives a byte's two codes exactly
+// (low nibble first: the even input), v_cvt_pk_bf16_f32 packs them and
+// v_dot2_f32_bf16 takes the activation pair; each group's dot product is
+// then scaled by its E4M3 scale.  The global factors (activation and weight
+// global scales) are applied to the row sums.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fp4_to_bf16x4(uint32_t w, uint32_t (&o)[4]) {
+    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    o[0] = pack_bf16x2(v0[0], v0[1]);
+    o[1] = pack_bf16x2(v1[0], v1[1]);
+    o[2] = pack_bf16x2(v2[0], v2[1]);
+    o[3] = pack_bf16x2(v3[0], v3[1]);
+}
+
+template <int R, int NR, int RA>
+__device__ __forceinline__ void nvfp4_stream_dot(const uint4* const (&rows)[NR], const uint8_t* const (&srow)[NR],
+                                                 int k0, int nv, int l16, const uint4* xs, int xstride,
+                                                 float (&acc)[4][RA]) {
+    for (int v = l16; v < nv; v += 16) {  // v: 32-input vector
+        uint4 w[NR];
+        uint32_t sc2[NR];
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            w[n] = rows[n][v];
+            sc2[n] = *reinterpret_cast<const uint16_t*>(srow[n] + ((k0 + 32 * v) >> 4));
+        }
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            const uint32_t ww[4] = {w[n].x, w[n].y, w[n].z, w[n].w};
+            const auto sv = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc2[n], false);  // the two E4M3 group scales
+            const float s0 = sv[0], s1 = sv[1];
+            uint32_t wb[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t o[4];
+                fp4_to_bf16x4(ww[q], o);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) wb[4 * q + b] = o[b];
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint4* xv = xs + i * xstride + 4 * v;
+                float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const uint4 x = xv[c];
+                    t0 = dot2_bf16(wb[4 * c + 0], x.x, t0);
+                    t0 = dot2_bf16(wb[4 * c + 1], x.y, t0);
+                    t0 = dot2_bf16(wb[4 * c + 2], x.z, t0);
+                    t0 = dot2_bf16(wb[4 * c + 3], x.w, t0);
+                }
+#pragma unroll
+                for (int c = 2; c < 4; ++c) {
+                    const uint4 x = xv[c];
+                    t1 = dot2_bf16(wb[4 * c + 0], x.x, t1);
+                    t1 = dot2_bf16(wb[4 * c + 1], x.y, t1);
+                    t1 = dot2_bf16(wb[4 * c + 2], x.z, t1);
+                    t1 = dot2_bf16(wb[4 * c + 3], x.w, t1);
+                }
+                acc[n][i] = fmaf(s1, t1, fmaf(s0, t0, acc[n][i]));
+            }
+        }
+    }
+}
+
+// NVFP4 gate/up: grid (expert slot, F/32 column chunks, KS input splits);
+// block 256 (4 waves).  Waves 0,1: gate columns c0..c0+31, waves 2,3: up.
+template <int RCH>
+__global__ __launch_bounds__(256) void nvfp4_gateup_kernel(GroupedArgs a, int KS, float* __restrict__ part) {
+    __shared__ uint4 xs[RCH * kBfChunkK / 8];
+    __shared__ float outv[64][RCH];
+    int r0, r1;
+    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    if (!a.offsets) { r0 = 0; r1 = a.T; }
+    if (e < 0) return;
+    const int H = a.H, F = a.F;
+    const int ks = blockIdx.z;
+    const int kb = (int)((long)H / 32 * ks / KS) * 32, ke = (int)((long)H / 32 * (ks + 1) / KS) * 32;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int sub = lane / 16, l16 = lane % 16;
+    const int c0 = blockIdx.y * 32;
+    const int mat = wave / 2;
+    const uint8_t* W = (mat ? a.up.codes : a.gate.codes) + (size_t)e * F * (H / 2);
+    const uint8_t* S = (mat ? a.up.gscales : a.gate.gscales) + (size_t)e * F * (H / 16);
+    const float gscale = a.gate.act * (mat ? a.up.wglobal : a.gate.wglobal)[e];
+    for (int rc = r0; rc < r1; rc += RCH) {
+        const int nr = min(RCH, r1 - rc);
+        float acc[4][RCH];
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
+        for (int k0 = kb; k0 < ke; k0 += kBfChunkK) {
+            const int kl = min(kBfChunkK, ke - k0), nx = kl / 8;
+            __syncthreads();
+            for (int it = threadIdx.x; it < nr * nx; it += blockDim.x) {
+                const int i = it / nx, v = it % nx;
+                const int t = row_token(a.sorted_pair, a.k, rc + i);
+                xs[i * (kBfChunkK / 8) + v] = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + k0)[v];
+            }
+            __syncthreads();
+            const uint4* rows[4];
+            const uint8_t* srow[4];
+#pragma unroll
+            for (int ps = 0; ps < 4; ++ps) {
+                const int col = c0 + (wave % 2) * 16 + ps * 4 + sub;
+                rows[ps] = reinterpret_cast<const uint4*>(W + (size_t)col * (H / 2) + k0 / 2);
+                srow[ps] = S + (size_t)col * (H / 16);
+            }
+            auto body = [&](auto rtag) {
+                constexpr int R = decltype(rtag)::value;
+                nvfp4_stream_dot<R, 4, RCH>(rows, srow, k0, kl / 32, l16, xs, kBfChunkK / 8, acc);
+            };
+            dispatch_rows<RCH>(nr, body);
+        }
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) {
+                float v = acc[ps][i];
+                v += __shfl_xor(v, 1, kWave);
+                v += __shfl_xor(v, 2, kWave);
+                v += __shfl_xor(v, 4, kWave);
+                v += __shfl_xor(v, 8, kWave);
+                if (l16 == 0) outv[wave * 16 + ps * 4 + sub][i] = v * gscale;
+            }
+        __syncthreads();
+        for (int it = threadIdx.x; it < 64 * nr; it += blockDim.x) {
+            const int o = it % 64, i = it / 64;
+            const int m = o / 32, col = c0 + o % 32;
+            part[((size_t)ks * a.P + rc + i) * (2 * F) + m * F + col] = outv[o][i];
+        }
+    }
+}
+
 // SwiGLU of the gate/up partials summed over the KS input splits: one bf16
 // pair (the product rounded once) per thread, h[r][F/2].
+// A pair of SwiGLU values to bf16; with qa > 0 (NVFP4) they are first
+// quantised with activation global scale qa in their group of 16, which
+// eight consecutive lanes hold (every lane of the group must take part).
+__device__ __forceinline__ uint32_t pack_h_pair(float h0, float h1, float qa) {
+    if (qa > 0.0f) {
+        float amax = fmaxf(fabsf(h0), fabsf(h1));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+        const float sc = nvfp4_group_scale(amax, qa);
+        h0 = nvfp4_qv(h0, sc, qa);
+        h1 = nvfp4_qv(h1, sc, qa);
+    }
+    return pack_bf16x2(h0, h1);
+}
+
 __device__ __forceinline__ uint32_t swiglu_pair(const float* __restrict__ part, int KS, int P, int F,
-                                                int r, int f) {
+                                                int r, int f, float qa) {
     float hv[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -494,17 +653,18 @@ __device__ __forceinline__ uint32_t swiglu_pair(const float* __restrict__ part, 
         }
         hv[u] = silu(g) * up;
     }
-    return pack_bf16x2(hv[0], hv[1]);
+    return pack_h_pair(hv[0], hv[1], qa);
 }
 
 // With several input splits the SwiGLU is formed once per row here, instead of
-// in every down-projection workgroup that reads the row.
+// in every down-projection workgroup that reads the row.  Groups of 16 values
+// (8 lanes) never straddle the end, so whole groups leave together.
 __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restrict__ part, int KS,
-                                                            int P, int F, uint32_t* __restrict__ h) {
+                                                            int P, int F, float qa, uint32_t* __restrict__ h) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= (long)P * (F / 2)) return;
     const int r = (int)(i / (F / 2)), f = 2 * (int)(i % (F / 2));
-    h[i] = swiglu_pair(part, KS, P, F, r, f);
+    h[i] = swiglu_pair(part, KS, P, F, r, f, qa);
 }
 
 // Rows [rc, rc+nr) of h into LDS as bf16 pairs h2[RCH][F/2]: copied from hsrc
@@ -512,7 +672,7 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restr
 template <int RCH>
 __device__ __forceinline__ void stage_swiglu(const float* __restrict__ part,
                                              const uint32_t* __restrict__ hsrc, int KS, int P,
-                                             int F, int rc, int nr, uint32_t* h2) {
+                                             int F, int rc, int nr, uint32_t* h2, float qa = 0.0f) {
     if (hsrc) {
         for (int it = threadIdx.x; it < RCH * (F / 2); it += blockDim.x) {
             const int i = it / (F / 2);
@@ -535,7 +695,7 @@ __device__ __forceinline__ void stage_swiglu(const float* __restrict__ part,
                 hv[u] = silu(g) * up;
             }
         }
-        h2[it] = pack_bf16x2(hv[0], hv[1]);
+        h2[it] = pack_h_pair(hv[0], hv[1], qa);  // rows >= nr: zeros, quantised to zeros
     }
 }
 
@@ -603,8 +763,8 @@ __device__ __forceinline__ void bf16_down_dot(const uint16_t* __restrict__ W, in
     bf16_stream_dot<R, NPASS, (NPASS >= 4 ? 2 : 4)>(rows, F / 8, l16, hv, F / 8, acc);
 }
 
-// The down projection of bf16 experts, or (FP8) of FP8 experts.
-template <int RCH, int NPASS, bool FP8 = false>
+// The down projection of bf16 (WF 0), FP8 (WF 2) or NVFP4 (WF 3) experts.
+template <int RCH, int NPASS, int WF = 0>
 __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
                                                         const float* __restrict__ part,
                                                         const uint32_t* __restrict__ hsrc) {
@@ -621,10 +781,11 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
     const int o0 = blockIdx.y * 16 * npass;
     const uint16_t* W = a.down.w + (size_t)e * H * F;
     const uint4* hv = reinterpret_cast<const uint4*>(h2);
+    const float oscale = WF == 3 ? a.down.act * a.down.wglobal[e] : 1.0f;
     for (int rc = r0; rc < r1; rc += RCH) {
         const int nr = min(RCH, r1 - rc);
         __syncthreads();
-        stage_swiglu<RCH>(part, hsrc, KS, a.P, F, rc, nr, h2);
+        stage_swiglu<RCH>(part, hsrc, KS, a.P, F, rc, nr, h2, WF == 3 ? a.down.act : 0.0f);
         __syncthreads();
         float acc[4][RCH];
 #pragma unroll
@@ -633,7 +794,19 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
             for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
         auto body = [&](auto rtag) {
             constexpr int R = decltype(rtag)::value;
-            if constexpr (FP8) {
+            if constexpr (WF == 3) {
+                const uint4* rows[NPASS];
+                const uint8_t* srow[NPASS];
+                const uint8_t* C = a.down.codes + (size_t)e * H * (F / 2);
+                const uint8_t* S = a.down.gscales + (size_t)e * H * (F / 16);
+#pragma unroll
+                for (int ps = 0; ps < NPASS; ++ps) {
+                    const int o = o0 + ps * 16 + wave * 4 + sub;
+                    rows[ps] = reinterpret_cast<const uint4*>(C + (size_t)o * (F / 2));
+                    srow[ps] = S + (size_t)o * (F / 16);
+                }
+                nvfp4_stream_dot<R, NPASS, RCH>(rows, srow, 0, F / 32, l16, hv, F / 8, acc);
+            } else if constexpr (WF == 2) {
                 const uint4* rows[NPASS];
                 const float* srow[NPASS];
                 const uint8_t* C = a.down.codes + (size_t)e * H * F;
@@ -659,7 +832,7 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
                 v += __shfl_xor(v, 2, kWave);
                 v += __shfl_xor(v, 4, kWave);
                 v += __shfl_xor(v, 8, kWave);
-                if (l16 == 0 && ps < npass) outv[ps * 16 + wave * 4 + sub][i] = v;
+                if (l16 == 0 && ps < npass) outv[ps * 16 + wave * 4 + sub][i] = WF == 3 ? v * oscale : v;
             }
         __syncthreads();
         const int nrows = 16 * npass;
@@ -744,7 +917,7 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s)
         if (hbuf) {
             const long pairs = (long)a.P * (F / 2);
             hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
-                               s, (const float*)part, KS, a.P, F, hbuf);
+                               s, (const float*)part, KS, a.P, F, 0.0f, hbuf);
         }
         const int OWd = H / 8, OWC = down_owc(OWd);
         const int RPd = row_phases(OWC);
@@ -754,18 +927,35 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s)
       } else {
         return hipErrorInvalidValue;  // AWQ takes at most two rows per pass
       }
+    } else if (a.nvfp4) {
+      if constexpr (RCH <= 8) {
+        hipLaunchKernelGGL(nvfp4_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS, part);
+        if (hbuf) {
+            const long pairs = (long)a.P * (F / 2);
+            hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
+                               s, (const float*)part, KS, a.P, F, a.down.act, hbuf);
+        }
+        if ((long)slots * (H / 64) >= 1024)
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4, 3>), dim3(slots, H / 64), dim3(256), 0, s, a, KS,
+                               (const float*)part, (const uint32_t*)hbuf);
+        else
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1, 3>), dim3(slots, H / 16), dim3(256), 0, s, a, KS,
+                               (const float*)part, (const uint32_t*)hbuf);
+      } else {
+        return hipErrorInvalidValue;  // NVFP4 takes at most eight rows per pass
+      }
     } else if (a.fp8) {
         hipLaunchKernelGGL(fp8_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS, part);
         if (hbuf) {
             const long pairs = (long)a.P * (F / 2);
             hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
-                               s, (const float*)part, KS, a.P, F, hbuf);
+                               s, (const float*)part, KS, a.P, F, 0.0f, hbuf);
         }
         if ((long)slots * (H / 64) >= 1024)
-            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4, true>), dim3(slots, H / 64), dim3(256), 0, s, a, KS,
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4, 2>), dim3(slots, H / 64), dim3(256), 0, s, a, KS,
                                (const float*)part, (const uint32_t*)hbuf);
         else
-            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1, true>), dim3(slots, H / 16), dim3(256), 0, s, a, KS,
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1, 2>), dim3(slots, H / 16), dim3(256), 0, s, a, KS,
                                (const float*)part, (const uint32_t*)hbuf);
     } else {
         hipLaunchKernelGGL(bf16_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS,
@@ -773,7 +963,7 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s)
         if (hbuf) {
             const long pairs = (long)a.P * (F / 2);
             hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
-                               s, (const float*)part, KS, a.P, F, hbuf);
+                               s, (const float*)part, KS, a.P, F, 0.0f, hbuf);
         }
         // rows per down workgroup: 64, or 16 when few experts are active
         if ((long)slots * (H / 64) >= 1024)
@@ -790,9 +980,9 @@ hipError_t launch_gemv(const GroupedArgs& a, void* ws, hipStream_t s) {
     // rows per pass: a bf16 shared expert sees every token (all of a decode
     // batch in one pass); a routed expert at decode sees one or two, and the
     // AWQ kernels keep two rows per pass to hold the next group's words in
-    // registers
-    if (!a.offsets && a.T > 2 && !a.awq && !a.fp8) return launch_gemv_rch<16>(a, ws, s);
-    if (!a.offsets && a.T > 2 && a.fp8) return launch_gemv_rch<8>(a, ws, s);
+    // registers; FP8 and NVFP4 shared experts take eight rows per pass
+    if (!a.offsets && a.T > 2 && !a.awq && !a.fp8 && !a.nvfp4) return launch_gemv_rch<16>(a, ws, s);
+    if (!a.offsets && a.T > 2 && (a.fp8 || a.nvfp4)) return launch_gemv_rch<8>(a, ws, s);
     return launch_gemv_rch<2>(a, ws, s);
 }
 

@@ -14,8 +14,11 @@ struct ProjDev {
     const int32_t* qweight;   // awq  [E][in][out/8]
     const int32_t* qzeros;    // awq  [E][in/32][out/8]
     const uint16_t* scales;   // awq  [E][in/32][out] fp16
-    const uint8_t* codes;     // fp8  [E][out][in] E4M3
+    const uint8_t* codes;     // fp8  [E][out][in] E4M3; nvfp4 [E][out][in/2] E2M1 pairs
     const float* bscales;     // fp8  [E][out/128][in/128]
+    const uint8_t* gscales;   // nvfp4 [E][out][in/16] E4M3
+    const float* wglobal;     // nvfp4 [E]
+    float act;                // nvfp4: global scale of the projection's input
 };
 
 struct GroupedArgs {
@@ -23,6 +26,7 @@ struct GroupedArgs {
     int T, k, H, F, E, P;       // P = T*k rows
     int awq;                    // 1: AWQ g32, 0: bf16 or fp8
     int fp8;                    // 1: FP8 E4M3 with 128 x 128 block scales
+    int nvfp4;                  // 1: NVFP4 W4A4 (x already quantised)
     const int32_t* offsets;     // [E+1] or nullptr (identity: E == 1, row r = token r)
     const int32_t* sorted_pair; // [P] or nullptr
     ProjDev gate, up, down;

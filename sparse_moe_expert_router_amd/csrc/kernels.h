@@ -36,7 +36,11 @@ struct FfnArgs {
     int out_f32;                  // 1: rows are fp32, else bf16
     void* rows;                   // [T*k][H]
 };
-size_t ffn_ws_bytes(int T, int k, int E, int H, int F);
+size_t ffn_ws_bytes(int T, int k, int E, int H, int F, bool nvfp4);
+
+// ---- NVFP4 activation quantisation (quant.hip)
+hipError_t launch_nvfp4_quantize(const uint16_t* x, int T, int n, float act_scale, uint16_t* out,
+                                 hipStream_t s);
 hipError_t launch_ffn(const FfnArgs& a, void* ws, hipStream_t s);
 
 // ---- combine (combine.hip)

@@ -16,7 +16,7 @@ OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -88,6 +88,35 @@ def test_grouped_ffn_validation():
     bad.down.in_dim = 64                                   # inconsistent projection sizes
     assert call(bad) == SHAPE
     assert L.moe_grouped_ffn(fake, 8, 2, None, fake, fake, 0, fake, fake, 1 << 30, None) == NULL
+
+
+def _nvfp4_bank(E=4, H=256, F=128, act=(0.01, 0.01, 0.01), gptr=256):
+    mk = lambda i, o, a: _lib._Proj(3, i, o, None, None, None, None, 256, None, gptr, 256, a)
+    return _lib._Experts(E, H, F, mk(H, F, act[0]), mk(H, F, act[1]), mk(F, H, act[2]))
+
+
+def test_nvfp4_validation():
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    call = lambda bank: L.moe_grouped_ffn(fake, 8, 2, ctypes.byref(bank), fake, fake, 0, fake, fake,
+                                          1 << 30, None)
+    assert call(_nvfp4_bank(F=48)) == UNSUP                     # inter % 32
+    assert call(_nvfp4_bank(act=(0.0, 0.0, 0.01))) == SHAPE     # act_scale must be > 0
+    assert call(_nvfp4_bank(act=(0.01, 0.01, float("nan")))) == SHAPE
+    assert call(_nvfp4_bank(act=(0.01, 0.02, 0.01))) == SHAPE   # gate and up share their input
+    assert call(_nvfp4_bank(gptr=257)) == UNSUP                 # group scales read two at a time
+    assert call(_nvfp4_bank(gptr=0)) == NULL
+    # the NVFP4 workspace covers the quantised input as well
+    for T in (1, 16, 4096):
+        assert L.moe_workspace_bytes(4, T, 10, 512, 2560, 640) >= \
+            L.moe_workspace_bytes(2, T, 10, 512, 2560, 640) + T * 2560 * 2
+    q = L.moe_nvfp4_quantize
+    assert q(fake, 4, 24, ctypes.c_float(0.01), fake, None) == UNSUP   # n % 16
+    assert q(fake, 4, 32, ctypes.c_float(-1.0), fake, None) == SHAPE
+    assert q(fake, -1, 32, ctypes.c_float(0.01), fake, None) == SHAPE
+    assert q(None, 0, 32, ctypes.c_float(0.01), None, None) == OK      # nothing to do
+    assert q(None, 4, 32, ctypes.c_float(0.01), fake, None) == NULL
+    assert q(ctypes.c_void_p(264), 4, 32, ctypes.c_float(0.01), fake, None) == UNSUP
 
 
 def test_refill_and_keep_validation():

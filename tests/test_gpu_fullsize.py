@@ -21,7 +21,7 @@ def _sample(n, T, seed):
     return np.sort(np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), n - 2, replace=False)]))
 
 
-@pytest.mark.parametrize("name", ["prefill_awq", "pruned_awq", "prefill_fp8"])
+@pytest.mark.parametrize("name", ["prefill_awq", "pruned_awq", "prefill_fp8", "prefill_nvfp4"])
 def test_fullsize_layer(name):
     moe = require_gpu()
     w = workloads.get(name)

@@ -25,7 +25,7 @@ def oracle_layer_sparse(x, wr, k, bank, shared, tokens=None, shared_scale=None):
     return O.combine(rows, g, s, shared_scale), idx, g
 
 
-@pytest.mark.parametrize("name", ["tiny_bf16", "decode_bf16", "decode_awq", "decode_fp8"])
+@pytest.mark.parametrize("name", ["tiny_bf16", "decode_bf16", "decode_awq", "decode_fp8", "decode_nvfp4"])
 def test_layer_matches_oracle(name):
     moe = require_gpu()
     w = workloads.get(name)

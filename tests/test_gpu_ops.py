@@ -136,7 +136,7 @@ def _random_routing(T, k, E, seed):
     return torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "awq", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "awq", "fp8", "nvfp4"])
 @pytest.mark.parametrize("T,E,k,H,F", [(32, 8, 2, 256, 128),      # few rows per expert: streaming
                                        (200, 8, 2, 256, 128),     # 50 rows: MFMA, 64-row tiles
                                        (400, 8, 2, 256, 128),     # 100 rows: 128-row tiles
@@ -161,6 +161,47 @@ def test_grouped_ffn_matches_oracle(fmt, T, E, k, H, F):
         ref = O.pair_outputs(bits(x), idx.numpy(), oracle_bank(bank))
         got = rows.float().cpu().numpy()[p2r.cpu().numpy().astype(np.int64)]
         check_close(got, ref, f"{fmt} T={T} E={E} out={out_dtype}")
+
+
+# ----------------------------------------------------------------------------- NVFP4 activations
+
+def _nvfp4_cases():
+    """bf16 rows exercising every branch of the NVFP4 quantiser: N(0,1) rows,
+    an all-zero group, groups whose block scale saturates at 448 or is an E4M3
+    subnormal, values exactly on E2M1 midpoints, and +-0."""
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn((37, 2560), generator=g)
+    x[1, :16] = 0.0                                           # zero group: scale 0, codes 0
+    x[2] *= 1e4                                               # amax / (6 ga) > 448: saturated scale
+    x[3] *= 1e-4                                              # subnormal E4M3 scales
+    x[4, :16] = torch.tensor([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0,
+                              -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0, -6.0])  # midpoints
+    x[5, :16] = torch.tensor([-0.0] * 8 + [0.0] * 7 + [1.0])  # signed zeros
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("ga", [0.002, 1.0 / 6.0, 3.0e-7])
+def test_nvfp4_quantize_is_bit_exact(ga):
+    moe = require_gpu()
+    x = _nvfp4_cases()
+    got = moe.nvfp4_quantize(x.cuda(), ga)
+    torch.cuda.synchronize()
+    ref = O.nvfp4_quantize(x.float().numpy(), ga)
+    g = got.float().cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(g, ref)
+    # the signs of zeros are not part of the contract; the values are
+    assert np.all(np.isfinite(g))
+
+
+def test_nvfp4_quantize_ragged_rows_and_empty():
+    moe = require_gpu()
+    x = _nvfp4_cases()[:, :48].contiguous()  # 3 groups a row
+    got = moe.nvfp4_quantize(x.cuda(), 0.01)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.float().cpu().numpy().astype(np.float64),
+                                  O.nvfp4_quantize(x.float().numpy(), 0.01))
+    empty = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    assert moe.nvfp4_quantize(empty, 0.01).shape == (0, 64)
 
 
 @pytest.mark.parametrize("T,H,F", [(16, 2560, 640), (100, 2560, 640), (5, 256, 128), (700, 256, 128)])
@@ -211,7 +252,7 @@ def test_combine_matches_oracle(rows_f32):
 
 # ----------------------------------------------------------------------------- pruning, keep policies
 
-@pytest.mark.parametrize("fmt", ["bf16", "awq", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "awq", "fp8", "nvfp4"])
 def test_prune_slice_is_exact_gather(fmt):
     moe = require_gpu()
     w = _wl(8, 256, 32, fmt=fmt)
@@ -225,7 +266,7 @@ def test_prune_slice_is_exact_gather(fmt):
     np.testing.assert_array_equal(bits(wr2), ref_wr)
     got = oracle_bank(bank2)
     for p in ("gate", "up", "down"):
-        for a in ("w", "qweight", "qzeros", "scales", "codes", "bscales"):
+        for a in ("w", "qweight", "qzeros", "scales", "codes", "bscales", "gscales", "wglobal"):
             ra, ga = getattr(getattr(ref_bank, p), a), getattr(getattr(got, p), a)
             if ra is not None:
                 np.testing.assert_array_equal(ga, ra)
