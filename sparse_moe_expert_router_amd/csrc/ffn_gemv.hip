@@ -171,7 +171,7 @@ __device__ __forceinline__ void reduce_phases(const float (&res)[8][RCH], int cl
 }
 
 // ---------------------------------------------------------------------------
-// AWQ gate/up: grid (expert slot, 2*KS); block = OW * RP threads.
+// AWQ gate/up: grid (2*KS, expert slot); block = OW * RP threads.
 // part[ks][r][mat*F + col] (fp32 partial over the WG's groups).
 // ---------------------------------------------------------------------------
 template <int RCH>
@@ -180,10 +180,10 @@ __global__ __launch_bounds__(512) void awq_gateup_kernel(GroupedArgs a, int KS, 
     __shared__ float xsum[RCH * 64];
     extern __shared__ float red[];  // [RCH][F]
     int r0, r1;
-    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    const int e = a.offsets ? slot_expert(a.slots, blockIdx.y, &r0, &r1) : 0;
     if (!a.offsets) { r0 = 0; r1 = a.T; }
     if (e < 0) return;
-    const int mat = blockIdx.y / KS, ks = blockIdx.y % KS;
+    const int mat = blockIdx.x / KS, ks = blockIdx.x % KS;
     const int H = a.H, F = a.F, OW = F / 8, G = H / 32;
     const int g0 = ks * G / KS, g1 = (ks + 1) * G / KS, ng = g1 - g0, npairs = ng * 16;
     const int c = threadIdx.x % OW, rp = threadIdx.x / OW, RP = blockDim.x / OW;
@@ -225,11 +225,15 @@ __global__ __launch_bounds__(512) void awq_gateup_kernel(GroupedArgs a, int KS, 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 gate/up: grid (expert slot, F/32 column chunks, KS input splits);
+// bf16 gate/up: grid (F/32 column chunks, expert slot, KS input splits);
 // block 256 (4 waves).  Waves 0,1: gate columns c0..c0+31, waves 2,3: up.
 // 16 lanes per weight row.  part[ks][r][mat*F + col].
 // ---------------------------------------------------------------------------
 constexpr int kBfChunkK = 2048;
+// NVFP4 GEMV shape: rows per lane and lanes per row of the down pass, lanes
+// per row of the gate/up pass, vectors each lane loads before using them
+// (0: the software-pipelined stream)
+constexpr int kNvDownRows = 2, kNvDownUnroll = 0, kNvDownLanes = 4, kNvGateLanes = 8, kNvGateUnroll = 2;
 
 // Dot products of NR weight rows (16-byte vectors, 16 lanes per row, vector
 // v of a row at rows[n][v]) with R activation rows staged in LDS (xs[i*xstride
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, int KS,
     __shared__ uint4 xs[RCH * kBfChunkK / 8];
     __shared__ float outv[64][RCH];
     int r0, r1;
-    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    const int e = a.offsets ? slot_expert(a.slots, blockIdx.y, &r0, &r1) : 0;
     if (!a.offsets) { r0 = 0; r1 = a.T; }
     if (e < 0) return;
     const int H = a.H, F = a.F;
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(256) void bf16_gateup_kernel(GroupedArgs a, int KS,
     const int kb = (int)((long)H / 8 * ks / KS) * 8, ke = (int)((long)H / 8 * (ks + 1) / KS) * 8;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int sub = lane / 16, l16 = lane % 16;  // 4 rows per pass, 16 lanes each
-    const int c0 = blockIdx.y * 32;
+    const int c0 = blockIdx.x * 32;
     const int mat = wave / 2;
     const uint16_t* W = (mat ? a.up.w : a.gate.w) + (size_t)e * F * H;
     for (int rc = r0; rc < r1; rc += RCH) {
@@ -409,14 +413,14 @@ __device__ __forceinline__ void fp8_stream_dot(const uint4* const (&rows)[NR], c
     }
 }
 
-// FP8 gate/up: grid (expert slot, F/32 column chunks, KS input splits);
+// FP8 gate/up: grid (F/32 column chunks, expert slot, KS input splits);
 // block 256 (4 waves).  Waves 0,1: gate columns c0..c0+31, waves 2,3: up.
 template <int RCH>
 __global__ __launch_bounds__(256) void fp8_gateup_kernel(GroupedArgs a, int KS, float* __restrict__ part) {
     __shared__ uint4 xs[RCH * kBfChunkK / 8];
     __shared__ float outv[64][RCH];
     int r0, r1;
-    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    const int e = a.offsets ? slot_expert(a.slots, blockIdx.y, &r0, &r1) : 0;
     if (!a.offsets) { r0 = 0; r1 = a.T; }
     if (e < 0) return;
     const int H = a.H, F = a.F;
@@ -425,7 +429,7 @@ __global__ __launch_bounds__(256) void fp8_gateup_kernel(GroupedArgs a, int KS, 
     const int kb = (int)((long)H / 16 * ks / KS) * 16, ke = (int)((long)H / 16 * (ks + 1) / KS) * 16;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int sub = lane / 16, l16 = lane % 16;
-    const int c0 = blockIdx.y * 32;
+    const int c0 = blockIdx.x * 32;
     const int mat = wave / 2;
     const ProjDev& pj = mat ? a.up : a.gate;
     const uint8_t* W = pj.codes + (size_t)e * F * H;
@@ -484,90 +488,150 @@ __global__ __launch_bounds__(256) void fp8_gateup_kernel(GroupedArgs a, int KS, 
 // NVFP4 experts (W4A4): the activations arrive quantised (e2m1 * block
 // scale, as bf16).  A 16-byte weight vector holds 32 E2M1 codes, inputs
 // 32v..32v+31 of one row, i.e. two groups of 16 with one E4M3 scale each.
-// v_cvt_scalef32_pk_f32_fp4 with scale 1 gives a byte's two codes exactly
-// (low nibble first: the even input), v_cvt_pk_bf16_f32 packs them and
-// v_dot2_f32_bf16 takes the activation pair; each group's dot product is
+// v_cvt_scalef32_pk_bf16_fp4 with scale 1 gives a byte's two codes exactly
+// as a bf16 pair (low nibble first: the even input) and v_dot2_f32_bf16
+// takes the activation pair; each group's dot product is
 // then scaled by its E4M3 scale.  The global factors (activation and weight
 // global scales) are applied to the row sums.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void fp4_to_bf16x4(uint32_t w, uint32_t (&o)[4]) {
-    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-    o[0] = pack_bf16x2(v0[0], v0[1]);
-    o[1] = pack_bf16x2(v1[0], v1[1]);
-    o[2] = pack_bf16x2(v2[0], v2[1]);
-    o[3] = pack_bf16x2(v3[0], v3[1]);
+    // v_cvt_scalef32_pk_bf16_fp4: the two codes of byte b (low nibble first)
+    // as a bf16 pair; E2M1 values are exact in bf16 and the scale 1 is exact
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
 }
 
-template <int R, int NR, int RA>
-__device__ __forceinline__ void nvfp4_stream_dot(const uint4* const (&rows)[NR], const uint8_t* const (&srow)[NR],
-                                                 int k0, int nv, int l16, const uint4* xs, int xstride,
-                                                 float (&acc)[4][RA]) {
-    for (int v = l16; v < nv; v += 16) {  // v: 32-input vector
-        uint4 w[NR];
-        uint32_t sc2[NR];
+// One weight vector (32 inputs, two groups) of one row against R staged
+// activation rows: xv[i * xstride .. + 3] are the vector's 32 inputs of row i.
+template <int R, int RA>
+__device__ __forceinline__ void nvfp4_vec_dot(uint4 w, uint32_t sc2, const uint4* xv, int xstride,
+                                              float (&acc)[RA]) {
+    const auto sv = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc2, false);  // the two E4M3 group scales
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    uint32_t wb[16];
 #pragma unroll
-        for (int n = 0; n < NR; ++n) {
-            w[n] = rows[n][v];
-            sc2[n] = *reinterpret_cast<const uint16_t*>(srow[n] + ((k0 + 32 * v) >> 4));
+    for (int q = 0; q < 4; ++q) {
+        uint32_t o[4];
+        fp4_to_bf16x4(ww[q], o);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) wb[4 * q + b] = o[b];
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const uint4* x = xv + i * xstride;
+        float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const uint4 a = x[c], b = x[c + 2];
+            t0 = dot2_bf16(wb[4 * c + 0], a.x, t0);
+            t0 = dot2_bf16(wb[4 * c + 1], a.y, t0);
+            t0 = dot2_bf16(wb[4 * c + 2], a.z, t0);
+            t0 = dot2_bf16(wb[4 * c + 3], a.w, t0);
+            t1 = dot2_bf16(wb[4 * c + 8], b.x, t1);
+            t1 = dot2_bf16(wb[4 * c + 9], b.y, t1);
+            t1 = dot2_bf16(wb[4 * c + 10], b.z, t1);
+            t1 = dot2_bf16(wb[4 * c + 11], b.w, t1);
         }
-#pragma unroll
-        for (int n = 0; n < NR; ++n) {
-            const uint32_t ww[4] = {w[n].x, w[n].y, w[n].z, w[n].w};
-            const auto sv = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc2[n], false);  // the two E4M3 group scales
-            const float s0 = sv[0], s1 = sv[1];
-            uint32_t wb[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t o[4];
-                fp4_to_bf16x4(ww[q], o);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) wb[4 * q + b] = o[b];
-            }
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const uint4* xv = xs + i * xstride + 4 * v;
-                float t0 = 0.0f, t1 = 0.0f;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const uint4 x = xv[c];
-                    t0 = dot2_bf16(wb[4 * c + 0], x.x, t0);
-                    t0 = dot2_bf16(wb[4 * c + 1], x.y, t0);
-                    t0 = dot2_bf16(wb[4 * c + 2], x.z, t0);
-                    t0 = dot2_bf16(wb[4 * c + 3], x.w, t0);
-                }
-#pragma unroll
-                for (int c = 2; c < 4; ++c) {
-                    const uint4 x = xv[c];
-                    t1 = dot2_bf16(wb[4 * c + 0], x.x, t1);
-                    t1 = dot2_bf16(wb[4 * c + 1], x.y, t1);
-                    t1 = dot2_bf16(wb[4 * c + 2], x.z, t1);
-                    t1 = dot2_bf16(wb[4 * c + 3], x.w, t1);
-                }
-                acc[n][i] = fmaf(s1, t1, fmaf(s0, t0, acc[n][i]));
-            }
-        }
+        acc[i] = fmaf(sv[1], t1, fmaf(sv[0], t0, acc[i]));
     }
 }
 
-// NVFP4 gate/up: grid (expert slot, F/32 column chunks, KS input splits);
-// block 256 (4 waves).  Waves 0,1: gate columns c0..c0+31, waves 2,3: up.
-template <int RCH>
+// Dot products of NR NVFP4 weight rows with R activation rows staged in LDS.
+// LPR lanes share a row, lane lr taking vectors lr, lr + LPR, ...; vector v
+// of row n is rows[n][v] with its two group scales at srow[n] + (k0 + 32 v) / 16.
+// U vectors of every row are loaded before any is used (NR * U loads in flight).
+template <int R, int NR, int U, int LPR, int RA>
+__device__ __forceinline__ void nvfp4_stream_dot(const uint4* const (&rows)[NR], const uint8_t* const (&srow)[NR],
+                                                 int k0, int nv, int lr, const uint4* xs, int xstride,
+                                                 float (&acc)[4][RA]) {
+    int v = lr;
+    for (; v + LPR * (U - 1) < nv; v += LPR * U) {
+        uint4 w[U][NR];
+        uint32_t sc[U][NR];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                const int vv = v + LPR * u;
+                w[u][n] = rows[n][vv];
+                sc[u][n] = *reinterpret_cast<const uint16_t*>(srow[n] + ((k0 + 32 * vv) >> 4));
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int n = 0; n < NR; ++n) nvfp4_vec_dot<R, RA>(w[u][n], sc[u][n], xs + 4 * (v + LPR * u), xstride, acc[n]);
+    }
+    for (; v < nv; v += LPR) {
+        uint4 w[NR];
+        uint32_t sc[NR];
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            w[n] = rows[n][v];
+            sc[n] = *reinterpret_cast<const uint16_t*>(srow[n] + ((k0 + 32 * v) >> 4));
+        }
+#pragma unroll
+        for (int n = 0; n < NR; ++n) nvfp4_vec_dot<R, RA>(w[n], sc[n], xs + 4 * v, xstride, acc[n]);
+    }
+}
+
+// Software-pipelined form: the loads of the lane's next vector are issued
+// before the current one is used, so NR loads stay in flight behind the
+// arithmetic.  wn / sn hold the lane's first vector (v = lr) and its scales,
+// loaded by the caller (before it stages the activations) when lr < nv.
+template <int NR>
+__device__ __forceinline__ void nvfp4_load_vec(const uint4* const (&rows)[NR], const uint8_t* const (&srow)[NR],
+                                               int k0, int v, uint4 (&w)[NR], uint32_t (&sc)[NR]) {
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+        w[n] = rows[n][v];
+        sc[n] = *reinterpret_cast<const uint16_t*>(srow[n] + ((k0 + 32 * v) >> 4));
+    }
+}
+
+template <int R, int NR, int LPR, int RA>
+__device__ __forceinline__ void nvfp4_stream_dot_pf(const uint4* const (&rows)[NR], const uint8_t* const (&srow)[NR],
+                                                    int k0, int nv, int lr, const uint4* xs, int xstride,
+                                                    float (&acc)[4][RA], uint4 (&wn)[NR], uint32_t (&sn)[NR]) {
+    for (int v = lr; v < nv; v += LPR) {
+        uint4 w[NR];
+        uint32_t sc[NR];
+#pragma unroll
+        for (int n = 0; n < NR; ++n) { w[n] = wn[n]; sc[n] = sn[n]; }
+        if (v + LPR < nv) nvfp4_load_vec<NR>(rows, srow, k0, v + LPR, wn, sn);
+#pragma unroll
+        for (int n = 0; n < NR; ++n) nvfp4_vec_dot<R, RA>(w[n], sc[n], xs + 4 * v, xstride, acc[n]);
+    }
+}
+
+// Lanes sharing one NVFP4 weight row, and the gate (or up) columns a gate/up
+// workgroup covers: two waves per matrix, four passes of 64 / LPR rows each.
+__host__ __device__ constexpr int nv_gate_cols(int lpr) { return 2 * 4 * (64 / lpr); }
+
+// NVFP4 gate/up: grid (F / nv_gate_cols(LPR) column chunks, expert slot, KS
+// input splits); block 256 (4 waves).  Waves 0,1: gate columns, waves 2,3 the
+// same up columns; LPR lanes stream one row (a row is H/2 bytes: 80 vectors
+// at H = 2560), so a workgroup covers 512 / LPR columns of each matrix per
+// staging of the activation rows.
+template <int RCH, int LPR>
 __global__ __launch_bounds__(256) void nvfp4_gateup_kernel(GroupedArgs a, int KS, float* __restrict__ part) {
-    __shared__ uint4 xs[RCH * kBfChunkK / 8];
-    __shared__ float outv[64][RCH];
+    constexpr int RPW = 64 / LPR;                  // rows per wave per pass
+    constexpr int CW = 4 * RPW;                    // columns per wave
+    constexpr int CPB = nv_gate_cols(LPR);         // columns per matrix per workgroup
+    constexpr int CK = RCH <= 2 ? 2 * kBfChunkK : kBfChunkK;  // inputs staged at once
+    __shared__ uint4 xs[RCH * CK / 8];
+    __shared__ float outv[2 * CPB][RCH];
     int r0, r1;
-    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    const int e = a.offsets ? slot_expert(a.slots, blockIdx.y, &r0, &r1) : 0;
     if (!a.offsets) { r0 = 0; r1 = a.T; }
     if (e < 0) return;
     const int H = a.H, F = a.F;
     const int ks = blockIdx.z;
     const int kb = (int)((long)H / 32 * ks / KS) * 32, ke = (int)((long)H / 32 * (ks + 1) / KS) * 32;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int sub = lane / 16, l16 = lane % 16;
-    const int c0 = blockIdx.y * 32;
+    const int sub = lane / LPR, lr = lane % LPR;
+    const int c0 = blockIdx.x * CPB;
     const int mat = wave / 2;
     const uint8_t* W = (mat ? a.up.codes : a.gate.codes) + (size_t)e * F * (H / 2);
     const uint8_t* S = (mat ? a.up.gscales : a.gate.gscales) + (size_t)e * F * (H / 16);
@@ -579,26 +643,33 @@ __global__ __launch_bounds__(256) void nvfp4_gateup_kernel(GroupedArgs a, int KS
         for (int ps = 0; ps < 4; ++ps)
 #pragma unroll
             for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
-        for (int k0 = kb; k0 < ke; k0 += kBfChunkK) {
-            const int kl = min(kBfChunkK, ke - k0), nx = kl / 8;
-            __syncthreads();
-            for (int it = threadIdx.x; it < nr * nx; it += blockDim.x) {
-                const int i = it / nx, v = it % nx;
-                const int t = row_token(a.sorted_pair, a.k, rc + i);
-                xs[i * (kBfChunkK / 8) + v] = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + k0)[v];
-            }
-            __syncthreads();
+        for (int k0 = kb; k0 < ke; k0 += CK) {
+            const int kl = min(CK, ke - k0), nx = kl / 8;
             const uint4* rows[4];
             const uint8_t* srow[4];
 #pragma unroll
             for (int ps = 0; ps < 4; ++ps) {
-                const int col = c0 + (wave % 2) * 16 + ps * 4 + sub;
+                const int col = c0 + (wave % 2) * CW + ps * RPW + sub;
                 rows[ps] = reinterpret_cast<const uint4*>(W + (size_t)col * (H / 2) + k0 / 2);
                 srow[ps] = S + (size_t)col * (H / 16);
             }
+            uint4 wn[4];
+            uint32_t sn[4];
+            if (kNvGateUnroll == 0 && lr < kl / 32)
+                nvfp4_load_vec<4>(rows, srow, k0, lr, wn, sn);  // in flight during the staging
+            __syncthreads();
+            for (int it = threadIdx.x; it < nr * nx; it += blockDim.x) {
+                const int i = it / nx, v = it % nx;
+                const int t = row_token(a.sorted_pair, a.k, rc + i);
+                xs[i * (CK / 8) + v] = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + k0)[v];
+            }
+            __syncthreads();
             auto body = [&](auto rtag) {
                 constexpr int R = decltype(rtag)::value;
-                nvfp4_stream_dot<R, 4, RCH>(rows, srow, k0, kl / 32, l16, xs, kBfChunkK / 8, acc);
+                if constexpr (kNvGateUnroll == 0)
+                    nvfp4_stream_dot_pf<R, 4, LPR, RCH>(rows, srow, k0, kl / 32, lr, xs, CK / 8, acc, wn, sn);
+                else
+                    nvfp4_stream_dot<R, 4, kNvGateUnroll, LPR, RCH>(rows, srow, k0, kl / 32, lr, xs, CK / 8, acc);
             };
             dispatch_rows<RCH>(nr, body);
         }
@@ -607,16 +678,14 @@ __global__ __launch_bounds__(256) void nvfp4_gateup_kernel(GroupedArgs a, int KS
 #pragma unroll
             for (int i = 0; i < RCH; ++i) {
                 float v = acc[ps][i];
-                v += __shfl_xor(v, 1, kWave);
-                v += __shfl_xor(v, 2, kWave);
-                v += __shfl_xor(v, 4, kWave);
-                v += __shfl_xor(v, 8, kWave);
-                if (l16 == 0) outv[wave * 16 + ps * 4 + sub][i] = v * gscale;
+#pragma unroll
+                for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, kWave);
+                if (lr == 0) outv[wave * CW + ps * RPW + sub][i] = v * gscale;
             }
         __syncthreads();
-        for (int it = threadIdx.x; it < 64 * nr; it += blockDim.x) {
-            const int o = it % 64, i = it / 64;
-            const int m = o / 32, col = c0 + o % 32;
+        for (int it = threadIdx.x; it < 2 * CPB * nr; it += blockDim.x) {
+            const int o = it % (2 * CPB), i = it / (2 * CPB);
+            const int m = o / CPB, col = c0 + o % CPB;
             part[((size_t)ks * a.P + rc + i) * (2 * F) + m * F + col] = outv[o][i];
         }
     }
@@ -700,7 +769,7 @@ __device__ __forceinline__ void stage_swiglu(const float* __restrict__ part,
 }
 
 // ---------------------------------------------------------------------------
-// AWQ down: grid (expert slot, OW/OWC column chunks); block = OWC * RP.
+// AWQ down: grid (OW/OWC column chunks, expert slot); block = OWC * RP.
 // ---------------------------------------------------------------------------
 template <int RCH>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void awq_down_kernel(GroupedArgs a, int KS, int OWC,
@@ -710,12 +779,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     __shared__ float xsum[RCH * 64];
     extern __shared__ float red[];  // [RCH][8*OWC]
     int r0, r1;
-    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    const int e = a.offsets ? slot_expert(a.slots, blockIdx.y, &r0, &r1) : 0;
     if (!a.offsets) { r0 = 0; r1 = a.T; }
     if (e < 0) return;
     const int H = a.H, F = a.F, OW = H / 8, G = F / 32, npairs = F / 2;
     const int cl = threadIdx.x % OWC, rp = threadIdx.x / OWC, RP = blockDim.x / OWC;
-    const int c = blockIdx.y * OWC + cl;
+    const int c = blockIdx.x * OWC + cl;
     const int32_t* qw = a.down.qweight + (size_t)e * F * OW;
     const int32_t* qz = a.down.qzeros + (size_t)e * G * OW;
     const uint16_t* sc = a.down.scales + (size_t)e * G * H;
@@ -740,7 +809,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
         const int ncol = 8 * OWC;
         for (int it = threadIdx.x; it < nr * ncol; it += blockDim.x) {
             const int i = it / ncol, col = it % ncol;
-            const size_t o = (size_t)(rc + i) * H + (size_t)blockIdx.y * ncol + col;
+            const size_t o = (size_t)(rc + i) * H + (size_t)blockIdx.x * ncol + col;
             const float v = red[i * ncol + col];
             if (a.out_f32) static_cast<float*>(a.rows)[o] = v;
             else static_cast<uint16_t*>(a.rows)[o] = (uint16_t)f32_to_bf16_bits(v);
@@ -749,7 +818,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
 }
 
 // ---------------------------------------------------------------------------
-// bf16 down: grid (expert slot, H/(16*npass) row chunks); block 256; 16 lanes
+// bf16 down: grid (H/(16*npass) row chunks, expert slot); block 256; 16 lanes
 // per weight row; each WG covers 16*npass output rows.
 // ---------------------------------------------------------------------------
 template <int R, int NPASS, int RA>
@@ -763,7 +832,7 @@ __device__ __forceinline__ void bf16_down_dot(const uint16_t* __restrict__ W, in
     bf16_stream_dot<R, NPASS, (NPASS >= 4 ? 2 : 4)>(rows, F / 8, l16, hv, F / 8, acc);
 }
 
-// The down projection of bf16 (WF 0), FP8 (WF 2) or NVFP4 (WF 3) experts.
+// The down projection of bf16 (WF 0) or FP8 (WF 2) experts.
 template <int RCH, int NPASS, int WF = 0>
 __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
                                                         const float* __restrict__ part,
@@ -772,20 +841,19 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
     __shared__ uint32_t h2[RCH * kGemvMaxKPairs];
     __shared__ float outv[64][RCH];
     int r0, r1;
-    const int e = a.offsets ? slot_expert(a.offsets, a.E, blockIdx.x, &r0, &r1) : 0;
+    const int e = a.offsets ? slot_expert(a.slots, blockIdx.y, &r0, &r1) : 0;
     if (!a.offsets) { r0 = 0; r1 = a.T; }
     if (e < 0) return;
     const int H = a.H, F = a.F;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int sub = lane / 16, l16 = lane % 16;
-    const int o0 = blockIdx.y * 16 * npass;
+    const int o0 = blockIdx.x * 16 * npass;
     const uint16_t* W = a.down.w + (size_t)e * H * F;
     const uint4* hv = reinterpret_cast<const uint4*>(h2);
-    const float oscale = WF == 3 ? a.down.act * a.down.wglobal[e] : 1.0f;
     for (int rc = r0; rc < r1; rc += RCH) {
         const int nr = min(RCH, r1 - rc);
         __syncthreads();
-        stage_swiglu<RCH>(part, hsrc, KS, a.P, F, rc, nr, h2, WF == 3 ? a.down.act : 0.0f);
+        stage_swiglu<RCH>(part, hsrc, KS, a.P, F, rc, nr, h2);
         __syncthreads();
         float acc[4][RCH];
 #pragma unroll
@@ -794,19 +862,7 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
             for (int i = 0; i < RCH; ++i) acc[ps][i] = 0.0f;
         auto body = [&](auto rtag) {
             constexpr int R = decltype(rtag)::value;
-            if constexpr (WF == 3) {
-                const uint4* rows[NPASS];
-                const uint8_t* srow[NPASS];
-                const uint8_t* C = a.down.codes + (size_t)e * H * (F / 2);
-                const uint8_t* S = a.down.gscales + (size_t)e * H * (F / 16);
-#pragma unroll
-                for (int ps = 0; ps < NPASS; ++ps) {
-                    const int o = o0 + ps * 16 + wave * 4 + sub;
-                    rows[ps] = reinterpret_cast<const uint4*>(C + (size_t)o * (F / 2));
-                    srow[ps] = S + (size_t)o * (F / 16);
-                }
-                nvfp4_stream_dot<R, NPASS, RCH>(rows, srow, 0, F / 32, l16, hv, F / 8, acc);
-            } else if constexpr (WF == 2) {
+            if constexpr (WF == 2) {
                 const uint4* rows[NPASS];
                 const float* srow[NPASS];
                 const uint8_t* C = a.down.codes + (size_t)e * H * F;
@@ -832,10 +888,86 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
                 v += __shfl_xor(v, 2, kWave);
                 v += __shfl_xor(v, 4, kWave);
                 v += __shfl_xor(v, 8, kWave);
-                if (l16 == 0 && ps < npass) outv[ps * 16 + wave * 4 + sub][i] = WF == 3 ? v * oscale : v;
+                if (l16 == 0 && ps < npass) outv[ps * 16 + wave * 4 + sub][i] = v;
             }
         __syncthreads();
         const int nrows = 16 * npass;
+        for (int it = threadIdx.x; it < nrows * nr; it += blockDim.x) {
+            const int o = it % nrows, i = it / nrows;
+            const size_t idx = (size_t)(rc + i) * H + o0 + o;
+            const float v = outv[o][i];
+            if (a.out_f32) static_cast<float*>(a.rows)[idx] = v;
+            else static_cast<uint16_t*>(a.rows)[idx] = (uint16_t)f32_to_bf16_bits(v);
+        }
+    }
+}
+
+// NVFP4 down: a row of W_down is F/2 bytes (20 vectors at F = 640), so LPR
+// lanes (few) share a row and a wave covers 64 / LPR rows per pass.  Grid
+// (H / rows per workgroup, expert slot); block 256; lane q = lane / LPR of
+// wave w takes rows o0 + p * 4 * (64 / LPR) + w * (64 / LPR) + q, p < NP.  The
+// SwiGLU product is staged (quantised) in LDS once per row chunk; the global
+// factor act_scale * global_scale[e] scales the sums.
+__host__ __device__ constexpr int nv_down_rows(int np, int lpr) { return np * 4 * (64 / lpr); }
+
+template <int RCH, int NP, int U, int LPR>
+__global__ __launch_bounds__(256) void nvfp4_down_kernel(GroupedArgs a, int KS, const float* __restrict__ part,
+                                                         const uint32_t* __restrict__ hsrc) {
+    constexpr int RPW = 64 / LPR, RPP = 4 * RPW, NROWS = nv_down_rows(NP, LPR);
+    __shared__ uint32_t h2[RCH * kGemvMaxKPairs];
+    __shared__ float outv[NROWS][RCH];
+    int r0, r1;
+    const int e = a.offsets ? slot_expert(a.slots, blockIdx.y, &r0, &r1) : 0;
+    if (!a.offsets) { r0 = 0; r1 = a.T; }
+    if (e < 0) return;
+    const int H = a.H, F = a.F;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int q = lane / LPR, lr = lane % LPR;
+    const int o0 = blockIdx.x * NROWS;
+    const int nrows = min(NROWS, H - o0);
+    const float oscale = a.down.act * a.down.wglobal[e];
+    const uint8_t* C = a.down.codes + (size_t)e * H * (F / 2);
+    const uint8_t* S = a.down.gscales + (size_t)e * H * (F / 16);
+    const uint4* rows[NP];
+    const uint8_t* srow[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int o = min(o0 + p * RPP + wave * RPW + q, H - 1);  // rows past H repeat the last, unused
+        rows[p] = reinterpret_cast<const uint4*>(C + (size_t)o * (F / 2));
+        srow[p] = S + (size_t)o * (F / 16);
+    }
+    const uint4* hv = reinterpret_cast<const uint4*>(h2);
+    for (int rc = r0; rc < r1; rc += RCH) {
+        const int nr = min(RCH, r1 - rc);
+        uint4 wn[NP];
+        uint32_t sn[NP];
+        if (lr < F / 32) nvfp4_load_vec<NP>(rows, srow, 0, lr, wn, sn);  // in flight during the staging
+        __syncthreads();
+        stage_swiglu<RCH>(part, hsrc, KS, a.P, F, rc, nr, h2, a.down.act);
+        __syncthreads();
+        float acc[4][RCH];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) acc[p][i] = 0.0f;
+        auto body = [&](auto rtag) {
+            constexpr int R = decltype(rtag)::value;
+            if constexpr (U == 0)
+                nvfp4_stream_dot_pf<R, NP, LPR, RCH>(rows, srow, 0, F / 32, lr, hv, F / 8, acc, wn, sn);
+            else
+                nvfp4_stream_dot<R, NP, U, LPR, RCH>(rows, srow, 0, F / 32, lr, hv, F / 8, acc);
+        };
+        dispatch_rows<RCH>(nr, body);
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int i = 0; i < RCH; ++i) {
+                float v = acc[p][i];
+#pragma unroll
+                for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, kWave);
+                if (lr == 0) outv[p * RPP + wave * RPW + q][i] = v * oscale;
+            }
+        __syncthreads();
         for (int it = threadIdx.x; it < nrows * nr; it += blockDim.x) {
             const int o = it % nrows, i = it / nrows;
             const size_t idx = (size_t)(rc + i) * H + o0 + o;
@@ -855,7 +987,8 @@ __global__ __launch_bounds__(256) void bf16_down_kernel(GroupedArgs a, int KS,
 int gemv_ksplit(const GroupedArgs& a) {
     if (!a.awq) {
         const int slots = a.offsets ? (a.P < a.E ? a.P : a.E) : 1;
-        const long wgs = (long)slots * (a.F / 32);
+        const int cols = a.nvfp4 && a.F % nv_gate_cols(kNvGateLanes) == 0 ? nv_gate_cols(kNvGateLanes) : 32;
+        const long wgs = (long)slots * (a.F / cols);
         int ks = 1;
         while (wgs * ks < 1024 && ks < 8 && (a.H / 8) % (ks * 2) == 0) ks *= 2;
         return ks;
@@ -866,6 +999,8 @@ int gemv_ksplit(const GroupedArgs& a) {
     while ((G + ks - 1) / ks * 16 > kGemvMaxKPairs) ++ks;  // LDS bound
     return ks;
 }
+
+static size_t slot_table_bytes(int P) { return ((size_t)P * sizeof(int4) + 255) & ~(size_t)255; }
 
 static size_t part_bytes(int P, int F, int ks) {
     return ((size_t)ks * P * 2 * F * sizeof(float) + 255) & ~(size_t)255;
@@ -879,8 +1014,8 @@ size_t gemv_ws_bytes(int P, int H, int F, int awq) {
         a.awq = awq;
         ks = gemv_ksplit(a);
     }
-    // partial sums, then h [P][F] bf16
-    return part_bytes(P, F, ks) + (size_t)P * F * sizeof(uint16_t);
+    // slot table, partial sums, then h [P][F] bf16
+    return slot_table_bytes(P) + part_bytes(P, F, ks) + (size_t)P * F * sizeof(uint16_t);
 }
 
 static int down_owc(int OW) {
@@ -899,6 +1034,9 @@ static int row_phases(int OW) {
     return rp;
 }
 
+// Grids put the column (or row) chunk along x and the expert slot along y, so
+// workgroups that are dispatched one after another stream adjacent parts of
+// one expert's weights (measured faster than slot-major order).
 template <int RCH>
 static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s) {
     const int slots = a.offsets ? (a.P < a.E ? a.P : a.E) : 1;
@@ -912,7 +1050,7 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s)
         const int OW = F / 8;
         const int RP = row_phases(OW);
         const size_t red_bytes = (size_t)RCH * F * sizeof(float);
-        hipLaunchKernelGGL(awq_gateup_kernel<RCH>, dim3(slots, 2 * KS), dim3(OW * RP), red_bytes, s,
+        hipLaunchKernelGGL(awq_gateup_kernel<RCH>, dim3(2 * KS, slots), dim3(OW * RP), red_bytes, s,
                            a, KS, part);
         if (hbuf) {
             const long pairs = (long)a.P * (F / 2);
@@ -921,7 +1059,7 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s)
         }
         const int OWd = H / 8, OWC = down_owc(OWd);
         const int RPd = row_phases(OWC);
-        hipLaunchKernelGGL(awq_down_kernel<RCH>, dim3(slots, OWd / OWC), dim3(OWC * RPd),
+        hipLaunchKernelGGL(awq_down_kernel<RCH>, dim3(OWd / OWC, slots), dim3(OWC * RPd),
                            (size_t)RCH * 8 * OWC * sizeof(float), s, a, KS, OWC,
                            (const float*)part, (const uint32_t*)hbuf);
       } else {
@@ -929,36 +1067,39 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s)
       }
     } else if (a.nvfp4) {
       if constexpr (RCH <= 8) {
-        hipLaunchKernelGGL(nvfp4_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS, part);
+        if (F % nv_gate_cols(kNvGateLanes) == 0)
+            hipLaunchKernelGGL((nvfp4_gateup_kernel<RCH, kNvGateLanes>), dim3(F / nv_gate_cols(kNvGateLanes), slots, KS),
+                               dim3(256), 0, s, a, KS, part);
+        else
+            hipLaunchKernelGGL((nvfp4_gateup_kernel<RCH, 16>), dim3(F / nv_gate_cols(16), slots, KS), dim3(256), 0,
+                               s, a, KS, part);
         if (hbuf) {
             const long pairs = (long)a.P * (F / 2);
             hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
                                s, (const float*)part, KS, a.P, F, a.down.act, hbuf);
         }
-        if ((long)slots * (H / 64) >= 1024)
-            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4, 3>), dim3(slots, H / 64), dim3(256), 0, s, a, KS,
-                               (const float*)part, (const uint32_t*)hbuf);
-        else
-            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1, 3>), dim3(slots, H / 16), dim3(256), 0, s, a, KS,
-                               (const float*)part, (const uint32_t*)hbuf);
+        constexpr int DR = nv_down_rows(kNvDownRows, kNvDownLanes);
+        hipLaunchKernelGGL((nvfp4_down_kernel<RCH, kNvDownRows, kNvDownUnroll, kNvDownLanes>),
+                           dim3((H + DR - 1) / DR, slots), dim3(256), 0, s, a, KS, (const float*)part,
+                           (const uint32_t*)hbuf);
       } else {
         return hipErrorInvalidValue;  // NVFP4 takes at most eight rows per pass
       }
     } else if (a.fp8) {
-        hipLaunchKernelGGL(fp8_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS, part);
+        hipLaunchKernelGGL(fp8_gateup_kernel<RCH>, dim3(F / 32, slots, KS), dim3(256), 0, s, a, KS, part);
         if (hbuf) {
             const long pairs = (long)a.P * (F / 2);
             hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
                                s, (const float*)part, KS, a.P, F, 0.0f, hbuf);
         }
         if ((long)slots * (H / 64) >= 1024)
-            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4, 2>), dim3(slots, H / 64), dim3(256), 0, s, a, KS,
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4, 2>), dim3(H / 64, slots), dim3(256), 0, s, a, KS,
                                (const float*)part, (const uint32_t*)hbuf);
         else
-            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1, 2>), dim3(slots, H / 16), dim3(256), 0, s, a, KS,
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1, 2>), dim3(H / 16, slots), dim3(256), 0, s, a, KS,
                                (const float*)part, (const uint32_t*)hbuf);
     } else {
-        hipLaunchKernelGGL(bf16_gateup_kernel<RCH>, dim3(slots, F / 32, KS), dim3(256), 0, s, a, KS,
+        hipLaunchKernelGGL(bf16_gateup_kernel<RCH>, dim3(F / 32, slots, KS), dim3(256), 0, s, a, KS,
                            part);
         if (hbuf) {
             const long pairs = (long)a.P * (F / 2);
@@ -967,16 +1108,51 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s)
         }
         // rows per down workgroup: 64, or 16 when few experts are active
         if ((long)slots * (H / 64) >= 1024)
-            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4>), dim3(slots, H / 64), dim3(256), 0, s, a, KS,
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 4>), dim3(H / 64, slots), dim3(256), 0, s, a, KS,
                                (const float*)part, (const uint32_t*)hbuf);
         else
-            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1>), dim3(slots, H / 16), dim3(256), 0, s, a, KS,
+            hipLaunchKernelGGL((bf16_down_kernel<RCH, 1>), dim3(H / 16, slots), dim3(256), 0, s, a, KS,
                                (const float*)part, (const uint32_t*)hbuf);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_gemv(const GroupedArgs& a, void* ws, hipStream_t s) {
+// Slot table of a grouped call: slot i (< nslots) = the i-th non-empty expert
+// in index order with its row range; later slots get expert -1.  One block of
+// 1024 threads (E <= 1024): a ballot prefix count of the non-empty experts.
+__global__ __launch_bounds__(1024) void slot_table_kernel(const int32_t* __restrict__ offsets, int E, int nslots,
+                                                          int4* __restrict__ slots) {
+    __shared__ int wsum[16];
+    const int e = threadIdx.x, lane = e % kWave, wave = e / kWave;
+    int r0 = 0, r1 = 0;
+    if (e < E) {
+        r0 = offsets[e];
+        r1 = offsets[e + 1];
+    }
+    const bool ne = r1 > r0;
+    const unsigned long long m = __ballot(ne);
+    if (lane == 0) wsum[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        before += w < wave ? wsum[w] : 0;
+        total += wsum[w];
+    }
+    const int pos = before + __popcll(m & ((1ull << lane) - 1ull));
+    if (ne && pos < nslots) slots[pos] = make_int4(e, r0, r1, 0);
+    if (e >= total && e < nslots) slots[e] = make_int4(-1, 0, 0, 0);
+}
+
+hipError_t launch_gemv(const GroupedArgs& a0, void* ws, hipStream_t s) {
+    GroupedArgs a = a0;
+    a.slots = nullptr;
+    if (a.offsets) {
+        int4* tab = static_cast<int4*>(ws);
+        ws = static_cast<char*>(ws) + slot_table_bytes(a.P);
+        hipLaunchKernelGGL(slot_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.P < a.E ? a.P : a.E, tab);
+        a.slots = tab;
+    }
     // rows per pass: a bf16 shared expert sees every token (all of a decode
     // batch in one pass); a routed expert at decode sees one or two, and the
     // AWQ kernels keep two rows per pass to hold the next group's words in

@@ -29,6 +29,7 @@ struct GroupedArgs {
     int nvfp4;                  // 1: NVFP4 W4A4 (x already quantised)
     const int32_t* offsets;     // [E+1] or nullptr (identity: E == 1, row r = token r)
     const int32_t* sorted_pair; // [P] or nullptr
+    const int4* slots;          // GEMV work slots: (expert, first row, end row), expert -1 = none
     ProjDev gate, up, down;
     int out_f32;
     void* rows;                 // [P][H]
@@ -49,45 +50,14 @@ size_t dense_gemm_ws_bytes(int M);
 hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t* B, int N, float* C,
                                  void* ws, hipStream_t s);
 
-// Find the expert of work slot `slot` among the non-empty experts of
-// offsets[0..E] (slot-th non-empty expert in index order).  Block-wide; every
-// thread gets the same answer.  Returns -1 when there is no such expert.
-__device__ __forceinline__ int slot_expert(const int32_t* offsets, int E, int slot, int* r0,
-                                           int* r1) {
-    __shared__ unsigned long long s_mask[16];
-    __shared__ int s_e, s_r0, s_r1;
-    const int tid = threadIdx.x;
-    // ballots from complete waves only (a partial wave would see a partial mask)
-    const int lane = tid % kWave, wave = tid / kWave, nfull = blockDim.x / kWave;
-    if (wave < nfull) {
-        for (int chunk = wave; chunk < 16; chunk += nfull) {
-            const int e = chunk * kWave + lane;
-            const bool ne = e < E && offsets[e + 1] > offsets[e];
-            const unsigned long long m = __ballot(ne);
-            if (lane == 0) s_mask[chunk] = m;
-        }
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int found = -1, left = slot;
-        for (int chunk = 0; chunk < 16 && found < 0; ++chunk) {
-            unsigned long long m = s_mask[chunk];
-            const int c = __popcll(m);
-            if (left < c) {
-                for (int i = 0; i < left; ++i) m &= m - 1;  // drop lowest set bits
-                found = chunk * kWave + __ffsll((long long)m) - 1;
-            } else {
-                left -= c;
-            }
-        }
-        s_e = found;
-        s_r0 = found >= 0 ? offsets[found] : 0;
-        s_r1 = found >= 0 ? offsets[found + 1] : 0;
-    }
-    __syncthreads();
-    *r0 = s_r0;
-    *r1 = s_r1;
-    return s_e;
+// Expert and rows of GEMV work slot `slot` (workgroup index along x): one
+// uniform 16-byte load from the slot table built for the call.  Returns -1
+// for a slot past the last non-empty expert.
+__device__ __forceinline__ int slot_expert(const int4* slots, int slot, int* r0, int* r1) {
+    const int4 t = slots[slot];
+    *r0 = t.y;
+    *r1 = t.z;
+    return t.x;
 }
 
 }  // namespace moe
