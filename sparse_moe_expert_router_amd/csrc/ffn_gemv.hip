@@ -35,7 +35,7 @@ constexpr bool kAwqPrefetch = false;  // next group's words in flight during the
 struct AwqGroupRegs {
     uint32_t w[32];
     uint32_t z;
-    uint4 s;
+    u32x4_t s;  // a native vector (HIP's uint4 class can keep a copy in scratch)
 };
 
 __device__ __forceinline__ void awq_load_group(const int32_t* __restrict__ qw,
@@ -46,7 +46,7 @@ __device__ __forceinline__ void awq_load_group(const int32_t* __restrict__ qw,
 #pragma unroll
     for (int q = 0; q < 32; ++q) r.w[q] = (uint32_t)wp[(size_t)q * OW];
     r.z = (uint32_t)qz[(size_t)g * OW + c];
-    r.s = *reinterpret_cast<const uint4*>(sc + (size_t)g * O + 8 * c);
+    r.s = *reinterpret_cast<const u32x4_t*>(sc + (size_t)g * O + 8 * c);
 }
 
 template <int RCH>
@@ -76,7 +76,7 @@ __device__ __forceinline__ void awq_group_dot(const AwqGroupRegs& r, const uint3
             for (int j = 0; j < 8; ++j) acc[j][i] = dot2_bf16(v[j], xp, acc[j][i]);
         }
     }
-    const uint32_t sw[4] = {r.s.x, r.s.y, r.s.z, r.s.w};
+    const uint32_t sw[4] = {r.s[0], r.s[1], r.s[2], r.s[3]};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int col = kAwqNib[j];
