@@ -11,7 +11,7 @@
 //
 // Workgroup: 4 waves, tile BM rows x 256 B-columns, K step 32 (= one AWQ
 // group).  BM = 256: waves 2 x 2, each 128 x 128 (64 accumulator tiles of
-// v_mfma_f32_16x16x32_bf16, 256 fp32 per lane); BM = 128 / 64: waves 1 x 4,
+// v_mfma_f32_16x16x32_bf16, 256 fp32 per lane); BM = 128 / 96 / 64: waves 1 x 4,
 // each BM x 64.  For gate/up the 256 B-columns are 128 gate columns and the
 // same 128 up columns; every wave holds matching gate and up tiles, so SwiGLU
 // is applied in registers.
@@ -126,7 +126,8 @@ struct GemmShape {
     static constexpr int MW = BM / WM;            // rows per wave
     static constexpr int NW = kBN / WN;           // B-columns per wave
     static constexpr int TM = MW / 16, TN = NW / 16;
-    static constexpr int APER = BM * 4 / NT;      // 16-byte A chunks per thread per step
+    static constexpr int AQ = BM * 4;             // 16-byte A chunks per step
+    static constexpr int APER = (AQ + NT - 1) / NT;  // per thread (BM = 96: the second covers half the threads)
     static constexpr int BPER = kBN * 4 / NT;     // 16-byte bf16 B chunks per thread per step
     static constexpr int RPT = 1024 / NT;         // AWQ: input rows per thread per step (one word column)
 };
@@ -244,7 +245,7 @@ __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APE
 #pragma unroll
     for (int i = 0; i < S::APER; ++i) {
         const int q = tid + i * S::NT;
-        *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[i];
+        if (S::AQ % S::NT == 0 || q < S::AQ) *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[i];
     }
     if (FP8) {
 #pragma unroll
@@ -326,7 +327,7 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
     for (int j = 0; j < 8; ++j) {
         if (j < S::APER) {
             const int q = tid + j * S::NT;
-            *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[j];
+            if (S::AQ % S::NT == 0 || q < S::AQ) *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[j];
         }
         if (FP8) {
             if (j < S::BPER / 2) fp8_store_chunk(rb[j], __uint_as_float(rw[j]), Bs, tid + j * S::NT);
@@ -648,11 +649,14 @@ static int max_tiles(int P, int E, int BM) { return (P + BM - 1) / BM + E; }
 // Grid for `mt` row tiles x `nt` column tiles: a multiple of the XCD count.
 static dim3 gemm_grid(int mt, int nt) { return dim3((unsigned)(((long)mt * nt + kXcd - 1) / kXcd * kXcd)); }
 
-// Row tile from the average rows per non-empty expert.
+// Row tile from the average rows per non-empty expert: one tile should hold
+// most experts whole (a second, mostly empty tile reads the expert's weights
+// again).
+constexpr int kBm128From = 96, kBm96From = 64;
 static int pick_bm(int P, int E) {
     const int active = P < E ? P : E;
     const int avg = active > 0 ? P / active : 0;
-    return avg >= 128 ? 256 : (avg >= 96 ? 128 : 64);
+    return avg >= 128 ? 256 : (avg >= kBm128From ? 128 : (avg >= kBm96From ? 96 : 64));
 }
 
 // Row tile of a single dense product (the shared expert, the router's
@@ -706,6 +710,7 @@ hipError_t launch_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
     hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, BM, tiles);
     if (BM == 256) launch_gemm_bm<256>(a, tiles, hbuf, mt, s);
     else if (BM == 128) launch_gemm_bm<128>(a, tiles, hbuf, mt, s);
+    else if (BM == 96) launch_gemm_bm<96>(a, tiles, hbuf, mt, s);
     else launch_gemm_bm<64>(a, tiles, hbuf, mt, s);
     return hipGetLastError();
 }
