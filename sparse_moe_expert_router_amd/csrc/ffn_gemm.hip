@@ -9,10 +9,9 @@
 //   gate/up: h[r] = silu(W_gate x_t) * (W_up x_t)   A = gathered token rows
 //   down:    rows[r] = W_down h[r]                  A = h rows (contiguous)
 //
-// Workgroup: 4 waves, tile BM rows x 256 B-columns, K step 32 (= one AWQ
-// group).  BM = 256: waves 2 x 2, each 128 x 128 (64 accumulator tiles of
-// v_mfma_f32_16x16x32_bf16, 256 fp32 per lane); BM = 128 / 96 / 64: waves 1 x 4,
-// each BM x 64.  For gate/up the 256 B-columns are 128 gate columns and the
+// Workgroup: tile BM rows x 256 B-columns, K step 32 (= one AWQ group).
+// BM = 256 / 192: 8 waves, 2 x 4, each 128 (96) x 64; BM = 128 / 96 / 64:
+// 4 waves, 1 x 4, each BM x 64.  For gate/up the 256 B-columns are 128 gate columns and the
 // same 128 up columns; every wave holds matching gate and up tiles, so SwiGLU
 // is applied in registers.
 //
@@ -120,7 +119,7 @@ __device__ __forceinline__ int awq_row(int c) { return c ^ ((c >> 3) & 3); }
 
 template <int BM>
 struct GemmShape {
-    static constexpr int WM = BM == 256 ? 2 : 1;  // waves along rows
+    static constexpr int WM = BM >= 192 ? 2 : 1;  // waves along rows
     static constexpr int WN = 4;                  // waves along columns
     static constexpr int NT = WM * WN * kWave;    // threads
     static constexpr int MW = BM / WM;            // rows per wave
@@ -548,16 +547,17 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
 #undef MOE_PARAMS
 
     // ---- epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile.
-    // Each wave passes its tile through a private 8 KB LDS region (the stages
-    // are free after one block barrier) as fp32, 16 rows at a time; row
-    // strides of 64 + 4 (32 + 4) floats put the four lane groups' rows on
-    // different banks.  It then writes whole 16-byte vectors of a row.  The
-    // region is the wave's own, so only the wave's LDS accesses need ordering.
+    // Each wave passes its tile through a private 4.5 KB LDS region (the
+    // stages are free after one block barrier: waves 0-3 in the B stages,
+    // 4-7 in the A stages) as fp32, 16 rows at a time; row strides of 64 + 4
+    // (32 + 4) floats put the four lane groups' rows on different banks.  It
+    // then writes whole 16-byte vectors of a row.  The region is the wave's
+    // own, so only the wave's LDS accesses need ordering.
+    constexpr int kStage = 4608;  // bytes per wave: 16 rows x (64 + 4) floats
+    static_assert(sizeof(Bs) >= 4 * kStage && (NTHR / kWave <= 4 || sizeof(As) >= 4 * kStage), "epilogue staging");
     __syncthreads();
-    float* st = reinterpret_cast<float*>(
-        NTHR / kWave > 4 ? (wave < 4 ? reinterpret_cast<char*>(&As[0][0]) + wave * 8192
-                                     : reinterpret_cast<char*>(&Bs[0][0]) + (wave - 4) * 8192)
-                         : reinterpret_cast<char*>(&Bs[0][0]) + wave * 8192);
+    float* st = reinterpret_cast<float*>(wave < 4 ? reinterpret_cast<char*>(&Bs[0][0]) + wave * kStage
+                                                  : reinterpret_cast<char*>(&As[0][0]) + (wave - 4) * kStage);
     const int wrow = m0 + wm * S::MW;  // first row of the wave tile
     // NVFP4 global factors of the accumulators (1 for the other formats)
     float cg = 1.0f, cu = 1.0f, cd = 1.0f;
@@ -652,11 +652,11 @@ static dim3 gemm_grid(int mt, int nt) { return dim3((unsigned)(((long)mt * nt + 
 // Row tile from the average rows per non-empty expert: one tile should hold
 // most experts whole (a second, mostly empty tile reads the expert's weights
 // again).
-constexpr int kBm128From = 96, kBm96From = 64;
+constexpr int kBm256From = 192, kBm192From = 128, kBm128From = 96, kBm96From = 64;
 static int pick_bm(int P, int E) {
     const int active = P < E ? P : E;
     const int avg = active > 0 ? P / active : 0;
-    return avg >= 128 ? 256 : (avg >= kBm128From ? 128 : (avg >= kBm96From ? 96 : 64));
+    return avg >= kBm256From ? 256 : avg >= kBm192From ? 192 : avg >= kBm128From ? 128 : avg >= kBm96From ? 96 : 64;
 }
 
 // Row tile of a single dense product (the shared expert, the router's
@@ -709,6 +709,7 @@ hipError_t launch_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
     uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + tiles_bytes(a.P, E));
     hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, BM, tiles);
     if (BM == 256) launch_gemm_bm<256>(a, tiles, hbuf, mt, s);
+    else if (BM == 192) launch_gemm_bm<192>(a, tiles, hbuf, mt, s);
     else if (BM == 128) launch_gemm_bm<128>(a, tiles, hbuf, mt, s);
     else if (BM == 96) launch_gemm_bm<96>(a, tiles, hbuf, mt, s);
     else launch_gemm_bm<64>(a, tiles, hbuf, mt, s);

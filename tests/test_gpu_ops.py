@@ -141,6 +141,7 @@ def _random_routing(T, k, E, seed):
                                        (200, 8, 2, 256, 128),     # 50 rows: MFMA, 64-row tiles
                                        (300, 8, 2, 256, 128),     # 75 rows: 96-row tiles (uneven A chunks)
                                        (400, 8, 2, 256, 128),     # 100 rows: 128-row tiles
+                                       (600, 8, 2, 256, 128),     # 150 rows: 192-row tiles
                                        (1100, 8, 2, 256, 128),    # 275 rows: 256-row tiles + tails
                                        (8, 4, 2, 2560, 640),      # full width, streaming
                                        (16, 512, 10, 2560, 640),  # decode geometry, streaming
