@@ -57,6 +57,10 @@ constexpr int kXcd = 8;
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
+// A fragments read one slice before their first MFMA instead of all at the
+// start of a K step (fewer live registers).
+constexpr bool kLazyA = true;
+
 // Orders a wave's own LDS accesses (writes by some lanes, then reads by
 // others): LDS instructions of one wave complete in issue order, so only the
 // compiler must be kept from moving them across this point.
@@ -282,9 +286,11 @@ __device__ __forceinline__ void read_frags(const uint16_t* As, const uint16_t* B
     (void)NV4;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
+    if constexpr (!kLazyA) {
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off(wm * S::MW + mi * 16 + lane % 16, lane / 16)]);
+        for (int mi = 0; mi < TM; ++mi)
+            af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off(wm * S::MW + mi * 16 + lane % 16, lane / 16)]);
+    }
 #pragma unroll
     for (int nj = 0; nj < TN; ++nj) {
         // gate/up: the wave's first TN/2 tiles are gate columns, the rest the matching up columns
@@ -299,14 +305,17 @@ __device__ __forceinline__ void read_frags(const uint16_t* As, const uint16_t* B
 // bf16 B chunks or one dequantised AWQ column) are cut into 8 slices, each
 // followed by 1/8 of this step's MFMAs; scheduling barriers keep the slices
 // in order, so that the VALU and LDS work issues while earlier MFMAs execute.
+// With lazy A fragments, each A fragment is read from the current stage
+// (Acur) one slice before its first MFMA, so only about two are live.
 template <int MODE, int WF, int BM>
-__device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<BM>::TM],
+__device__ __forceinline__ void step_interleaved(bf16x8_t (&af)[GemmShape<BM>::TM],
                                                  const bf16x8_t (&bfr)[GemmShape<BM>::TN],
                                                  f32x4_t (&acc)[GemmShape<BM>::TM][GemmShape<BM>::TN],
                                                  const uint4 (&ra)[GemmShape<BM>::APER],
                                                  const uint4 (&rb)[GemmShape<BM>::BPER],
                                                  const uint32_t (&rw)[GemmShape<BM>::RPT],
-                                                 const float2* Ps, uint16_t* As, uint16_t* Bs, int tid) {
+                                                 const float2* Ps, uint16_t* As, uint16_t* Bs, int tid,
+                                                 const uint16_t* Acur, int wm, int lane) {
     constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
     (void)FP8;
     (void)NV4;
@@ -314,6 +323,14 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
     constexpr int TM = S::TM, TN = S::TN;
     constexpr int NM = TM * TN;  // MFMAs this step
     constexpr int PER = NM / 8;  // per slice
+    auto load_a = [&](int mi) {
+        af[mi] = *reinterpret_cast<const bf16x8_t*>(&Acur[lds_off(wm * S::MW + mi * 16 + lane % 16, lane / 16)]);
+    };
+    if constexpr (kLazyA) {
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+            if ((mi * TN) / PER == 0) load_a(mi);  // fragments first used in slice 0
+    }
     int cbase = 0, sub = 0;
     uint32_t even[S::RPT], odd[S::RPT];
     float sc[8], cc[8];
@@ -339,6 +356,11 @@ __device__ __forceinline__ void step_interleaved(const bf16x8_t (&af)[GemmShape<
             }
         } else {
             awq_store_col<MODE, S::RPT>(j, even, odd, sc, cc, Bs, cbase, sub);
+        }
+        if constexpr (kLazyA) {
+#pragma unroll
+            for (int mi = 0; mi < TM; ++mi)
+                if ((mi * TN) / PER == j + 1) load_a(mi);  // first used in the next slice
         }
 #pragma unroll
         for (int m = j * PER; m < (j + 1) * PER; ++m)
@@ -531,7 +553,8 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
         MOE_LOAD(ra0, rb0, rw0, pz0, ps0, min(kt + 2, nk - 1));
         bf16x8_t af[TM], bfr[TN];
         read_frags<MODE, WF, BM>(As[cur], Bs[cur], af, bfr, wm, wn, lane);
-        step_interleaved<MODE, WF, BM>(af, bfr, acc, ra1, rb1, rw1, Ps[cur ^ 1], As[cur ^ 1], Bs[cur ^ 1], tid);
+        step_interleaved<MODE, WF, BM>(af, bfr, acc, ra1, rb1, rw1, Ps[cur ^ 1], As[cur ^ 1], Bs[cur ^ 1], tid,
+                                       As[cur], wm, lane);
         MOE_PARAMS(pz0, ps0, cur);  // parameters of step kt+2 (table cur held step kt's)
         __syncthreads();
 #pragma unroll
