@@ -492,8 +492,9 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Two register stages with the raw global data of one K step each; the loop
-    // is unrolled by two so that they alternate roles without register moves.
+    // Two register stages with the raw global data of one K step each; they
+    // swap roles by value at the end of each step (a third stage, loading
+    // three steps ahead, measured slower).
     uint4 ra0[APER], ra1[APER];
     uint4 rb0[BPER], rb1[BPER];
     uint32_t rw0[S::RPT], rw1[S::RPT];
