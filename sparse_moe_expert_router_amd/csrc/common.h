@@ -71,4 +71,18 @@ __device__ __forceinline__ int find_group(const int32_t* offsets, int n, int i) 
 
 __device__ __forceinline__ double shfl_xor_f64(double v, int m) { return __shfl_xor(v, m, kWave); }
 
+// Maximum of v over the 64 lanes of a wave whose lanes are all active; the
+// result is uniform.  Four DPP steps inside each row of 16 lanes (swap
+// neighbours, swap pairs, mirror the half-row, mirror the row) leave the row
+// maximum in every lane of the row; the four rows are then read as scalars.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
 }  // namespace moe

@@ -26,8 +26,11 @@ __device__ __forceinline__ int bits_for(int E) {
     return b;
 }
 
-// One wave scatters pairs [p0, p1) in order; cursor[e] (LDS) is the next row of e.
-__device__ void wave_scatter(const int32_t* __restrict__ idx, int p0, int p1, int E, int nbits,
+// One wave scatters pairs [p0, p1) in order; cursor[e] (LDS) is the next row
+// of e.  ids: the pairs' expert ids, in global memory (clamped here) or, with
+// kClamped, already clamped (the single-workgroup path keeps them in LDS).
+template <bool kClamped>
+__device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ ids, int p0, int p1, int E, int nbits,
                              int* cursor, int32_t* __restrict__ sorted_pair,
                              int32_t* __restrict__ pair_to_row) {
     const int lane = threadIdx.x % kWave;
@@ -35,7 +38,7 @@ __device__ void wave_scatter(const int32_t* __restrict__ idx, int p0, int p1, in
     for (int c = p0; c < p1; c += kWave) {
         const int p = c + lane;
         const bool active = p < p1;
-        const int e = active ? clamp_expert(idx[p], E) : 0;
+        const int e = !active ? 0 : kClamped ? ids[p] : clamp_expert(ids[p], E);
         uint64_t peers = __ballot(active);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (e >> b) & 1;
@@ -56,44 +59,65 @@ __device__ void wave_scatter(const int32_t* __restrict__ idx, int p0, int p1, in
     }
 }
 
-// Single workgroup: histogram, scan, scatter.  block = 256.
+// Single workgroup: histogram (the clamped expert ids stay in LDS for the
+// scatter), exclusive scan (a wave scan per 64 threads, then the waves'
+// totals), scatter by wave 0.  block = 256, P <= kSmallPairs.
 __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t* __restrict__ idx, int P,
                                                             int E, int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ sorted_pair,
                                                             int32_t* __restrict__ pair_to_row) {
+    constexpr int kBatch = 4;  // id loads in flight per thread
     __shared__ int cnt[1024];
-    __shared__ int scan_tmp[256];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __shared__ int ids[kSmallPairs];
+    __shared__ int wtot[4];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&cnt[clamp_expert(idx[p], E)], 1);
+    for (int p0 = 0; p0 < P; p0 += kBatch * 256) {
+        int ev[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) ev[u] = idx[min(p0 + u * 256 + tid, P - 1)];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int p = p0 + u * 256 + tid;
+            if (p < P) {
+                const int e = clamp_expert(ev[u], E);
+                ids[p] = e;
+                atomicAdd(&cnt[e], 1);
+            }
+        }
+    }
     __syncthreads();
-    // exclusive scan over E (<= 1024): each thread owns 4 consecutive experts
+    // each thread owns experts 4 tid .. 4 tid + 3 (E <= 1024)
     int local[4], sum = 0;
+#pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int e = threadIdx.x * 4 + j;
+        const int e = tid * 4 + j;
         local[j] = e < E ? cnt[e] : 0;
         sum += local[j];
     }
-    scan_tmp[threadIdx.x] = sum;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        int v = threadIdx.x >= off ? scan_tmp[threadIdx.x - off] : 0;
-        __syncthreads();
-        scan_tmp[threadIdx.x] += v;
-        __syncthreads();
+    int inc = sum;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const int o = __shfl_up(inc, m, kWave);
+        if (lane >= m) inc += o;
     }
-    int run = scan_tmp[threadIdx.x] - sum;
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    int run = inc - sum;
+    for (int w = 0; w < wave; ++w) run += wtot[w];
+#pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int e = threadIdx.x * 4 + j;
+        const int e = tid * 4 + j;
         if (e < E) {
-            cnt[e] = run;          // becomes the cursor
+            cnt[e] = run;  // becomes the cursor
             offsets[e] = run;
         }
         run += local[j];
     }
-    if (threadIdx.x == 0) offsets[E] = P;
+    if (tid == 0) offsets[E] = P;
     __syncthreads();
-    if (threadIdx.x < kWave) wave_scatter(idx, 0, P, E, bits_for(E), cnt, sorted_pair, pair_to_row);
+    if (wave == 0) wave_scatter<true>(ids, 0, P, E, bits_for(E), cnt, sorted_pair, pair_to_row);
 }
 
 // Multi-block path, pass 1: per-block histograms counts[b][e].
@@ -176,7 +200,7 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(const int32_t* __re
     for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] = counts[(size_t)blockIdx.x * E + e];
     __syncthreads();
     const int p0 = blockIdx.x * kPermChunk, p1 = min(P, p0 + kPermChunk);
-    wave_scatter(idx, p0, p1, E, bits_for(E), cursor, sorted_pair, pair_to_row);
+    wave_scatter<false>(idx, p0, p1, E, bits_for(E), cursor, sorted_pair, pair_to_row);
 }
 
 size_t permute_ws_bytes(int T, int k, int E) {

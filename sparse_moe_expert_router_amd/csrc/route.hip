@@ -15,68 +15,75 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Exact logits.  One wave per expert row; lanes split the hidden dimension;
-// a tile of up to 16 tokens is staged in LDS in chunks of kLogitChunk
-// columns (one chunk at H = 2560).  Each lane loads its whole share of the
-// router row before the tile is staged, so the row streams in while the
-// activations are copied.
-// grid = (ceil(E / kLogitWaves), ceil(T / 16)), block = 64 * kLogitWaves.
+// a tile of TOK tokens (8 or 16) is staged in LDS in chunks of kLogitChunk
+// columns (one chunk at H = 2560).  Each thread issues all of its loads for
+// a chunk (its share of the router row, then its share of the activation
+// tile) before it waits for any, so a chunk costs one memory round trip.
+// Small batches take 8-token tiles: twice the workgroups, half the fp64 work
+// per wave.
+// grid = (ceil(E / kLogitWaves), ceil(T / TOK)), block = 64 * kLogitWaves.
 // ---------------------------------------------------------------------------
-constexpr int kLogitTok = 16;
 constexpr int kLogitChunk = 2560;
-constexpr int kLogitVecs = kLogitChunk / 8 / kWave;  // 16-byte vectors per lane per chunk
+constexpr int kLogitRowVecs = kLogitChunk / 8;         // 16-byte vectors per token row per chunk
+constexpr int kLogitVecs = kLogitRowVecs / kWave;      // 16-byte vectors per lane per chunk
 constexpr int kLogitWaves = 4;
+constexpr int kLogitThreads = kLogitWaves * kWave;
 
-// Sum a[0..15] over the 64 lanes of a wave.  Halving exchange: at each of the
-// first four steps a lane keeps half of its tokens and adds its partner's
-// share of them; the last two steps add single values.  Afterwards lane L
-// holds the total of token ((L >> 2) & 15) reordered as tok_of_lane() says.
-__device__ __forceinline__ double wave_reduce16(double (&a)[kLogitTok], int lane) {
-    double b[8], c[4], d[2], e;
-    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
+// One halving step of wave_reduce_tokens: lanes with bit MASK set keep the
+// upper half of the N values and receive their partner's upper half.
+template <int N, int MASK>
+__device__ __forceinline__ void halve_tokens(const double (&a)[N], double (&b)[N / 2], int lane) {
+    const bool up = lane & MASK;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const double send = h5 ? a[j] : a[j + 8];
-        const double keep = h5 ? a[j + 8] : a[j];
-        b[j] = keep + shfl_xor_f64(send, 32);
+    for (int j = 0; j < N / 2; ++j) {
+        const double send = up ? a[j] : a[j + N / 2];
+        const double keep = up ? a[j + N / 2] : a[j];
+        b[j] = keep + shfl_xor_f64(send, MASK);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const double send = h4 ? b[j] : b[j + 4];
-        const double keep = h4 ? b[j + 4] : b[j];
-        c[j] = keep + shfl_xor_f64(send, 16);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const double send = h3 ? c[j] : c[j + 2];
-        const double keep = h3 ? c[j + 2] : c[j];
-        d[j] = keep + shfl_xor_f64(send, 8);
-    }
-    {
-        const double send = h2 ? d[0] : d[1];
-        const double keep = h2 ? d[1] : d[0];
-        e = keep + shfl_xor_f64(send, 4);
-    }
-    e += shfl_xor_f64(e, 2);
-    e += shfl_xor_f64(e, 1);
-    return e;
 }
 
-// Token held by lane L after wave_reduce16: bit 5 chose the upper 8, bit 4
-// the upper 4 of those, bit 3 the upper 2, bit 2 the upper one.
+// Sum a[0..N-1] (N a power of two) over the 64 lanes of a wave: log2(N)
+// halving steps with partner masks 32, 16, ..., then single-value steps for
+// the remaining masks.  Afterwards lane L holds the total of token
+// tok_of_lane<N>(L).
+template <int N, int MASK = kWave / 2>
+__device__ __forceinline__ double wave_reduce_tokens(const double (&a)[N], int lane) {
+    if constexpr (N == 1) {
+        double e = a[0];
+#pragma unroll
+        for (int m = MASK; m >= 1; m >>= 1) e += shfl_xor_f64(e, m);
+        return e;
+    } else {
+        static_assert((N & (N - 1)) == 0 && N <= kWave / 2, "N must be a power of two <= 32");
+        double b[N / 2];
+        halve_tokens<N, MASK>(a, b, lane);
+        return wave_reduce_tokens<N / 2, MASK / 2>(b, lane);
+    }
+}
+
+// Token held by lane L after wave_reduce_tokens<N>: the halving step with
+// mask m sent the upper half of the remaining tokens to lanes with bit m set.
+template <int N>
 __device__ __forceinline__ int tok_of_lane(int lane) {
-    return ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+    int t = 0;
+#pragma unroll
+    for (int n = N, m = kWave / 2; n > 1; n >>= 1, m >>= 1) t += (lane & m) ? n / 2 : 0;
+    return t;
 }
 
-__global__ __launch_bounds__(kLogitWaves * kWave) void exact_logits_kernel(
+template <int TOK>
+__global__ __launch_bounds__(kLogitThreads) void exact_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int E,
     float* __restrict__ logits) {
-    __shared__ uint4 xs[kLogitTok * kLogitChunk / 8];
+    constexpr int kStage = TOK * kLogitRowVecs / kLogitThreads;  // tile vectors per thread
+    static_assert(TOK * kLogitRowVecs % kLogitThreads == 0, "tile must split evenly");
+    __shared__ uint4 xs[TOK * kLogitRowVecs];
     const int lane = threadIdx.x % kWave;
     const int e = blockIdx.x * kLogitWaves + threadIdx.x / kWave;
-    const int t0 = blockIdx.y * kLogitTok;
-    double acc[kLogitTok];
+    const int t0 = blockIdx.y * TOK;
+    double acc[TOK];
 #pragma unroll
-    for (int t = 0; t < kLogitTok; ++t) acc[t] = 0.0;
+    for (int t = 0; t < TOK; ++t) acc[t] = 0.0;
 
     for (int h0 = 0; h0 < H; h0 += kLogitChunk) {
         const int len = min(kLogitChunk, H - h0);  // multiple of 8
@@ -89,14 +96,18 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void exact_logits_kernel(
                         ? *reinterpret_cast<const uint4*>(wr + (size_t)e * H + h0 + c * 8)
                         : make_uint4(0, 0, 0, 0);
         }
-        __syncthreads();
-        for (int v = threadIdx.x; v < kLogitTok * (kLogitChunk / 8); v += blockDim.x) {
-            const int t = v / (kLogitChunk / 8), c = v % (kLogitChunk / 8);
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (c < vecs && t0 + t < T)
-                val = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * H + h0 + c * 8);
-            xs[v] = val;
+        uint4 st[kStage];
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int v = threadIdx.x + i * kLogitThreads;
+            const int t = v / kLogitRowVecs, c = v % kLogitRowVecs;
+            st[i] = (c < vecs && t0 + t < T)
+                        ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * H + h0 + c * 8)
+                        : make_uint4(0, 0, 0, 0);
         }
+        __syncthreads();  // the previous chunk's tile has been read
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) xs[threadIdx.x + i * kLogitThreads] = st[i];
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kLogitVecs; ++j) {
@@ -110,8 +121,8 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void exact_logits_kernel(
                 wd[2 * i + 1] = (double)bf16_to_f32(ww[i] >> 16);
             }
 #pragma unroll
-            for (int t = 0; t < kLogitTok; ++t) {
-                const uint4 x4 = xs[t * (kLogitChunk / 8) + c];
+            for (int t = 0; t < TOK; ++t) {
+                const uint4 x4 = xs[t * kLogitRowVecs + c];
                 const uint32_t xx[4] = {x4.x, x4.y, x4.z, x4.w};
                 double a = acc[t];
 #pragma unroll
@@ -123,24 +134,33 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void exact_logits_kernel(
             }
         }
     }
-    const double tot = wave_reduce16(acc, lane);
-    const int t = t0 + tok_of_lane(lane);
-    if (e < E && (lane & 3) == 0 && t < T) logits[(size_t)t * E + e] = (float)tot;
+    const double tot = wave_reduce_tokens<TOK>(acc, lane);
+    const int t = t0 + tok_of_lane<TOK>(lane);
+    if (e < E && lane % (kWave / TOK) == 0 && t < T) logits[(size_t)t * E + e] = (float)tot;
 }
 
 hipError_t launch_exact_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
                                float* logits, hipStream_t s) {
-    dim3 grid((E + kLogitWaves - 1) / kLogitWaves, (T + kLogitTok - 1) / kLogitTok);
-    hipLaunchKernelGGL(exact_logits_kernel, grid, dim3(kLogitWaves * kWave), 0, s, x, wr, T, H, E,
-                       logits);
+    const unsigned ex = (E + kLogitWaves - 1) / kLogitWaves;
+    // 8-token tiles while 16-token tiles would leave the grid under two
+    // workgroups per compute unit
+    if ((long)ex * ((T + 15) / 16) < 512)
+        hipLaunchKernelGGL(exact_logits_kernel<8>, dim3(ex, (T + 7) / 8), dim3(kLogitThreads), 0, s, x, wr,
+                           T, H, E, logits);
+    else
+        hipLaunchKernelGGL(exact_logits_kernel<16>, dim3(ex, (T + 15) / 16), dim3(kLogitThreads), 0, s, x,
+                           wr, T, H, E, logits);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Top-k.  One wave per token.  Each expert becomes a 64-bit key whose order
-// is (logit descending, index ascending): high word = order-preserving
-// encoding of the fp32 logit (-0 canonicalised to +0), low word = ~index.
-// k+extra rounds of a wave-wide max pick the winners in rank order.
+// Top-k.  One wave per token.  Expert e = v * 64 + lane sits in key[v] of its
+// lane as the order-preserving 32-bit encoding of its fp32 logit (-0
+// canonicalised to +0; 0 marks "none", real keys are at least 1).  Each of
+// the k+extra rounds takes the wave-wide maximum key (DPP inside rows of 16
+// lanes, then scalar reads of the four rows); among experts holding that key
+// the lowest index wins: ballots in expert order, first hit.  So the ranks
+// order (logit descending, index ascending).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t float_order_key(float l) {
     uint32_t u = __float_as_uint(l + 0.0f);  // -0 + 0 = +0
@@ -151,19 +171,38 @@ __device__ __forceinline__ float float_from_order_key(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        uint64_t o = __shfl_xor(v, m, kWave);
-        v = o > v ? o : v;
-    }
-    return v;
-}
+// Key of a present expert: never 0 (only a NaN with every bit set encodes to 0).
+__device__ __forceinline__ uint32_t expert_key(float l) { return max(float_order_key(l), 1u); }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
     return v;
+}
+
+// K rounds over key[VPL] (consumed); lane r receives rank r's expert and
+// logit.  Every lane of the wave must be active.
+template <int VPL>
+__device__ __forceinline__ void wave_topk(uint32_t (&key)[VPL], int K, int lane, int& my_e, float& my_l) {
+    for (int r = 0; r < K; ++r) {
+        uint32_t best = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) best = max(best, key[v]);
+        best = wave_max_u32(best);
+        int e = -1;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const uint64_t hit = __ballot(key[v] == best);
+            if (e < 0 && hit) e = v * kWave + __ffsll((long long)hit) - 1;
+        }
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            if (v * kWave + lane == e) key[v] = 0;
+        if (lane == r) {
+            my_e = e;
+            my_l = float_from_order_key(best);
+        }
+    }
 }
 
 template <int VPL>
@@ -174,30 +213,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= T) return;  // whole wave leaves together; no block barrier below
-    uint64_t key[VPL];
+    // unconditional loads (clamped index), so that all of them are in flight at once
+    float l[VPL];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-        const int e = v * kWave + lane;
-        key[v] = 0;
-        if (e < E)
-            key[v] = ((uint64_t)float_order_key(logits[(size_t)t * E + e]) << 32) | (uint32_t)(~e);
-    }
+    for (int v = 0; v < VPL; ++v) l[v] = logits[(size_t)t * E + min(v * kWave + lane, E - 1)];
+    uint32_t key[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) key[v] = v * kWave + lane < E ? expert_key(l[v]) : 0u;
     int my_e = 0;
     float my_l = 0.0f;
-    for (int r = 0; r < K; ++r) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(~(uint32_t)best);
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            if (v * kWave + lane == e) key[v] = 0;
-        if (lane == r) {
-            my_e = e;
-            my_l = float_from_order_key((uint32_t)(best >> 32));
-        }
-    }
+    wave_topk<VPL>(key, K, lane, my_e, my_l);
     if (lane < K) {
         idx[(size_t)t * K + lane] = my_e;
         if (topk_logit) topk_logit[(size_t)t * K + lane] = my_l;
@@ -285,7 +310,9 @@ __device__ __forceinline__ float wave_exact_logit(const uint16_t* __restrict__ x
 // Exact fp32 logits of four (token, expert) pairs at once: lane group
 // g = lane / 16 takes expert e_g (e_g < 0: none) and 16 lanes split the
 // hidden dimension; fp64 FMAs, a 16-lane tree, one rounding.  Every lane
-// returns its group's logit.
+// returns its group's logit.  Loads go out kQuadBatch vectors at a time
+// before any of them is used.
+constexpr int kQuadBatch = 5;
 __device__ __forceinline__ float quad_exact_logit(const uint16_t* __restrict__ xr,
                                                   const uint16_t* __restrict__ wr, int H, int e_g) {
     const int l16 = threadIdx.x % 16;
@@ -293,15 +320,27 @@ __device__ __forceinline__ float quad_exact_logit(const uint16_t* __restrict__ x
     if (e_g >= 0) {
         const uint4* wv = reinterpret_cast<const uint4*>(wr + (size_t)e_g * H);
         const uint4* xv = reinterpret_cast<const uint4*>(xr);
-        for (int c = l16; c < H / 8; c += 16) {
-            const uint4 x4 = xv[c];
-            const uint4 w4 = wv[c];
-            const uint32_t xx[4] = {x4.x, x4.y, x4.z, x4.w};
-            const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+        const int nvec = H / 8;
+        for (int c0 = l16; c0 < nvec; c0 += 16 * kQuadBatch) {
+            uint4 x4[kQuadBatch], w4[kQuadBatch];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc = fma((double)bf16_to_f32(xx[i] & 0xFFFFu), (double)bf16_to_f32(ww[i] & 0xFFFFu), acc);
-                acc = fma((double)bf16_to_f32(xx[i] >> 16), (double)bf16_to_f32(ww[i] >> 16), acc);
+            for (int u = 0; u < kQuadBatch; ++u) {
+                const int c = c0 + 16 * u;
+                if (c < nvec) {
+                    x4[u] = xv[c];
+                    w4[u] = wv[c];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kQuadBatch; ++u) {
+                if (c0 + 16 * u >= nvec) break;
+                const uint32_t xx[4] = {x4[u].x, x4[u].y, x4[u].z, x4[u].w};
+                const uint32_t ww[4] = {w4[u].x, w4[u].y, w4[u].z, w4[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc = fma((double)bf16_to_f32(xx[i] & 0xFFFFu), (double)bf16_to_f32(ww[i] & 0xFFFFu), acc);
+                    acc = fma((double)bf16_to_f32(xx[i] >> 16), (double)bf16_to_f32(ww[i] >> 16), acc);
+                }
             }
         }
     }
@@ -455,32 +494,18 @@ __global__ __launch_bounds__(256) void route_refine_kernel(
     }
     // fallback: every logit of this token exactly (kept in the owning lane's
     // registers), then the plain top-K
-    uint64_t keys[VPL];
+    uint32_t keys[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) keys[v] = 0;
     for (int e = 0; e < E; ++e) {
-        const float l = wave_exact_logit(xr, wr + (size_t)e * H, H);
-        const uint64_t kk = ((uint64_t)float_order_key(l) << 32) | (uint32_t)(~e);
+        const uint32_t kk = expert_key(wave_exact_logit(xr, wr + (size_t)e * H, H));
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
             if (v * kWave + lane == e) keys[v] = kk;
     }
     int my_e = 0;
     float my_l = 0.0f;
-    for (int r = 0; r < K; ++r) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) best = keys[v] > best ? keys[v] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(~(uint32_t)best);
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            if (v * kWave + lane == e) keys[v] = 0;
-        if (lane == r) {
-            my_e = e;
-            my_l = float_from_order_key((uint32_t)(best >> 32));
-        }
-    }
+    wave_topk<VPL>(keys, K, lane, my_e, my_l);
     if (lane < K) {
         idx[(size_t)t * K + lane] = my_e;
         if (topk_logit) topk_logit[(size_t)t * K + lane] = my_l;
