@@ -2,7 +2,7 @@
 """Throughput of the MoE feed-forward layer on one MI355X.
 
 A step is one pass of the whole layer over one batch of seeded synthetic
-input resident in HBM: route -> permute -> routed experts -> combine, with the
+input resident in HBM: route and permute (one call) -> routed experts -> combine, with the
 shared expert on a second stream beside them (for the Refill-RMS workload: route with the 11th expert -> permute ->
 routed experts (fp32 rows) -> refill score -> keep-set).  Steps cycle through
 several independently generated weight copies so that the weights do not stay
@@ -123,8 +123,7 @@ def main():
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             s = moe.grouped_ffn(x, 1, d["shared"], ws=side_ws)
-        idx, tl, gate, _ = moe.route(x, d["router"], w.k, ws=ws)
-        off, sp, p2r = moe.permute(idx, w.E, ws=ws)
+        idx, tl, gate, off, sp, p2r = moe.route_permute(x, d["router"], w.k, ws=ws)
         if ev: ev[0].record(stream)
         rows = moe.grouped_ffn(x, w.k, d["experts"], off, sp, ws=ws)
         if ev: ev[1].record(stream)
@@ -205,7 +204,7 @@ def main():
 
 
 def graph_steps(moe, w, sets, ws, side, side_ws, stream, eager_step):
-    """Steps replayed from HIP graphs, one set per weight copy: [route, permute],
+    """Steps replayed from HIP graphs, one set per weight copy: [route and permute],
     [routed experts], [combine] captured separately so that the HIP events
     around the routed call are recorded between replays.  The shared expert
     runs on the side stream as in the eager step.  Capture happens after an
@@ -222,8 +221,7 @@ def graph_steps(moe, w, sets, ws, side, side_ws, stream, eager_step):
         s_buf = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=x.device)
         g1, g2, g3 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(g1):
-            idx, tl, gate, _ = moe.route(x, d["router"], w.k, ws=ws)
-            off, sp, p2r = moe.permute(idx, w.E, ws=ws)
+            idx, tl, gate, off, sp, p2r = moe.route_permute(x, d["router"], w.k, ws=ws)
         with torch.cuda.graph(g2):
             rows = moe.grouped_ffn(x, w.k, d["experts"], off, sp, ws=ws)
         with torch.cuda.graph(g3):

@@ -118,7 +118,8 @@ typedef struct {
 
 /* Operation ids for moe_workspace_bytes(). */
 enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_FFN = 2, MOE_OP_REFILL_SCORE = 3,
-       MOE_OP_GROUPED_FFN_NVFP4 = 4 /* grouped FFN of an NVFP4 bank (adds the quantised input) */ };
+       MOE_OP_GROUPED_FFN_NVFP4 = 4, /* grouped FFN of an NVFP4 bank (adds the quantised input) */
+       MOE_OP_ROUTE_PERMUTE = 5 };
 
 /*
  * Router: logits, softmax, top-k, renormalised gates.
@@ -151,6 +152,20 @@ moe_status moe_route(const uint16_t *x, const uint16_t *w_router, int32_t T, int
 moe_status moe_permute(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E,
                        int32_t *expert_offsets, int32_t *sorted_pair, int32_t *pair_to_row,
                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_route (extra = 0) followed by moe_permute of its topk_idx, in one call;
+ * the outputs and the requirements are those of the two calls (topk_logit
+ * and topk_gate nullable).  For decode-sized batches (T < 64, T * k <= 4096)
+ * the selection and the permutation share one single-workgroup kernel after
+ * the logits, saving a launch on the layer's critical path; otherwise the
+ * two calls run as they are.  Workspace: moe_workspace_bytes(
+ * MOE_OP_ROUTE_PERMUTE, T, k, E, H, 0).
+ */
+moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, int32_t T, int32_t H,
+                             int32_t E, int32_t k, int32_t *topk_idx, float *topk_logit,
+                             float *topk_gate, int32_t *expert_offsets, int32_t *sorted_pair,
+                             int32_t *pair_to_row, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Grouped SwiGLU experts: for every row r with pair p = sorted_pair[r],

@@ -4,12 +4,12 @@ The compute path is libmoe.so (hand-written HIP kernels behind a C ABI,
 include/moe.h); this package is its thin Python binding.
 """
 from ._lib import (EXPORTS, LIB_PATH, OP_GROUPED_FFN, OP_GROUPED_FFN_NVFP4, OP_PERMUTE, OP_REFILL_SCORE,
-                   OP_ROUTE, OUT_BF16, OUT_F32, MoeError, Workspace, combine, grouped_ffn, lib, moe_layer,
-                   nvfp4_quantize, permute, prune_slice, refill_finalize, refill_score, route,
-                   router_norm_keep, workspace_bytes)
+                   OP_ROUTE, OP_ROUTE_PERMUTE, OUT_BF16, OUT_F32, MoeError, Workspace, combine, grouped_ffn, lib,
+                   moe_layer, nvfp4_quantize, permute, prune_slice, refill_finalize, refill_score, route,
+                   route_permute, router_norm_keep, workspace_bytes)
 from .calibration import RefillCalibration
 
 __all__ = ["EXPORTS", "LIB_PATH", "OP_GROUPED_FFN", "OP_GROUPED_FFN_NVFP4", "OP_PERMUTE", "OP_REFILL_SCORE",
-           "OP_ROUTE", "OUT_BF16", "OUT_F32", "MoeError", "Workspace", "combine", "grouped_ffn", "lib",
+           "OP_ROUTE", "OP_ROUTE_PERMUTE", "OUT_BF16", "OUT_F32", "MoeError", "Workspace", "combine", "grouped_ffn", "lib",
            "moe_layer", "nvfp4_quantize", "permute", "prune_slice", "refill_finalize", "refill_score",
-           "route", "router_norm_keep", "workspace_bytes", "RefillCalibration"]
+           "route", "route_permute", "router_norm_keep", "workspace_bytes", "RefillCalibration"]

@@ -27,11 +27,11 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-OP_ROUTE, OP_PERMUTE, OP_GROUPED_FFN, OP_REFILL_SCORE, OP_GROUPED_FFN_NVFP4 = 0, 1, 2, 3, 4
+OP_ROUTE, OP_PERMUTE, OP_GROUPED_FFN, OP_REFILL_SCORE, OP_GROUPED_FFN_NVFP4, OP_ROUTE_PERMUTE = 0, 1, 2, 3, 4, 5
 W_BF16, W_AWQ, W_FP8, W_NVFP4 = 0, 1, 2, 3
 OUT_BF16, OUT_F32 = 0, 1
 
-EXPORTS = ["moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_refill_score",
+EXPORTS = ["moe_route", "moe_permute", "moe_route_permute", "moe_grouped_ffn", "moe_combine", "moe_refill_score",
            "moe_refill_finalize", "moe_prune_slice", "moe_router_norm_keep",
            "moe_nvfp4_quantize", "moe_workspace_bytes", "moe_status_string", "moe_last_hip_error"]
 
@@ -70,6 +70,7 @@ def lib():
     sig = {
         "moe_route": [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P],
         "moe_permute": [P, i32, i32, i32, P, P, P, P, sz, P],
+        "moe_route_permute": [P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P],
         "moe_grouped_ffn": [P, i32, i32, ctypes.POINTER(_Experts), P, P, i32, P, P, sz, P],
         "moe_combine": [P, i32, P, P, i32, i32, i32, P, P, P, P],
         "moe_refill_score": [P, P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, sz, P],
@@ -209,6 +210,25 @@ def permute(topk_idx, E: int, ws=None):
     return off, sp, p2r
 
 
+def route_permute(x, w_router, k: int, ws=None):
+    """route (extra = 0) then permute in one call.  Returns (topk_idx, topk_logit, gate,
+    expert_offsets, sorted_pair, pair_to_row), as the two calls return them."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tl = torch.empty((T, k), dtype=torch.float32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(T * k, dtype=torch.int32, device=dev)
+    p2r = torch.empty(T * k, dtype=torch.int32, device=dev)
+    buf, n = _ws(ws, dev).get(workspace_bytes(OP_ROUTE_PERMUTE, T, k, E, H))
+    _check("moe_route_permute", lib().moe_route_permute(_ptr(x), _ptr(w_router), T, H, E, k, _ptr(idx), _ptr(tl),
+                                                        _ptr(gate), _ptr(off), _ptr(sp), _ptr(p2r), _ptr(buf),
+                                                        n, _stream()))
+    return idx, tl, gate, off, sp, p2r
+
+
 def grouped_ffn(x, k: int, bank: dict, offsets=None, sorted_pair=None, out_dtype=OUT_BF16,
                 ws=None, rows=None):
     """rows [T*k, H]: expert outputs in grouped order (identity order when offsets is None)."""
@@ -314,7 +334,6 @@ def moe_layer(x, w_router, k: int, bank: dict, shared: dict | None = None, share
     With `shared_stream` (a torch.cuda.Stream) the shared expert, which needs
     only x, runs on that stream beside routing and the routed experts, with its
     own workspace `shared_ws`; the combine waits for it."""
-    E = w_router.shape[0]
     main = torch.cuda.current_stream(x.device)
     s = None
     if shared is not None and shared_stream is not None:
@@ -325,8 +344,7 @@ def moe_layer(x, w_router, k: int, bank: dict, shared: dict | None = None, share
         with torch.cuda.stream(shared_stream):
             s = grouped_ffn(x, 1, shared, ws=shared_ws)
         x.record_stream(shared_stream)
-    idx, tl, gate, _ = route(x, w_router, k, ws=ws)
-    off, sp, p2r = permute(idx, E, ws=ws)
+    idx, tl, gate, off, sp, p2r = route_permute(x, w_router, k, ws=ws)
     rows = grouped_ffn(x, k, bank, off, sp, ws=ws)
     if shared is not None and shared_stream is None:
         s = grouped_ffn(x, 1, shared, ws=ws)

@@ -84,6 +84,13 @@ bool bank_ok(const moe_experts* ex, moe_status* st) {
     return true;
 }
 
+// Workspace of moe_route_permute: the two calls run one after the other on
+// one stream, so they share it.
+size_t route_permute_ws(int T, int k, int E, int H) {
+    const size_t a = route_ws(T, E, H), b = moe::permute_ws_bytes(T, k, E);
+    return a > b ? a : b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,6 +135,32 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
     if (need && !ws) return MOE_ERR_NULL;
     return hip_status(moe::launch_permute(topk_idx, T, k, E, expert_offsets, sorted_pair,
                                           pair_to_row, ws, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_route_permute(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H, int32_t E,
+                             int32_t k, int32_t* topk_idx, float* topk_logit, float* topk_gate,
+                             int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_to_row, void* ws,
+                             size_t ws_bytes, void* stream) {
+    if (T < 0 || H < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_SHAPE;
+    if (E > kMaxE || H % 8 || k > 64 || (int64_t)T * k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !topk_idx || !expert_offsets || !sorted_pair || !pair_to_row) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_UNSUPPORTED;
+    if (ws_bytes < route_permute_ws(T, k, E, H)) return MOE_ERR_WORKSPACE;
+    if (!ws) return MOE_ERR_NULL;
+    if (!aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!route_filtered(T, H, E) && moe::topk_permute_fits(T, k, E)) {
+        float* lbuf = static_cast<float*>(ws);
+        moe_status st = hip_status(moe::launch_exact_logits(x, w_router, T, H, E, lbuf, s));
+        if (st != MOE_OK) return st;
+        return hip_status(moe::launch_topk_permute(lbuf, T, E, k, topk_idx, topk_logit, topk_gate,
+                                                   expert_offsets, sorted_pair, pair_to_row, s));
+    }
+    moe_status st = moe_route(x, w_router, T, H, E, k, 0, topk_idx, topk_logit, topk_gate, nullptr, ws,
+                              ws_bytes, stream);
+    if (st != MOE_OK) return st;
+    return moe_permute(topk_idx, T, k, E, expert_offsets, sorted_pair, pair_to_row, ws, ws_bytes, stream);
 }
 
 moe_status moe_grouped_ffn(const uint16_t* x, int32_t T, int32_t k, const moe_experts* ex,
@@ -303,6 +336,7 @@ size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t k, int32_t E, int32_t 
         case MOE_OP_PERMUTE: return moe::permute_ws_bytes(T, k, E);
         case MOE_OP_GROUPED_FFN: return moe::ffn_ws_bytes(T, k, E, H, F, false);
         case MOE_OP_GROUPED_FFN_NVFP4: return moe::ffn_ws_bytes(T, k, E, H, F, true);
+        case MOE_OP_ROUTE_PERMUTE: return route_permute_ws(T, k, E, H);
         case MOE_OP_REFILL_SCORE: return moe::refill_ws_bytes(T, k);
         default: return 0;
     }

@@ -16,6 +16,11 @@ hipError_t launch_exact_logits(const uint16_t* x, const uint16_t* wr, int T, int
                                float* logits, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int extra, int32_t* idx,
                        float* topk_logit, float* gate, hipStream_t s);
+// top-k followed by the permutation, one workgroup (when topk_permute_fits)
+bool topk_permute_fits(int T, int k, int E);
+hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* idx, float* topk_logit,
+                               float* gate, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_to_row,
+                               hipStream_t s);
 size_t route_filter_ws_bytes(int T, int E, int H);
 hipError_t launch_route_filter(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
                                int extra, int32_t* idx, float* topk_logit, float* gate, void* ws,

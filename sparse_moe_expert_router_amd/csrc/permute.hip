@@ -11,54 +11,11 @@
 // Chunks are processed in order by one wave, so the order is deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace moe {
 
 constexpr int kPermChunk = 512;      // pairs per block in the multi-block path
-constexpr int kSmallPairs = 4096;    // single-workgroup path up to this many pairs
-
-// Expert ids outside [0, E) are clamped so that every row stays inside the buffers.
-__device__ __forceinline__ int clamp_expert(int e, int E) { return min(max(e, 0), E - 1); }
-
-__device__ __forceinline__ int bits_for(int E) {
-    int b = 0;
-    while ((1 << b) < E) ++b;
-    return b;
-}
-
-// One wave scatters pairs [p0, p1) in order; cursor[e] (LDS) is the next row
-// of e.  ids: the pairs' expert ids, in global memory (clamped here) or, with
-// kClamped, already clamped (the single-workgroup path keeps them in LDS).
-template <bool kClamped>
-__device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ ids, int p0, int p1, int E, int nbits,
-                             int* cursor, int32_t* __restrict__ sorted_pair,
-                             int32_t* __restrict__ pair_to_row) {
-    const int lane = threadIdx.x % kWave;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    for (int c = p0; c < p1; c += kWave) {
-        const int p = c + lane;
-        const bool active = p < p1;
-        const int e = !active ? 0 : kClamped ? ids[p] : clamp_expert(ids[p], E);
-        uint64_t peers = __ballot(active);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t m = __ballot(active && bit);
-            peers &= bit ? m : ~m;
-        }
-        const int rank = __popcll(peers & below);
-        const int cnt = __popcll(peers);
-        const int base = active ? cursor[e] : 0;
-        __builtin_amdgcn_wave_barrier();
-        if (active) {
-            const int row = base + rank;
-            sorted_pair[row] = p;
-            pair_to_row[p] = row;
-        }
-        if (active && rank == 0) cursor[e] = base + cnt;
-        __builtin_amdgcn_wave_barrier();
-    }
-}
-
 // Single workgroup: histogram (the clamped expert ids stay in LDS for the
 // scatter), exclusive scan (a wave scan per 64 threads, then the waves'
 // totals), scatter by wave 0.  block = 256, P <= kSmallPairs.

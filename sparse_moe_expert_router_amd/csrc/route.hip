@@ -10,6 +10,7 @@
 #include "common.h"
 #include "ffn_internal.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace moe {
 
@@ -162,49 +163,6 @@ hipError_t launch_exact_logits(const uint16_t* x, const uint16_t* wr, int T, int
 // the lowest index wins: ballots in expert order, first hit.  So the ranks
 // order (logit descending, index ascending).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t float_order_key(float l) {
-    uint32_t u = __float_as_uint(l + 0.0f);  // -0 + 0 = +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float float_from_order_key(uint32_t o) {
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
-// Key of a present expert: never 0 (only a NaN with every bit set encodes to 0).
-__device__ __forceinline__ uint32_t expert_key(float l) { return max(float_order_key(l), 1u); }
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
-    return v;
-}
-
-// K rounds over key[VPL] (consumed); lane r receives rank r's expert and
-// logit.  Every lane of the wave must be active.
-template <int VPL>
-__device__ __forceinline__ void wave_topk(uint32_t (&key)[VPL], int K, int lane, int& my_e, float& my_l) {
-    for (int r = 0; r < K; ++r) {
-        uint32_t best = 0;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) best = max(best, key[v]);
-        best = wave_max_u32(best);
-        int e = -1;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-            const uint64_t hit = __ballot(key[v] == best);
-            if (e < 0 && hit) e = v * kWave + __ffsll((long long)hit) - 1;
-        }
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            if (v * kWave + lane == e) key[v] = 0;
-        if (lane == r) {
-            my_e = e;
-            my_l = float_from_order_key(best);
-        }
-    }
-}
-
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                   int K, int k, int32_t* __restrict__ idx,
@@ -213,26 +171,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= T) return;  // whole wave leaves together; no block barrier below
-    // unconditional loads (clamped index), so that all of them are in flight at once
-    float l[VPL];
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) l[v] = logits[(size_t)t * E + min(v * kWave + lane, E - 1)];
-    uint32_t key[VPL];
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) key[v] = v * kWave + lane < E ? expert_key(l[v]) : 0u;
-    int my_e = 0;
-    float my_l = 0.0f;
-    wave_topk<VPL>(key, K, lane, my_e, my_l);
-    if (lane < K) {
-        idx[(size_t)t * K + lane] = my_e;
-        if (topk_logit) topk_logit[(size_t)t * K + lane] = my_l;
-    }
-    if (gate) {
-        const float l0 = __shfl(my_l, 0, kWave);
-        const float p = lane < k ? expf(my_l - l0) : 0.0f;
-        const float z = wave_sum_f32(p);
-        if (lane < k) gate[(size_t)t * k + lane] = p / z;
-    }
+    select_token<VPL>(logits, (size_t)t, E, K, k, lane, idx, topk_logit, gate);
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int extra, int32_t* idx,
@@ -250,6 +189,73 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int extra, int3
         hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, T, E, K, k, idx, topk_logit, gate);
     else
         hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, T, E, K, k, idx, topk_logit, gate);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-k and permutation in one workgroup, for decode-sized batches
+// (T * k <= kSmallPairs, E <= 1024): 16 waves select the tokens' experts as
+// topk_kernel does, keeping the ids in LDS and counting them per expert;
+// then an exclusive scan (one expert per thread) gives the offsets, and wave
+// 0 scatters the pairs in pair order exactly as the permutation kernels do.
+// The results equal those of launch_topk followed by launch_permute.
+// ---------------------------------------------------------------------------
+constexpr int kSelWaves = 16;
+
+template <int VPL>
+__global__ __launch_bounds__(kSelWaves * kWave) void topk_permute_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
+    float* __restrict__ topk_logit, float* __restrict__ gate, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_to_row) {
+    __shared__ int cnt[1024];
+    __shared__ int ids[kSmallPairs];
+    __shared__ int wtot[kSelWaves];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    for (int t = wave; t < T; t += kSelWaves) {
+        const int e = select_token<VPL>(logits, (size_t)t, E, k, k, lane, idx, topk_logit, gate);
+        if (lane < k) {
+            ids[t * k + lane] = e;
+            atomicAdd(&cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    const int c = tid < E ? cnt[tid] : 0;
+    int inc = c;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const int o = __shfl_up(inc, m, kWave);
+        if (lane >= m) inc += o;
+    }
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    int run = inc - c;
+    for (int w = 0; w < wave; ++w) run += wtot[w];
+    if (tid < E) {
+        cnt[tid] = run;  // becomes the cursor
+        offsets[tid] = run;
+    }
+    if (tid == 0) offsets[E] = T * k;
+    __syncthreads();
+    if (wave == 0) wave_scatter<true>(ids, 0, T * k, E, bits_for(E), cnt, sorted_pair, pair_to_row);
+}
+
+bool topk_permute_fits(int T, int k, int E) { return (long)T * k <= kSmallPairs && E <= 1024; }
+
+hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* idx, float* topk_logit,
+                               float* gate, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_to_row,
+                               hipStream_t s) {
+    const int vpl = (E + kWave - 1) / kWave;
+#define MOE_SEL(V)                                                                                        \
+    hipLaunchKernelGGL(topk_permute_kernel<V>, dim3(1), dim3(kSelWaves * kWave), 0, s, logits, T, E, k, idx, \
+                       topk_logit, gate, offsets, sorted_pair, pair_to_row)
+    if (vpl <= 1) MOE_SEL(1);
+    else if (vpl <= 2) MOE_SEL(2);
+    else if (vpl <= 4) MOE_SEL(4);
+    else if (vpl <= 8) MOE_SEL(8);
+    else MOE_SEL(16);
+#undef MOE_SEL
     return hipGetLastError();
 }
 

@@ -51,6 +51,26 @@ def test_route_validation():
     assert L.moe_route(fake, fake, 4, 64, 8, 2, 0, fake, None, fake, None, fake, 16, None) == WS
 
 
+def test_route_permute_validation():
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    args = lambda T, H, E, k, x=fake, off=fake, ws=fake, n=1 << 30: (
+        x, fake, T, H, E, k, fake, None, fake, off, fake, fake, ws, n, None)
+    assert L.moe_route_permute(*args(4, 64, 8, 9)) == SHAPE        # k > E
+    assert L.moe_route_permute(*args(-1, 64, 8, 2)) == SHAPE
+    assert L.moe_route_permute(*args(4, 64, 2048, 2)) == UNSUP     # E > 1024
+    assert L.moe_route_permute(*args(4, 60, 8, 2)) == UNSUP        # H % 8
+    assert L.moe_route_permute(*args(4, 64, 128, 65)) == UNSUP     # k > 64
+    assert L.moe_route_permute(*args(0, 64, 8, 2)) == OK           # T = 0: no-op
+    assert L.moe_route_permute(*args(4, 64, 8, 2, x=None)) == NULL
+    assert L.moe_route_permute(*args(4, 64, 8, 2, off=None)) == NULL
+    need = L.moe_workspace_bytes(5, 4, 2, 8, 64, 0)
+    assert need >= L.moe_workspace_bytes(0, 4, 2, 8, 64, 0)
+    assert need >= L.moe_workspace_bytes(1, 4, 2, 8, 64, 0)
+    assert L.moe_route_permute(*args(4, 64, 8, 2, n=need - 1)) == WS
+    assert L.moe_route_permute(*args(4, 64, 8, 2, ws=None, n=need)) == NULL
+
+
 def test_permute_and_combine_validation():
     L = moe.lib()
     fake = ctypes.c_void_p(256)

@@ -99,6 +99,37 @@ def test_route_ties_take_lowest_index():
     np.testing.assert_allclose(g0.cpu().numpy(), 0.25, rtol=1e-6)
 
 
+@pytest.mark.parametrize("T,H,E,k", [(16, 2560, 512, 10), (1, 2560, 512, 10), (63, 512, 1024, 64),
+                                     (40, 256, 65, 64), (5, 64, 1, 1), (300, 512, 100, 7),
+                                     (70, 128, 1024, 10), (64, 256, 256, 8), (600, 512, 512, 10)])
+def test_route_permute_matches_oracle(T, H, E, k):
+    """One call for route + permute: the single-workgroup selection and
+    permutation for small batches, the two separate paths otherwise.  The
+    results equal the oracle's ranking and permutation bit for bit, and those
+    of the two separate calls."""
+    moe = require_gpu()
+    w = _wl(T, H, E)
+    x = workloads.activations(w, seed=11, device="cuda")
+    wr = workloads.router(w, seed=11, device="cuda")
+    if E > 20:
+        wr[E - 1] = wr[3]  # a tie between experts 3 and E - 1
+    idx, tl, gate, off, sp, p2r = moe.route_permute(x, wr, k)
+    idx2, tl2, gate2, _ = moe.route(x, wr, k)
+    off2, sp2, p2r2 = moe.permute(idx2, E)
+    torch.cuda.synchronize()
+    ref_l, _ = O.router_logits(bits(x), bits(wr))
+    ref_idx = O.rank(ref_l, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(tl.cpu().numpy(), np.take_along_axis(ref_l, ref_idx, 1))
+    np.testing.assert_allclose(gate.cpu().numpy(), O.gates(ref_l, ref_idx, k), rtol=1e-5, atol=1e-7)
+    ro, rs, rp = O.permute(ref_idx.astype(np.int32), E)
+    np.testing.assert_array_equal(off.cpu().numpy(), ro)
+    np.testing.assert_array_equal(sp.cpu().numpy(), rs)
+    np.testing.assert_array_equal(p2r.cpu().numpy(), rp)
+    for a, b in ((idx, idx2), (tl, tl2), (gate, gate2), (off, off2), (sp, sp2), (p2r, p2r2)):
+        assert torch.equal(a, b)
+
+
 # ----------------------------------------------------------------------------- permute
 
 @pytest.mark.parametrize("T,k,E,skew", [(16, 10, 512, False), (64, 2, 16, False), (4096, 10, 512, False),
