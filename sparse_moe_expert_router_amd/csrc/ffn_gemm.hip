@@ -45,10 +45,14 @@ namespace moe {
 constexpr int kBN = 256, kBK = 32;  // B-columns per workgroup, K step
 
 // LDS tiles are [row][32] bf16 (64-byte rows, no padding).  The 16-byte chunk
-// c of row r is stored at chunk c ^ ((r >> 2) & 3): sixteen lanes that read
-// 16 consecutive rows at one chunk, or write four rows x four chunks, then
-// touch 256 distinct bytes (all 64 banks once).
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3); }
+// c of row r is stored at chunk c ^ ((r >> 1) & 3): any eight lanes that read
+// eight consecutive rows at one chunk (an MFMA fragment read) then touch eight
+// distinct 16-byte bank groups, 128 contiguous bank bytes, and so do eight
+// lanes that write two rows x four chunks.  (With c ^ ((r >> 2) & 3) the
+// fragment reads were two-way conflicted: rocprofv3's SQ_LDS_BANK_CONFLICT
+// was about equal to SQ_ACTIVE_INST_LDS and drops about 70-fold with this
+// layout.)
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 32 + ((chunk ^ ((row >> 1) & 3)) << 3); }
 
 // AWQ B tiles store B-column c at LDS row c ^ ((c >> 3) & 3): the 8-byte stores
 // of four adjacent packed words (columns 8 apart) then land in four different
@@ -56,10 +60,6 @@ __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 32 + (
 constexpr int kXcd = 8;
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
-
-// A fragments read one slice before their first MFMA instead of all at the
-// start of a K step (fewer live registers).
-constexpr bool kLazyA = true;
 
 // Orders a wave's own LDS accesses (writes by some lanes, then reads by
 // others): LDS instructions of one wave complete in issue order, so only the
@@ -276,61 +276,58 @@ __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APE
 }
 
 // MFMA operand fragments of one K step from an LDS stage.
+// One MFMA operand fragment from an LDS stage: B fragment nj (16 B-columns of
+// the wave's share; gate/up: the first TN/2 are gate columns, the rest the
+// matching up columns) and A fragment mi (16 rows of the wave's share).
 template <int MODE, int WF, int BM>
-__device__ __forceinline__ void read_frags(const uint16_t* As, const uint16_t* Bs,
-                                           bf16x8_t (&af)[GemmShape<BM>::TM],
-                                           bf16x8_t (&bfr)[GemmShape<BM>::TN], int wm, int wn,
-                                           int lane) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
-    (void)FP8;
-    (void)NV4;
+__device__ __forceinline__ bf16x8_t b_frag(const uint16_t* Bs, int nj, int wn, int lane) {
     using S = GemmShape<BM>;
-    constexpr int TM = S::TM, TN = S::TN;
-    if constexpr (!kLazyA) {
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
-            af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off(wm * S::MW + mi * 16 + lane % 16, lane / 16)]);
-    }
-#pragma unroll
-    for (int nj = 0; nj < TN; ++nj) {
-        // gate/up: the wave's first TN/2 tiles are gate columns, the rest the matching up columns
-        const int bcol = MODE == MODE_GATEUP ? (nj / (TN / 2)) * (kBN / 2) + wn * (S::NW / 2) + (nj % (TN / 2)) * 16
-                                             : wn * S::NW + nj * 16;
-        const int brow = AWQ ? awq_row(bcol + lane % 16) : bcol + lane % 16;
-        bfr[nj] = *reinterpret_cast<const bf16x8_t*>(&Bs[lds_off(brow, lane / 16)]);
-    }
+    constexpr int TN = S::TN;
+    const int bcol = MODE == MODE_GATEUP ? (nj / (TN / 2)) * (kBN / 2) + wn * (S::NW / 2) + (nj % (TN / 2)) * 16
+                                         : wn * S::NW + nj * 16;
+    const int brow = WF == 1 ? awq_row(bcol + lane % 16) : bcol + lane % 16;
+    return *reinterpret_cast<const bf16x8_t*>(&Bs[lds_off(brow, lane / 16)]);
 }
 
-// One K step, interleaved by hand: the next stage's LDS stores (A chunks, and
-// bf16 B chunks or one dequantised AWQ column) are cut into 8 slices, each
-// followed by 1/8 of this step's MFMAs; scheduling barriers keep the slices
-// in order, so that the VALU and LDS work issues while earlier MFMAs execute.
-// With lazy A fragments, each A fragment is read from the current stage
-// (Acur) one slice before its first MFMA, so only about two are live.
+template <int BM>
+__device__ __forceinline__ bf16x8_t a_frag(const uint16_t* As, int mi, int wm, int lane) {
+    return *reinterpret_cast<const bf16x8_t*>(&As[lds_off(wm * GemmShape<BM>::MW + mi * 16 + lane % 16, lane / 16)]);
+}
+
+// A K step is cut into 8 slices of PER = TM*TN/8 MFMAs.  Slices 0..kPipeSplit-1
+// (step_pre) also store the next step's LDS stage (A chunks, and bf16 B chunks
+// or the dequantised AWQ/FP8/NVFP4 columns), then the block barrier makes that
+// stage visible, and the remaining slices (step_post) read the next step's
+// fragments while this step's last MFMAs run.  With three LDS stages nothing
+// is written to a stage that another wave may still be reading: stage kt+1 is
+// written during step kt, and its previous contents (step kt-2) were last read
+// before step kt-1's barrier.
+constexpr int kPipeSplit = 6;
+
+// Slice of the first MFMA of A row mi (MFMAs run row-major before the barrier).
+template <int BM>
+constexpr int first_slice(int mi) {
+    return mi * GemmShape<BM>::TN / (GemmShape<BM>::TM * GemmShape<BM>::TN / 8);
+}
+
+// Slices 0..kPipeSplit-1 of step kt: stores of step kt+1 (registers ra/rb/rw,
+// parameters Ps, into As/Bs) and MFMAs from the fragments in registers (bfr,
+// af[0]) and A fragments read from Acur one slice before their first use;
+// fragments of rows whose MFMAs fall after the barrier are read in the last
+// slice here.
 template <int MODE, int WF, int BM>
-__device__ __forceinline__ void step_interleaved(bf16x8_t (&af)[GemmShape<BM>::TM],
-                                                 const bf16x8_t (&bfr)[GemmShape<BM>::TN],
-                                                 f32x4_t (&acc)[GemmShape<BM>::TM][GemmShape<BM>::TN],
-                                                 const uint4 (&ra)[GemmShape<BM>::APER],
-                                                 const uint4 (&rb)[GemmShape<BM>::BPER],
-                                                 const uint32_t (&rw)[GemmShape<BM>::RPT],
-                                                 const float2* Ps, uint16_t* As, uint16_t* Bs, int tid,
-                                                 const uint16_t* Acur, int wm, int lane) {
+__device__ __forceinline__ void step_pre(bf16x8_t (&af)[GemmShape<BM>::TM], const bf16x8_t (&bfr)[GemmShape<BM>::TN],
+                                         f32x4_t (&acc)[GemmShape<BM>::TM][GemmShape<BM>::TN],
+                                         const uint4 (&ra)[GemmShape<BM>::APER],
+                                         const uint4 (&rb)[GemmShape<BM>::BPER],
+                                         const uint32_t (&rw)[GemmShape<BM>::RPT], const float2* Ps, uint16_t* As,
+                                         uint16_t* Bs, int tid, const uint16_t* Acur, int wm, int lane) {
     constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
-    (void)FP8;
-    (void)NV4;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
-    constexpr int NM = TM * TN;  // MFMAs this step
-    constexpr int PER = NM / 8;  // per slice
-    auto load_a = [&](int mi) {
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(&Acur[lds_off(wm * S::MW + mi * 16 + lane % 16, lane / 16)]);
-    };
-    if constexpr (kLazyA) {
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
-            if ((mi * TN) / PER == 0) load_a(mi);  // fragments first used in slice 0
-    }
+    constexpr int PER = TM * TN / 8, SB = kPipeSplit;
+    static_assert(TM * TN % 8 == 0 && SB * PER >= TN, "row 0 must end before the barrier");
+    static_assert(S::APER <= SB && S::BPER <= SB, "stores must fit before the barrier");
     int cbase = 0, sub = 0;
     uint32_t even[S::RPT], odd[S::RPT];
     float sc[8], cc[8];
@@ -340,7 +337,7 @@ __device__ __forceinline__ void step_interleaved(bf16x8_t (&af)[GemmShape<BM>::T
         awq_split<S::RPT>(rw, even, odd);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < SB; ++j) {
         if (j < S::APER) {
             const int q = tid + j * S::NT;
             if (S::AQ % S::NT == 0 || q < S::AQ) *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[j];
@@ -355,18 +352,41 @@ __device__ __forceinline__ void step_interleaved(bf16x8_t (&af)[GemmShape<BM>::T
                 *reinterpret_cast<uint4*>(&Bs[lds_off(q / 4, q % 4)]) = rb[j];
             }
         } else {
-            awq_store_col<MODE, S::RPT>(j, even, odd, sc, cc, Bs, cbase, sub);
-        }
-        if constexpr (kLazyA) {
 #pragma unroll
-            for (int mi = 0; mi < TM; ++mi)
-                if ((mi * TN) / PER == j + 1) load_a(mi);  // first used in the next slice
+            for (int c = 0; c < 8; ++c)
+                if (c * SB / 8 == j) awq_store_col<MODE, S::RPT>(c, even, odd, sc, cc, Bs, cbase, sub);
+        }
+#pragma unroll
+        for (int mi = 1; mi < TM; ++mi) {
+            const int f = first_slice<BM>(mi);
+            if ((f < SB && f == j + 1) || (f >= SB && j == SB - 1)) af[mi] = a_frag<BM>(Acur, mi, wm, lane);
         }
 #pragma unroll
         for (int m = j * PER; m < (j + 1) * PER; ++m)
             acc[m / TN][m % TN] =
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m / TN], bfr[m % TN], acc[m / TN][m % TN], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The MFMAs after the barrier, column by column, each B fragment register
+// refilled with the next step's fragment (from Bn) once its last MFMA has
+// issued; A fragment 0 of the next step (from An) is read first.
+template <int MODE, int WF, int BM>
+__device__ __forceinline__ void step_post(bf16x8_t (&af)[GemmShape<BM>::TM], bf16x8_t (&bfr)[GemmShape<BM>::TN],
+                                          f32x4_t (&acc)[GemmShape<BM>::TM][GemmShape<BM>::TN],
+                                          const uint16_t* An, const uint16_t* Bn, int wm, int wn, int lane) {
+    using S = GemmShape<BM>;
+    constexpr int TM = S::TM, TN = S::TN;
+    constexpr int M0 = kPipeSplit * (TM * TN / 8);  // first MFMA after the barrier (row-major index)
+    af[0] = a_frag<BM>(An, 0, wm, lane);
+#pragma unroll
+    for (int nj = 0; nj < TN; ++nj) {
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+            if (mi * TN + nj >= M0)
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
+        bfr[nj] = b_frag<MODE, WF, BM>(Bn, nj, wn, lane);
     }
 }
 
@@ -379,9 +399,9 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
     (void)NV4;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN, APER = S::APER, BPER = S::BPER, NTHR = S::NT;
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kBK];
-    __shared__ __attribute__((aligned(16))) float2 Ps[2][kBN];  // AWQ (s, -(16 + z) s) per column
+    __shared__ __attribute__((aligned(16))) uint16_t As[3][BM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[3][kBN * kBK];
+    __shared__ __attribute__((aligned(16))) float2 Ps[3][kBN];  // AWQ (s, -(16 + z) s) per column
 
     const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
     if (l < 0) return;
@@ -536,7 +556,8 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
         }                                                                                     \
     } while (0)
 
-    // prologue: steps 0 and 1 in registers, their parameters in LDS, step 0 in LDS
+    // prologue: steps 0 and 1 in registers, their parameters in LDS, step 0 in
+    // LDS stage 0 and its first fragments in registers
     MOE_LOAD(ra0, rb0, rw0, pz0, ps0, 0);
     MOE_LOAD(ra1, rb1, rw1, pz1, ps1, 1);
     MOE_PARAMS(pz0, ps0, 0);
@@ -544,20 +565,23 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
     __syncthreads();
     store_stage<MODE, WF, BM>(ra0, rb0, rw0, Ps[0], As[0], Bs[0], tid);
     __syncthreads();
-    // Loads past the end repeat the last step; the spare LDS stage absorbs the
-    // last stores.  No branches inside a step: one scheduling region.  Stage 0
-    // refills with step kt+2 while stage 1 (step kt+1) is stored; the stages then
-    // swap by value (register moves; unrolling instead makes the compiler merge
-    // the two halves and address the stages in memory).
+    bf16x8_t af[TM], bfr[TN];
+    af[0] = a_frag<BM>(As[0], 0, wm, lane);
+#pragma unroll
+    for (int nj = 0; nj < TN; ++nj) bfr[nj] = b_frag<MODE, WF, BM>(Bs[0], nj, wn, lane);
+    // Loads past the end repeat the last step; the spare LDS stages absorb the
+    // last stores.  No branches inside a step: one scheduling region per half.
+    // Register stage 0 refills with step kt+2 while stage 1 (step kt+1) is
+    // stored; the stages then swap by value (register moves; unrolling instead
+    // makes the compiler merge the two halves and address the stages in memory).
+    int s0 = 0;  // LDS stage of step kt
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
+        const int s1 = s0 == 2 ? 0 : s0 + 1, s2 = s1 == 2 ? 0 : s1 + 1;  // stages of steps kt+1, kt+2
         MOE_LOAD(ra0, rb0, rw0, pz0, ps0, min(kt + 2, nk - 1));
-        bf16x8_t af[TM], bfr[TN];
-        read_frags<MODE, WF, BM>(As[cur], Bs[cur], af, bfr, wm, wn, lane);
-        step_interleaved<MODE, WF, BM>(af, bfr, acc, ra1, rb1, rw1, Ps[cur ^ 1], As[cur ^ 1], Bs[cur ^ 1], tid,
-                                       As[cur], wm, lane);
-        MOE_PARAMS(pz0, ps0, cur);  // parameters of step kt+2 (table cur held step kt's)
+        step_pre<MODE, WF, BM>(af, bfr, acc, ra1, rb1, rw1, Ps[s1], As[s1], Bs[s1], tid, As[s0], wm, lane);
+        MOE_PARAMS(pz0, ps0, s2);  // parameters of step kt+2 (the table of step kt-1, read before the last barrier)
         __syncthreads();
+        step_post<MODE, WF, BM>(af, bfr, acc, As[s1], Bs[s1], wm, wn, lane);
 #pragma unroll
         for (int i = 0; i < APER; ++i) { const uint4 t = ra0[i]; ra0[i] = ra1[i]; ra1[i] = t; }
 #pragma unroll
@@ -566,6 +590,7 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) void grouped_gemm_kernel(Grouped
         for (int i = 0; i < S::RPT; ++i) { const uint32_t t = rw0[i]; rw0[i] = rw1[i]; rw1[i] = t; }
         { const uint32_t t = pz0; pz0 = pz1; pz1 = t; }
         { const uint32_t t = ps0; ps0 = ps1; ps1 = t; }
+        s0 = s1;
     }
 #undef MOE_LOAD
 #undef MOE_PARAMS
