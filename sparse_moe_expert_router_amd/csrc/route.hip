@@ -277,15 +277,31 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t
 //    than 64 experts qualify (near-degenerate logits) the token is recomputed
 //    for all experts.
 // ---------------------------------------------------------------------------
+// 16-byte loads, kQuadBatch of them in flight per lane
+constexpr int kQuadBatch = 5;
+
 __global__ __launch_bounds__(256) void row_norms_kernel(const uint16_t* __restrict__ w, int E, int H,
                                                         double* __restrict__ norm) {
     const int lane = threadIdx.x % kWave;
     const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (e >= E) return;
+    const uint4* wv = reinterpret_cast<const uint4*>(w + (size_t)e * H);
     double s = 0.0;
-    for (int h = lane; h < H; h += kWave) {
-        const double v = (double)bf16_to_f32(w[(size_t)e * H + h]);
-        s = fma(v, v, s);
+    for (int c0 = lane; c0 < H / 8; c0 += kWave * kQuadBatch) {
+        uint4 w4[kQuadBatch];
+#pragma unroll
+        for (int u = 0; u < kQuadBatch; ++u) w4[u] = wv[min(c0 + kWave * u, H / 8 - 1)];
+#pragma unroll
+        for (int u = 0; u < kQuadBatch; ++u) {
+            if (c0 + kWave * u >= H / 8) break;
+            const uint32_t ww[4] = {w4[u].x, w4[u].y, w4[u].z, w4[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double lo = (double)bf16_to_f32(ww[i] & 0xFFFFu), hi = (double)bf16_to_f32(ww[i] >> 16);
+                s = fma(lo, lo, s);
+                s = fma(hi, hi, s);
+            }
+        }
     }
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) s += shfl_xor_f64(s, m);
@@ -318,7 +334,6 @@ __device__ __forceinline__ float wave_exact_logit(const uint16_t* __restrict__ x
 // hidden dimension; fp64 FMAs, a 16-lane tree, one rounding.  Every lane
 // returns its group's logit.  Loads go out kQuadBatch vectors at a time
 // before any of them is used.
-constexpr int kQuadBatch = 5;
 __device__ __forceinline__ float quad_exact_logit(const uint16_t* __restrict__ xr,
                                                   const uint16_t* __restrict__ wr, int H, int e_g) {
     const int l16 = threadIdx.x % 16;
@@ -410,14 +425,20 @@ __global__ __launch_bounds__(256) void route_refine_kernel(
 
     // ||x_t|| (fp64) and the bound factor
     double xs = 0.0;
-    for (int c = lane; c < H / 8; c += kWave) {
-        const uint4 x4 = reinterpret_cast<const uint4*>(xr)[c];
-        const uint32_t xx[4] = {x4.x, x4.y, x4.z, x4.w};
+    for (int c0 = lane; c0 < H / 8; c0 += kWave * kQuadBatch) {
+        uint4 x4[kQuadBatch];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const double a = (double)bf16_to_f32(xx[i] & 0xFFFFu), b = (double)bf16_to_f32(xx[i] >> 16);
-            xs = fma(a, a, xs);
-            xs = fma(b, b, xs);
+        for (int u = 0; u < kQuadBatch; ++u) x4[u] = reinterpret_cast<const uint4*>(xr)[min(c0 + kWave * u, H / 8 - 1)];
+#pragma unroll
+        for (int u = 0; u < kQuadBatch; ++u) {
+            if (c0 + kWave * u >= H / 8) break;
+            const uint32_t xx[4] = {x4[u].x, x4[u].y, x4[u].z, x4[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double a = (double)bf16_to_f32(xx[i] & 0xFFFFu), b = (double)bf16_to_f32(xx[i] >> 16);
+                xs = fma(a, a, xs);
+                xs = fma(b, b, xs);
+            }
         }
     }
 #pragma unroll
