@@ -264,23 +264,28 @@ def test_grouped_ffn_is_deterministic():
 # ----------------------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("rows_f32", [False, True])
-def test_combine_matches_oracle(rows_f32):
+@pytest.mark.parametrize("T,k,H,with_shared", [(50, 3, 256, True),      # one wave per 64 vectors
+                                               (16, 10, 2560, True),    # decode shape: batches 8 + 2
+                                               (4200, 2, 256, True),    # one workgroup per token, 32 of 64 lanes
+                                               (7, 70, 136, False),     # k > 64: slots in two chunks, 17 vectors
+                                               (3, 13, 64, False)])     # batches 8 + 4 + 1
+def test_combine_matches_oracle(rows_f32, T, k, H, with_shared):
     moe = require_gpu()
-    T, k, H = 50, 3, 256
-    g = torch.Generator().manual_seed(9)
+    g = torch.Generator().manual_seed(9 + T + k)
     rows = torch.randn((T * k, H), generator=g).cuda()
     if not rows_f32:
         rows = rows.to(torch.bfloat16)
     perm = torch.randperm(T * k, generator=g).to(torch.int32).cuda()
     gate = torch.softmax(torch.randn((T, k), generator=g), 1).cuda()
-    shared = torch.randn((T, H), generator=g).to(torch.bfloat16).cuda()
-    scale = torch.randn(T, generator=g).cuda()
+    shared = torch.randn((T, H), generator=g).to(torch.bfloat16).cuda() if with_shared else None
+    scale = torch.randn(T, generator=g).cuda() if with_shared else None
     y = moe.combine(rows, perm, gate, shared, scale)
     torch.cuda.synchronize()
     r = rows.double().cpu().numpy()[perm.cpu().numpy().astype(np.int64)]
-    ref = O.combine(r, gate.double().cpu().numpy(), shared.double().cpu().numpy(),
-                    scale.double().cpu().numpy())
-    check_close(y.float().cpu().numpy(), ref, "combine")
+    sh = shared.double().cpu().numpy() if with_shared else None
+    sc = scale.double().cpu().numpy() if with_shared else None
+    ref = O.combine(r, gate.double().cpu().numpy(), sh, sc)
+    check_close(y.float().cpu().numpy(), ref, f"combine T={T} k={k} H={H}")
 
 
 # ----------------------------------------------------------------------------- pruning, keep policies
