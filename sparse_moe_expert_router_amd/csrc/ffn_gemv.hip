@@ -28,8 +28,6 @@ __device__ __forceinline__ int row_token(const int32_t* sorted_pair, int k, int 
     return sorted_pair ? sorted_pair[r] / k : r;
 }
 
-constexpr bool kAwqPrefetch = false;  // next group's words in flight during the current group
-
 // Registers of one group of one word column: 32 code words (input rows
 // 32g..32g+31), the packed zero word and the 8 fp16 scales.
 struct AwqGroupRegs {
@@ -92,7 +90,9 @@ __device__ __forceinline__ void awq_group_dot(const AwqGroupRegs& r, const uint3
 // word column c of a projection (I inputs, OW = O/8 words per input row).
 // xs: activation pairs [RCH][npairs] (row pairs relative to group g_base),
 // xsum: [RCH][ngroups] group sums.  res[j][i]: column 8c + kAwqNib[j], row i.
-// The next group's words are in flight while the current one is computed.
+// One group's 37 loads are in flight at a time per thread; the other waves of
+// the compute unit cover the latency (a second register set for the next
+// group costs occupancy and measured slower).
 template <int RCH>
 __device__ __forceinline__ void awq_gemv_groups(const int32_t* __restrict__ qw,
                                                 const int32_t* __restrict__ qz,
@@ -101,23 +101,10 @@ __device__ __forceinline__ void awq_gemv_groups(const int32_t* __restrict__ qw,
                                                 int g_step, const uint32_t* xs, int npairs,
                                                 const float* xsum, int ngroups,
                                                 float (&res)[8][RCH]) {
-    if (g_begin >= g_end) return;
-    if constexpr (kAwqPrefetch) {
-        AwqGroupRegs cur, nxt;
-        awq_load_group(qw, qz, sc, O, OW, c, g_begin, cur);
-        int g = g_begin;
-        for (; g + g_step < g_end; g += g_step) {
-            awq_load_group(qw, qz, sc, O, OW, c, g + g_step, nxt);
-            awq_group_dot<RCH>(cur, xs, npairs, xsum, ngroups, g - g_base, res);
-            cur = nxt;
-        }
+    for (int g = g_begin; g < g_end; g += g_step) {
+        AwqGroupRegs cur;
+        awq_load_group(qw, qz, sc, O, OW, c, g, cur);
         awq_group_dot<RCH>(cur, xs, npairs, xsum, ngroups, g - g_base, res);
-    } else {
-        for (int g = g_begin; g < g_end; g += g_step) {
-            AwqGroupRegs cur;
-            awq_load_group(qw, qz, sc, O, OW, c, g, cur);
-            awq_group_dot<RCH>(cur, xs, npairs, xsum, ngroups, g - g_base, res);
-        }
     }
 }
 
