@@ -408,8 +408,12 @@ __device__ __forceinline__ void rank_emit(uint64_t key, int n, uint64_t* kbuf, f
     }
 }
 
-template <int VPL>
-__global__ __launch_bounds__(256) void route_refine_kernel(
+// XV > 0: H == 512 * XV, and token t's inputs stay in registers as fp64
+// (vector c = lane + 64 u of 8 inputs, u < XV) while the candidates' exact
+// logits are formed one per wave pass; XV = 0: four candidates at a time with
+// 16 lanes each (quad_exact_logit), any H.
+template <int VPL, int XV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(XV == 5 && VPL <= 8 ? 4 : 1))) void route_refine_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ la,
     const double* __restrict__ wnorm, int T, int H, int E, int K, int k, int32_t* __restrict__ idx,
     float* __restrict__ topk_logit, float* __restrict__ gate) {
@@ -501,6 +505,45 @@ __global__ __launch_bounds__(256) void route_refine_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (ncand > kWave) overflow = true;
 
+    if (!overflow && XV > 0) {
+        // exact logits of the candidates, one per pass of the whole wave over
+        // the fp64 inputs; candidate j's logit ends in lane j
+        const uint4* xv = reinterpret_cast<const uint4*>(xr);
+        double xd[XV > 0 ? XV : 1][8];
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const uint4 x4 = xv[lane + kWave * u];
+            const uint32_t xx[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xd[u][2 * i] = (double)bf16_to_f32(xx[i] & 0xFFFFu);
+                xd[u][2 * i + 1] = (double)bf16_to_f32(xx[i] >> 16);
+            }
+        }
+        float mine = 0.0f;
+        for (int j = 0; j < ncand; ++j) {
+            const uint4* wv4 = reinterpret_cast<const uint4*>(wr + (size_t)cand[wv][j] * H);
+            uint4 w4[XV > 0 ? XV : 1];
+#pragma unroll
+            for (int u = 0; u < XV; ++u) w4[u] = wv4[lane + kWave * u];
+            double acc = 0.0;
+#pragma unroll
+            for (int u = 0; u < XV; ++u) {
+                const uint32_t ww[4] = {w4[u].x, w4[u].y, w4[u].z, w4[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc = fma(xd[u][2 * i], (double)bf16_to_f32(ww[i] & 0xFFFFu), acc);
+                    acc = fma(xd[u][2 * i + 1], (double)bf16_to_f32(ww[i] >> 16), acc);
+                }
+            }
+            const float lj = (float)wave_sum_f64(acc);  // every lane takes part
+            if (lane == j) mine = lj;
+        }
+        uint64_t key = 0;
+        if (lane < ncand) key = ((uint64_t)float_order_key(mine) << 32) | (uint32_t)(~cand[wv][lane]);
+        rank_emit(key, ncand, kbuf[wv], lbuf[wv], K, k, idx, topk_logit, gate, (size_t)t);
+        return;
+    }
     if (!overflow) {
         // exact logits of the candidates, four at a time; candidate j's logit
         // ends in lane j
@@ -567,14 +610,21 @@ hipError_t launch_route_filter(const uint16_t* x, const uint16_t* wr, int T, int
     const int K = k + extra;
     const int vpl = (E + kWave - 1) / kWave;
     dim3 grid((T + 3) / 4), block(256);
-#define MOE_REFINE(V) \
-    hipLaunchKernelGGL(route_refine_kernel<V>, grid, block, 0, s, x, wr, la, wn, T, H, E, K, k, idx, \
+#define MOE_REFINE_XV(V, XV) \
+    hipLaunchKernelGGL((route_refine_kernel<V, XV>), grid, block, 0, s, x, wr, la, wn, T, H, E, K, k, idx, \
                        topk_logit, gate)
+#define MOE_REFINE(V)                          \
+    do {                                       \
+        if (H == 2560) MOE_REFINE_XV(V, 5);    \
+        else if (H == 512) MOE_REFINE_XV(V, 1); \
+        else MOE_REFINE_XV(V, 0);              \
+    } while (0)
     if (vpl <= 2) MOE_REFINE(2);
     else if (vpl <= 4) MOE_REFINE(4);
     else if (vpl <= 8) MOE_REFINE(8);
     else MOE_REFINE(16);
 #undef MOE_REFINE
+#undef MOE_REFINE_XV
     return hipGetLastError();
 }
 
