@@ -8,9 +8,10 @@
 
 namespace moe {
 
-// Rows of a token are summed in slot order, loaded in batches of 8, 4, 2
-// and 1 rows whose loads all go out before any is used (unconditional loads:
-// lanes past the row's end read its last vector and discard it).  Each wave
+// Rows of a token are summed in slot order, loaded in batches whose loads all
+// go out before any is used (unconditional loads: lanes past the row's end
+// read its last vector and discard it): bf16 rows of 9 to 16 slots in one
+// batch, otherwise batches of 8, 4, 2 and 1 rows.  Each wave
 // first reads the token's gates and row indices one per lane and takes them
 // as scalars (readlane).  grid = (T, chunks of blockDim 16-byte vectors); a
 // wave walks the vectors in steps of the whole grid's width, every lane
@@ -59,8 +60,34 @@ __device__ __forceinline__ void combine_batch(const void* rows, int H, int v, in
     }
 }
 
+// Rows j .. j+n-1 (8 < n <= 16) in one round trip: 16 loads, slots past the
+// last re-read the last slot's row (uniform clamp) and are not summed.
 template <bool kF32Rows>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ rows,
+__device__ __forceinline__ void combine_batch16(const void* rows, int H, int v, int j, int n, int rl, int gl,
+                                                float (&acc)[8]) {
+    uint4 w[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const size_t r = (size_t)__builtin_amdgcn_readlane(rl, j + min(u, n - 1));
+        w[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(rows) + r * H + v * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        if (u < n) {
+            const float g = __int_as_float(__builtin_amdgcn_readlane(gl, j + u));
+            const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] = fmaf(g, bf16_to_f32(ww[i] & 0xFFFFu), acc[2 * i]);
+                acc[2 * i + 1] = fmaf(g, bf16_to_f32(ww[i] >> 16), acc[2 * i + 1]);
+            }
+        }
+    }
+}
+
+template <bool kF32Rows>
+__global__ __launch_bounds__(512) void combine_kernel(const void* __restrict__ rows,
                                                      const int32_t* __restrict__ pair_to_row,
                                                      const float* __restrict__ gate, int T, int k,
                                                      int H, const uint16_t* __restrict__ shared,
@@ -93,6 +120,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ r
                 rl = pair_to_row[pbase + j];
             }
             int j = 0;
+            if constexpr (!kF32Rows) {
+                if (nj > 8 && nj <= 16) {
+                    combine_batch16<kF32Rows>(rows, H, v, 0, nj, rl, gl, acc);
+                    j = nj;
+                }
+            }
             for (; j + 8 <= nj; j += 8) combine_batch<8, kF32Rows>(rows, H, v, j, rl, gl, acc);
             if (j + 4 <= nj) { combine_batch<4, kF32Rows>(rows, H, v, j, rl, gl, acc); j += 4; }
             if (j + 2 <= nj) { combine_batch<2, kF32Rows>(rows, H, v, j, rl, gl, acc); j += 2; }
@@ -122,11 +155,12 @@ hipError_t launch_combine(const void* rows, int rows_f32, const int32_t* pair_to
                           const float* gate, int T, int k, int H, const uint16_t* shared,
                           const float* shared_scale, uint16_t* y, hipStream_t s) {
     const int nv = H / 8;
-    // one workgroup of up to 256 threads per token when there are many
-    // tokens; otherwise one wave per 64 vectors of a token
+    // one workgroup per token when there are many tokens (a wave per 64
+    // vectors, so that every wave makes one pass at H <= 4096); otherwise
+    // one wave per 64 vectors of a token
     int threads = 64, chunks = (nv + 63) / 64;
     if ((long)T * chunks >= 4096) {
-        threads = nv >= 256 ? 256 : ((nv + 63) / 64) * 64;
+        threads = min(((nv + 63) / 64) * 64, 512);
         chunks = 1;
     }
     const dim3 grid(T, chunks);

@@ -265,10 +265,13 @@ def test_grouped_ffn_is_deterministic():
 
 @pytest.mark.parametrize("rows_f32", [False, True])
 @pytest.mark.parametrize("T,k,H,with_shared", [(50, 3, 256, True),      # one wave per 64 vectors
-                                               (16, 10, 2560, True),    # decode shape: batches 8 + 2
+                                               (16, 10, 2560, True),    # decode shape: one batch of 10 (fp32: 8 + 2)
                                                (4200, 2, 256, True),    # one workgroup per token, 32 of 64 lanes
+                                               (1000, 11, 2560, True),  # five waves per token, batch of 11 (8 + 2 + 1)
+                                               (5000, 16, 512, False),  # one full batch of 16 (fp32: 8 + 8)
                                                (7, 70, 136, False),     # k > 64: slots in two chunks, 17 vectors
-                                               (3, 13, 64, False)])     # batches 8 + 4 + 1
+                                               (3, 13, 64, False),      # batch of 13 (fp32: 8 + 4 + 1)
+                                               (3, 9, 64, False)])      # batch of 9 (fp32: 8 + 1)
 def test_combine_matches_oracle(rows_f32, T, k, H, with_shared):
     moe = require_gpu()
     g = torch.Generator().manual_seed(9 + T + k)
