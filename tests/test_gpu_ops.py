@@ -45,6 +45,8 @@ def test_route_matches_oracle(T, H, E, k, extra):
 
 
 @pytest.mark.parametrize("T,H,E,k,extra", [(4096, 2560, 512, 10, 0), (2000, 2560, 256, 10, 1),
+                                           (300, 2560, 100, 7, 0),   # inputs in registers, 2 keys per lane
+                                           (200, 512, 512, 10, 1),   # inputs in registers, one vector per lane
                                            (64, 256, 256, 8, 1), (517, 512, 1024, 20, 0)])
 def test_route_screened_matches_oracle(T, H, E, k, extra):
     """Batches of >= 64 tokens with E % 256 == 0 take the screened path."""
@@ -61,11 +63,12 @@ def test_route_screened_matches_oracle(T, H, E, k, extra):
     np.testing.assert_allclose(gate.cpu().numpy(), O.gates(ref_l, ref_idx, k), rtol=1e-5, atol=1e-7)
 
 
-def test_route_screened_ties_and_degenerate_tokens():
+@pytest.mark.parametrize("H", [512, 2560])
+def test_route_screened_ties_and_degenerate_tokens(H):
     """Exact ties between router rows, and tokens whose logits are all equal
     (every expert is a candidate: the per-token fallback)."""
     moe = require_gpu()
-    w = _wl(256, 512, 256)
+    w = _wl(256, H, 256)
     x = workloads.activations(w, seed=6, device="cuda")
     wr = workloads.router(w, seed=6, device="cuda")
     for dst, src in ((9, 4), (100, 4), (200, 17), (201, 17)):
