@@ -141,8 +141,10 @@ moe_status moe_route(const uint16_t *x, const uint16_t *w_router, int32_t T, int
                      float *topk_gate, float *logits, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Permutation of (token, slot) pairs by expert: a stable counting sort of the
- * pair ids p = t*k + slot by topk_idx[p].
+ * Permutation of (token, slot) pairs by expert (architecture sheet, FFN /
+ * MoE entries: each token's hidden state goes to the k experts it selected,
+ * so every expert processes the group of rows routed to it): a stable
+ * counting sort of the pair ids p = t*k + slot by topk_idx[p].
  *   expert_offsets [E+1]: rows of expert e are [offsets[e], offsets[e+1])
  *   sorted_pair    [T*k]: pair id held by each row, ascending within an expert
  *   pair_to_row    [T*k]: inverse of sorted_pair
@@ -206,23 +208,28 @@ moe_status moe_combine(const void *rows, int32_t rows_dtype, const int32_t *pair
 
 /*
  * Refill-RMS statistics (RAZOR E256of512 card, "Selection and calibration"):
- * for each valid token t and each selected slot j < k, drop expert
- * topk_idx[t][j], promote topk_idx[t][k] (the highest-ranked unselected
+ * for each valid token t and each selected slot j < k, drop the slot's
+ * expert, promote the expert of slot k (the highest-ranked unselected
  * expert), renormalise the gates over the new set, and add the squared L2
- * norm of the change of the routed output to stat_sum[topk_idx[t][j]] and 1
- * to stat_count[...].  The shared expert cancels in the change and is not
- * needed.  Inputs come from the k+1 routing: rows are fp32 expert outputs
- * of the k+1 permutation (expert_offsets, sorted_pair, pair_to_row over
- * T*(k+1) pairs), topk_idx / topk_logit are [T][k+1].  token_valid
- * (nullable = all valid) is [T] uint8.  stat_sum (fp32 [E]) and stat_count
- * (uint32 [E]) are ADDED to, so batches accumulate; each expert's additions
- * are summed in a fixed order (64 strided partial sums over the expert's rows
- * in grouped order, then a fixed tree) and added once per call, so results
- * are reproducible.
+ * norm of the change of the routed output to stat_sum[e] and 1 to
+ * stat_count[e], e the dropped expert.  The shared expert cancels in the
+ * change and is not needed.  Inputs come from moe_route with extra = 1 and
+ * moe_permute over its k+1 slots: rows are the fp32 expert outputs of that
+ * permutation (expert_offsets [E+1], sorted_pair and pair_to_row over
+ * T*(k+1) pairs), topk_logit is [T][k+1].  The expert of every pair is the
+ * group its row falls in (expert_offsets), so the expert ids themselves are
+ * not an input.  token_valid (nullable = all valid) is [T] uint8.  stat_sum
+ * (fp32 [E]) and stat_count (uint32 [E]) are ADDED to, so batches
+ * accumulate; each expert's additions are summed in a fixed order (64
+ * strided partial sums over the expert's rows in grouped order, then a fixed
+ * tree) and added once per call, so results are reproducible.  Workspace:
+ * moe_workspace_bytes(MOE_OP_REFILL_SCORE, T, k, E, H, 0) bytes, 16-byte
+ * aligned (MOE_ERR_UNSUPPORTED otherwise).  Requires E >= k + 1,
+ * k + 1 <= 32, E <= 1024.
  */
 moe_status moe_refill_score(const float *rows, const int32_t *expert_offsets,
                             const int32_t *sorted_pair, const int32_t *pair_to_row,
-                            const int32_t *topk_idx, const float *topk_logit,
+                            const float *topk_logit,
                             const uint8_t *token_valid, int32_t T, int32_t k, int32_t H,
                             int32_t E, float *stat_sum, uint32_t *stat_count, void *ws,
                             size_t ws_bytes, void *stream);
@@ -243,7 +250,9 @@ moe_status moe_refill_finalize(const float *stat_sum, const uint32_t *stat_count
  * weights are slices of the base, in the keep-set's order):
  *   w_router_dst[j] = w_router_src[keep_idx[j]]        (may be NULL to skip)
  *   every tensor of dst expert j = that of src expert keep_idx[j]
- * keep_idx is a device array of n_keep ids in [0, src->num_experts); src and
+ * keep_idx is a device array of n_keep ids in [0, src->num_experts) (an id
+ * outside that range is clamped into it, so no access leaves the source
+ * buffers; the copied slab is then that of the clamped id); src and
  * dst are HOST pointers to structs of device pointers with the same format
  * and sizes, dst->num_experts == n_keep.
  */

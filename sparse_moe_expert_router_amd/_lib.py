@@ -73,7 +73,7 @@ def lib():
         "moe_route_permute": [P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P],
         "moe_grouped_ffn": [P, i32, i32, ctypes.POINTER(_Experts), P, P, i32, P, P, sz, P],
         "moe_combine": [P, i32, P, P, i32, i32, i32, P, P, P, P],
-        "moe_refill_score": [P, P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, sz, P],
+        "moe_refill_score": [P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, sz, P],
         "moe_refill_finalize": [P, P, i32, i32, i32, P, P, P, P],
         "moe_prune_slice": [P, i32, P, P, i32, ctypes.POINTER(_Experts), ctypes.POINTER(_Experts), P],
         "moe_router_norm_keep": [P, i32, i32, i32, P, P, P],
@@ -258,7 +258,7 @@ def combine(rows, pair_to_row, gate, shared=None, shared_scale=None, y=None):
     return y
 
 
-def refill_score(rows, offsets, sorted_pair, pair_to_row, topk_idx, topk_logit, stat_sum,
+def refill_score(rows, offsets, sorted_pair, pair_to_row, topk_logit, stat_sum,
                  stat_count, token_valid=None, ws=None):
     """Adds Refill-RMS statistics of one batch into stat_sum (f32 [E]) and stat_count (int32 [E],
     read as uint32)."""
@@ -268,8 +268,7 @@ def refill_score(rows, offsets, sorted_pair, pair_to_row, topk_idx, topk_logit, 
     E = stat_sum.shape[0]
     buf, n = _ws(ws, rows.device).get(workspace_bytes(OP_REFILL_SCORE, T, k, E, H))
     _check("moe_refill_score", lib().moe_refill_score(
-        _ptr(rows), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_to_row), _ptr(topk_idx),
-        _ptr(topk_logit), _ptr(token_valid), T, k, H, E, _ptr(stat_sum), _ptr(stat_count),
+        _ptr(rows), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_to_row), _ptr(topk_logit), _ptr(token_valid), T, k, H, E, _ptr(stat_sum), _ptr(stat_count),
         _ptr(buf), n, _stream()))
 
 

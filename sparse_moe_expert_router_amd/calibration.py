@@ -51,7 +51,7 @@ class RefillCalibration:
         idx, tl, _, _ = _lib.route(x, w_router, self.k, extra=1, ws=self.ws)
         off, sp, p2r = _lib.permute(idx, self.experts, ws=self.ws)
         rows = _lib.grouped_ffn(x, self.k + 1, bank, off, sp, out_dtype=_lib.OUT_F32, ws=self.ws)
-        _lib.refill_score(rows, off, sp, p2r, idx, tl, self.stat_sum[layer], self.stat_count[layer],
+        _lib.refill_score(rows, off, sp, p2r, tl, self.stat_sum[layer], self.stat_count[layer],
                           token_valid=token_valid, ws=self.ws)
 
     def add_row(self, layer_inputs, layers, token_valid=None):

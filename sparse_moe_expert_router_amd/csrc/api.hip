@@ -215,7 +215,7 @@ moe_status moe_combine(const void* rows, int32_t rows_dtype, const int32_t* pair
 
 moe_status moe_refill_score(const float* rows, const int32_t* expert_offsets,
                             const int32_t* sorted_pair, const int32_t* pair_to_row,
-                            const int32_t* topk_idx, const float* topk_logit,
+                            const float* topk_logit,
                             const uint8_t* token_valid, int32_t T, int32_t k, int32_t H,
                             int32_t E, float* stat_sum, uint32_t* stat_count, void* ws,
                             size_t ws_bytes, void* stream) {
@@ -227,8 +227,9 @@ moe_status moe_refill_score(const float* rows, const int32_t* expert_offsets,
         return MOE_ERR_NULL;
     if (ws_bytes < moe::refill_ws_bytes(T, k)) return MOE_ERR_WORKSPACE;
     if (!ws) return MOE_ERR_NULL;
+    if (!aligned16(ws)) return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_refill_score(rows, expert_offsets, sorted_pair, pair_to_row,
-                                               topk_idx, topk_logit, token_valid, T, k, H, E,
+                                               topk_logit, token_valid, T, k, H, E,
                                                stat_sum, stat_count, ws,
                                                static_cast<hipStream_t>(stream)));
 }
@@ -260,7 +261,7 @@ moe_status moe_prune_slice(const int32_t* keep_idx, int32_t n_keep, const uint16
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int F = src->inter;
     if (w_router_src) {
-        st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, w_router_src, w_router_dst,
+        st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, w_router_src, w_router_dst,
                                                  (size_t)H * sizeof(uint16_t), s));
         if (st != MOE_OK) return st;
     }
@@ -270,37 +271,37 @@ moe_status moe_prune_slice(const int32_t* keep_idx, int32_t n_keep, const uint16
         const size_t in = sp[m]->in_dim, out = sp[m]->out_dim;
         (void)F;
         if (sp[m]->fmt == MOE_W_BF16) {
-            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->w, const_cast<uint16_t*>(dp[m]->w),
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, sp[m]->w, const_cast<uint16_t*>(dp[m]->w),
                                                      in * out * sizeof(uint16_t), s));
             if (st != MOE_OK) return st;
         } else if (sp[m]->fmt == MOE_W_NVFP4) {
-            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->codes,
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, sp[m]->codes,
                                                      const_cast<uint8_t*>(dp[m]->codes), in / 2 * out, s));
             if (st != MOE_OK) return st;
-            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->group_scales,
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, sp[m]->group_scales,
                                                      const_cast<uint8_t*>(dp[m]->group_scales), in / 16 * out, s));
             if (st != MOE_OK) return st;
-            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->global_scale,
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, sp[m]->global_scale,
                                                      const_cast<float*>(dp[m]->global_scale), sizeof(float), s));
             if (st != MOE_OK) return st;
         } else if (sp[m]->fmt == MOE_W_FP8_BLOCK) {
-            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->codes,
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, sp[m]->codes,
                                                      const_cast<uint8_t*>(dp[m]->codes), in * out, s));
             if (st != MOE_OK) return st;
-            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->block_scales,
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, sp[m]->block_scales,
                                                      const_cast<float*>(dp[m]->block_scales),
                                                      (in / 128) * (out / 128) * sizeof(float), s));
             if (st != MOE_OK) return st;
         } else {
-            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->qweight,
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, sp[m]->qweight,
                                                      const_cast<int32_t*>(dp[m]->qweight),
                                                      in * (out / 8) * sizeof(int32_t), s));
             if (st != MOE_OK) return st;
-            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->qzeros,
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, sp[m]->qzeros,
                                                      const_cast<int32_t*>(dp[m]->qzeros),
                                                      (in / 32) * (out / 8) * sizeof(int32_t), s));
             if (st != MOE_OK) return st;
-            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, sp[m]->scales,
+            st = hip_status(moe::launch_gather_slabs(keep_idx, n_keep, src->num_experts, sp[m]->scales,
                                                      const_cast<uint16_t*>(dp[m]->scales),
                                                      (in / 32) * out * sizeof(uint16_t), s));
             if (st != MOE_OK) return st;

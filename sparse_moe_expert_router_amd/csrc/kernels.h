@@ -56,7 +56,7 @@ hipError_t launch_combine(const void* rows, int rows_f32, const int32_t* pair_to
 // ---- Refill-RMS, keep policies, pruning (refill.hip, slice.hip)
 size_t refill_ws_bytes(int T, int k);
 hipError_t launch_refill_score(const float* rows, const int32_t* offsets, const int32_t* sorted_pair,
-                               const int32_t* pair_to_row, const int32_t* idx, const float* tl,
+                               const int32_t* pair_to_row, const float* tl,
                                const uint8_t* valid, int T, int k, int H, int E, float* stat_sum,
                                uint32_t* stat_count, void* ws, hipStream_t s);
 hipError_t launch_refill_finalize(const float* stat_sum, const uint32_t* stat_count, int E, int H,
@@ -64,7 +64,7 @@ hipError_t launch_refill_finalize(const float* stat_sum, const uint32_t* stat_co
                                   hipStream_t s);
 hipError_t launch_router_norm_keep(const uint16_t* wr, int E, int H, int keep, float* norm,
                                    int32_t* keep_idx, hipStream_t s);
-hipError_t launch_gather_slabs(const int32_t* keep_idx, int n_keep, const void* src, void* dst,
+hipError_t launch_gather_slabs(const int32_t* keep_idx, int n_keep, int src_n, const void* src, void* dst,
                                size_t slab_bytes, hipStream_t s);
 
 }  // namespace moe

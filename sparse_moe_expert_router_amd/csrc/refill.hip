@@ -119,10 +119,9 @@ __global__ __launch_bounds__(64) void refill_reduce_kernel(const int32_t* __rest
 size_t refill_ws_bytes(int T, int k) { return (size_t)T * k * sizeof(float); }
 
 hipError_t launch_refill_score(const float* rows, const int32_t* offsets, const int32_t* sorted_pair,
-                               const int32_t* pair_to_row, const int32_t* idx, const float* tl,
+                               const int32_t* pair_to_row, const float* tl,
                                const uint8_t* valid, int T, int k, int H, int E, float* stat_sum,
                                uint32_t* stat_count, void* ws, hipStream_t s) {
-    (void)idx;
     float* dsq = static_cast<float*>(ws);
     const int K1 = k + 1;
     if (K1 <= 4)

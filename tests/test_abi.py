@@ -142,12 +142,14 @@ def test_nvfp4_validation():
 def test_refill_and_keep_validation():
     L = moe.lib()
     fake = ctypes.c_void_p(256)
-    assert L.moe_refill_score(fake, fake, fake, fake, fake, fake, None, 8, 10, 64, 10, fake, fake,
+    assert L.moe_refill_score(fake, fake, fake, fake, fake, None, 8, 10, 64, 10, fake, fake,
                               fake, 1 << 30, None) == SHAPE   # E < k + 1
-    assert L.moe_refill_score(fake, fake, fake, fake, fake, fake, None, 8, 40, 64, 512, fake, fake,
+    assert L.moe_refill_score(fake, fake, fake, fake, fake, None, 8, 40, 64, 512, fake, fake,
                               fake, 1 << 30, None) == UNSUP   # k + 1 > 32
-    assert L.moe_refill_score(fake, fake, fake, fake, fake, fake, None, 8, 10, 64, 512, fake, fake,
+    assert L.moe_refill_score(fake, fake, fake, fake, fake, None, 8, 10, 64, 512, fake, fake,
                               fake, 0, None) == WS
+    assert L.moe_refill_score(fake, fake, fake, fake, fake, None, 8, 10, 64, 512, fake, fake,
+                              ctypes.c_void_p(260), 1 << 30, None) == UNSUP   # misaligned workspace
     assert L.moe_refill_finalize(fake, fake, 16, 64, 17, fake, fake, fake, None) == SHAPE
     assert L.moe_refill_finalize(fake, fake, 2048, 64, 17, fake, fake, fake, None) == UNSUP
     assert L.moe_router_norm_keep(fake, 16, 64, -1, fake, fake, None) == SHAPE

@@ -89,7 +89,7 @@ def _gpu_refill(moe, d, w, keep, batches=1):
         idx, tl, gate, _ = moe.route(x, d["router"], w.k, extra=1)
         off, sp, p2r = moe.permute(idx, E)
         rows = moe.grouped_ffn(x, w.k + 1, d["experts"], off, sp, out_dtype=moe.OUT_F32)
-        moe.refill_score(rows, off, sp, p2r, idx, tl, stat_sum, stat_count)
+        moe.refill_score(rows, off, sp, p2r, tl, stat_sum, stat_count)
     score, mask, kidx = moe.refill_finalize(stat_sum, stat_count, w.H, keep)
     torch.cuda.synchronize()
     return (stat_sum.cpu().numpy(), stat_count.cpu().numpy(), score.cpu().numpy(),
