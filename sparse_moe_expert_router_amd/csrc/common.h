@@ -18,6 +18,14 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
+// True when either bf16 of a packed pair is denormal (exponent field 0,
+// mantissa not 0).
+__device__ __forceinline__ bool bf16x2_has_denormal(uint32_t w) {
+    const bool lo = (w & 0x7F80u) == 0 && (w & 0x007Fu) != 0;
+    const bool hi = (w & 0x7F800000u) == 0 && (w & 0x007F0000u) != 0;
+    return lo || hi;
+}
+
 // Round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);

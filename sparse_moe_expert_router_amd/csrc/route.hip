@@ -264,18 +264,33 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t
 //
 // 1. Approximate logits la = x . w (bf16 MFMA, fp32 accumulation) for all
 //    (token, expert) pairs.
-// 2. A bound on |la - l| that holds for any order of fp32 accumulation inside
-//    the MFMA: each K-step of 32 products adds at most 16 ulp-units
-//    (2^-20) of (|partial sum| + sum |products|), over S = H/32 steps:
-//      |la - l| <= 2^-20 (S + 1) sum_h |x_h w_h| + H 2^-100
-//               <= 2^-20 (S + 1) ||x|| ||w_e|| + H 2^-100      (Cauchy-Schwarz).
-//    Products of bf16 values are exact in fp32; the absolute term covers
-//    flushed denormal products.
-// 3. Experts whose upper bound reaches the K-th largest lower bound are the
-//    only ones that can be in the exact top K; their logits are recomputed
-//    exactly (fp64 FMAs, one fp32 rounding) and ranked exactly.  When more
-//    than 64 experts qualify (near-degenerate logits) the token is recomputed
-//    for all experts.
+// 2. A bound on |la - L|, L the exact real logit, that assumes nothing about
+//    the order or the number of roundings inside the MFMA:
+//    - a product of two bf16 values is exact in fp32 (8-bit significands);
+//    - one K-step adds 32 products to the fp32 accumulator P.  However it
+//      does so (up to 32 two-operand fp32 additions, each rounded to nearest
+//      or toward zero: relative error < 2^-23 each; or all 33 terms aligned
+//      to the largest exponent and truncated to 24 bits: < 2^-23 of the
+//      largest term each), the step's error is below
+//      33 * 2^-23 (|P| + sum_step |p|) < 2^-17 (|P| + sum_step |p|);
+//    - with |P| <= sum |p| (1 + O(2^-17 S)) over S = H/32 steps, the total is
+//      below 2^-17 (S + 1) sum_h |x_h w_h| (the +1 absorbs the second-order
+//      terms);
+//    - one more 2^-17 sum |x w| covers the fp32 rounding of L (<= 2^-24 |L|),
+//      so an expert whose exact fp32 logit could tie the K-th is a candidate;
+//    - sum_h |x_h w_h| <= ||x|| ||w_e|| (Cauchy-Schwarz), norms in fp64;
+//    - products or partial sums that fall below the fp32 normal range and
+//      are flushed lose < 2^-126 each: H 2^-100 covers them;
+//    - a bf16 input that is itself denormal might be flushed by the MFMA,
+//      an error the bound does not cover: a router row with a denormal entry
+//      gets an infinite bound (always a candidate) and a token with one is
+//      recomputed exactly for every expert.
+//    So |la - L| <= delta = 2^-17 (S + 2) ||x|| ||w_e|| + H 2^-100.
+// 3. Experts whose upper bound la + delta reaches the K-th largest lower
+//    bound are the only ones that can be in the exact top K; their logits are
+//    recomputed exactly (fp64 FMAs, one fp32 rounding) and ranked exactly.
+//    When more than 64 experts qualify (near-degenerate logits) the token is
+//    recomputed for all experts.
 // ---------------------------------------------------------------------------
 // 16-byte loads, kQuadBatch of them in flight per lane
 constexpr int kQuadBatch = 5;
@@ -287,6 +302,7 @@ __global__ __launch_bounds__(256) void row_norms_kernel(const uint16_t* __restri
     if (e >= E) return;
     const uint4* wv = reinterpret_cast<const uint4*>(w + (size_t)e * H);
     double s = 0.0;
+    bool den = false;
     for (int c0 = lane; c0 < H / 8; c0 += kWave * kQuadBatch) {
         uint4 w4[kQuadBatch];
 #pragma unroll
@@ -300,12 +316,14 @@ __global__ __launch_bounds__(256) void row_norms_kernel(const uint16_t* __restri
                 const double lo = (double)bf16_to_f32(ww[i] & 0xFFFFu), hi = (double)bf16_to_f32(ww[i] >> 16);
                 s = fma(lo, lo, s);
                 s = fma(hi, hi, s);
+                den |= bf16x2_has_denormal(ww[i]);
             }
         }
     }
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) s += shfl_xor_f64(s, m);
-    if (lane == 0) norm[e] = sqrt(s) * (1.0 + 1e-12);
+    const bool any_den = __ballot(den) != 0;
+    if (lane == 0) norm[e] = any_den ? INFINITY : sqrt(s) * (1.0 + 1e-12);
 }
 
 // Exact fp32 logit of one (token, expert): fp64 FMAs over the wave, one rounding.
@@ -429,6 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(XV == 5 && 
 
     // ||x_t|| (fp64) and the bound factor
     double xs = 0.0;
+    bool xden = false;
     for (int c0 = lane; c0 < H / 8; c0 += kWave * kQuadBatch) {
         uint4 x4[kQuadBatch];
 #pragma unroll
@@ -442,14 +461,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(XV == 5 && 
                 const double a = (double)bf16_to_f32(xx[i] & 0xFFFFu), b = (double)bf16_to_f32(xx[i] >> 16);
                 xs = fma(a, a, xs);
                 xs = fma(b, b, xs);
+                xden |= bf16x2_has_denormal(xx[i]);
             }
         }
     }
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) xs += shfl_xor_f64(xs, m);
     const double S = (double)((H + 31) / 32);
-    const double fac = ldexp(S + 1.0, -20) * sqrt(xs) * (1.0 + 1e-12);
+    const double fac = ldexp(S + 2.0, -17) * sqrt(xs) * (1.0 + 1e-12);
     const double dabs = (double)H * ldexp(1.0, -100);
+    // a denormal input may have been flushed by the MFMA: no bound holds
+    const bool x_denormal = __ballot(xden) != 0;
 
     double lo[VPL], hi[VPL];
     double mylo = -INFINITY;
@@ -457,7 +479,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(XV == 5 && 
     for (int v = 0; v < VPL; ++v) {
         const int e = v * kWave + lane;
         if (e < E) {
-            const double d = fac * wnorm[e] + dabs;
+            const double wn = wnorm[e];
+            const double d = wn == INFINITY ? INFINITY : fac * wn + dabs;
             const double l = (double)lrow[e];
             lo[v] = l - d;
             hi[v] = l + d;
@@ -503,7 +526,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(XV == 5 && 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (ncand > kWave) overflow = true;
+    if (ncand > kWave || x_denormal) overflow = true;
 
     if (!overflow && XV > 0) {
         // exact logits of the candidates, one per pass of the whole wave over
