@@ -54,3 +54,33 @@ def check_close(got, ref, what="", atol=ATOL, rtol=RTOL, norm_rtol=NORM_RTOL):
 
 def gpu_inputs(w, seed=0, device="cuda", copy=0):
     return workloads.generate(w, seed=seed, device=device, copy=copy)
+
+
+def screen_margin(moe, x, wr, k, extra, ref_l):
+    """Measured margin of the screened router's error bound.
+
+    Runs moe_route without the logits output (the screened path for batches
+    of at least 64 tokens and E a multiple of 256), reads the approximate MFMA
+    logits la that the call leaves at the start of its workspace ([T][E]
+    fp32), and compares them with the oracle's exact logits l over every
+    (token, expert) pair.  Returns (max |la - l| / delta, max |la - l| /
+    (2^-24 (S + 1) ||x|| ||w||)): the first must stay below 1 (delta =
+    2^-17 (S + 2) ||x|| ||w|| + H 2^-100 is the bound the refine step uses,
+    S = H / 32 MFMA K-steps); the second is the worst error in units of one
+    fp32 rounding (relative 2^-24) per K-step."""
+    T, H = x.shape
+    E = wr.shape[0]
+    ws = moe.Workspace(x.device)
+    moe.route(x, wr, k, extra=extra, ws=ws)
+    torch.cuda.synchronize()
+    la = ws.buf[: T * E * 4].view(torch.float32).view(T, E).cpu().numpy().astype(np.float64)
+    xf = O.bf16_bits_to_f64(bits(x))
+    wf = O.bf16_bits_to_f64(bits(wr))
+    xn = np.sqrt((xf * xf).sum(1))
+    wn = np.sqrt((wf * wf).sum(1))
+    S = (H + 31) // 32
+    scale = np.outer(xn, wn)
+    err = np.abs(la - np.asarray(ref_l, np.float64))
+    delta = np.ldexp(S + 2.0, -17) * scale + H * np.ldexp(1.0, -100)
+    units = np.ldexp(S + 1.0, -24) * scale
+    return float((err / delta).max()), float((err / np.maximum(units, 1e-300)).max())

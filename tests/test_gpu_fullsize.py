@@ -1,17 +1,20 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py times.
 
 Routing indices and the permutation are checked whole (the oracle computes
-every exact logit); layer outputs are checked on sampled tokens, Refill-RMS
-scores on sampled experts (the oracle re-evaluates every token routed to the
-expert), keep-sets and counts by properties that hold at any size."""
+every exact logit), and so is the screened router's error bound (the
+approximate MFMA logits against the exact ones); layer outputs are checked on
+sampled tokens; the Refill-RMS pass is checked whole: every expert's score
+and count and the keep-set against the oracle's full re-evaluation of all
+8192 tokens (oracle/grouped.py)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import workloads
-from tests.gpu_helpers import bits, check_close, oracle_bank, require_gpu
-from tests.test_gpu_layer import oracle_layer_sparse
+from oracle import grouped as OG
+from tests.gpu_helpers import bits, check_close, oracle_bank, require_gpu, screen_margin
+from tests.test_gpu_layer import check_refill, oracle_layer_sparse
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +53,11 @@ def test_fullsize_layer(name):
     np.testing.assert_array_equal(mid["offsets"].cpu().numpy(), ro)
     np.testing.assert_array_equal(mid["sorted_pair"].cpu().numpy(), rs)
     np.testing.assert_array_equal(mid["pair_to_row"].cpu().numpy(), rp)
+    # the screened router's bound holds for every (token, expert) pair
+    ratio, units = screen_margin(moe, d["x"], wr, w.k, 0, ref_l)
+    print(f"{name}: screened-router error / bound = {ratio:.4f} "
+          f"(worst error {units:.3f} x 2^-24 (S+1) ||x|| ||w|| )")
+    assert ratio < 1.0
     # outputs of sampled tokens (first, last and random)
     tok = _sample(16, w.T, 1)
     ref_y, _, _ = oracle_layer_sparse(d["x"], wr, w.k, bank, d["shared"], tokens=tok)
@@ -66,7 +74,7 @@ def test_fullsize_refill():
     rows = moe.grouped_ffn(d["x"], k + 1, d["experts"], off, sp, out_dtype=moe.OUT_F32)
     stat_sum = torch.zeros(E, dtype=torch.float32, device="cuda")
     stat_count = torch.zeros(E, dtype=torch.int32, device="cuda")
-    moe.refill_score(rows, off, sp, p2r, idx, tl, stat_sum, stat_count)
+    moe.refill_score(rows, off, sp, p2r, tl, stat_sum, stat_count)
     score, mask, kidx = moe.refill_finalize(stat_sum, stat_count, w.H, w.keep)
     torch.cuda.synchronize()
 
@@ -84,20 +92,47 @@ def test_fullsize_refill():
     ref_rows = O.pair_outputs(bits(d["x"])[toks], np.searchsorted(used, ref_idx[toks, slots])[:, None].astype(np.int32), ob)
     got_rows = rows.cpu().numpy()[p2r.cpu().numpy()[pairs]]
     check_close(got_rows, ref_rows, "refill rows")
-    # scores of sampled experts: the oracle re-evaluates every token routed to each
+    # every score, count and the keep-set: the oracle re-evaluates all tokens
     g_score = score.cpu().numpy()
-    full_bank = oracle_bank(d["experts"])
-    xb = bits(d["x"])
-    for e in rng.choice(E, 3, replace=False):
-        toks_e = np.nonzero((ref_idx[:, :k] == e).any(1))[0]
-        s = np.zeros(E)
-        c = np.zeros(E, np.int64)
-        O.refill_accumulate(xb[toks_e], ref_l[toks_e], k, full_bank, None, s, c)
-        ref_score = np.sqrt(s[e] / (c[e] * w.H)) if c[e] else 0.0
-        assert c[e] == len(toks_e)
-        np.testing.assert_allclose(g_score[e], ref_score, rtol=1e-3, err_msg=f"expert {e}")
-    # keep-set: the exact ranking of the GPU scores, as mask and ascending list
-    order = np.lexsort((np.arange(E), -g_score.astype(np.float64)))
-    np.testing.assert_array_equal(kidx.cpu().numpy(), np.sort(order[:w.keep]))
-    assert mask.cpu().numpy().sum() == w.keep
+    ref_s, ref_c = np.zeros(E), np.zeros(E, np.int64)
+    OG.refill_accumulate(bits(d["x"]), ref_l, k, oracle_bank(d["experts"]), ref_s, ref_c)
+    ref_score, ref_mask, ref_kidx = O.refill_finalize(ref_s, ref_c, w.H, w.keep)
+    gpu = (stat_sum.cpu().numpy(), stat_count.cpu().numpy().view(np.uint32), g_score, mask.cpu().numpy(),
+           kidx.cpu().numpy())
+    check_refill(gpu, (ref_s, ref_c, ref_score, ref_mask, ref_kidx), w.keep)
     assert np.isfinite(g_score).all() and (g_score >= 0).all()
+    ratio, units = screen_margin(moe, d["x"], d["router"], k, 1, ref_l)
+    print(f"refill_bf16: screened-router error / bound = {ratio:.4f} (worst error {units:.3f} units)")
+    assert ratio < 1.0
+
+
+def test_fullsize_calibration_row():
+    """One packed row of 32768 tokens at full geometry (hidden 2560, 512 bf16
+    experts, top-10 + 1) through the calibration stream; scores and counts of
+    sampled experts against the oracle's re-evaluation of every token routed
+    to them (RAZOR E256of512 card, "Selection and calibration": packed rows of
+    at most 32768 tokens, only valid tokens counted)."""
+    moe = require_gpu()
+    from sparse_moe_expert_router_amd.calibration import RefillCalibration
+    w = workloads.scaled(workloads.get("refill_bf16"), T=32768)
+    d = workloads.generate(w, seed=3, device="cuda", with_shared=False)
+    valid = (torch.arange(w.T, device="cuda") % 97 != 5).to(torch.uint8)   # a few padding tokens
+    cal = RefillCalibration(layers=1, experts=w.E, hidden=w.H, k=w.k, device="cuda")
+    cal.add(0, d["x"], d["router"], d["experts"], token_valid=valid)
+    torch.cuda.synchronize()
+    g_sum = cal.stat_sum[0].cpu().numpy()
+    g_cnt = cal.stat_count[0].cpu().numpy().view(np.uint32)
+    ref_l, _ = O.router_logits(bits(d["x"]), bits(d["router"]))
+    ref_idx = O.rank(ref_l, w.k)
+    vm = valid.cpu().numpy().astype(bool)
+    np.testing.assert_array_equal(g_cnt, np.bincount(ref_idx[vm].ravel(), minlength=w.E))
+    rng = np.random.default_rng(9)
+    experts = rng.choice(w.E, 4, replace=False)
+    toks = np.nonzero(np.isin(ref_idx, experts).any(1) & vm)[0]
+    ref_s, ref_c = np.zeros(w.E), np.zeros(w.E, np.int64)
+    OG.refill_accumulate(bits(d["x"]), ref_l, w.k, oracle_bank(d["experts"]), ref_s, ref_c, tokens=toks)
+    for e in experts:
+        assert ref_c[e] == g_cnt[e]
+        np.testing.assert_allclose(g_sum[e], ref_s[e], rtol=2e-3, err_msg=f"expert {e}")
+        g_score = np.sqrt(g_sum[e] / (g_cnt[e] * w.H))
+        np.testing.assert_allclose(g_score, np.sqrt(ref_s[e] / (ref_c[e] * w.H)), rtol=1e-3)
