@@ -8,9 +8,16 @@ routed experts (fp32 rows) -> refill score -> keep-set).  Steps cycle through
 several independently generated weight copies so that the weights do not stay
 in the 256 MB on-die cache between steps.
 
-Prints one JSON line: tokens/s, the roofline position of the dominant kernel
+Prints one JSON line: tokens/s; the roofline position of the dominant kernel
 (the routed grouped-expert call, timed with HIP events on its stream inside
-the timed region) and the oracle's CPU throughput on a bounded sample.
+the timed region); the roofline position of the whole layer (its algorithmic
+flops or bytes over the wall time of a step); the same figures for the
+16-token W4A16 decode layer, measured in the same process; and the oracle's
+CPU throughput on a bounded sample.
+
+The default workload is the expert-pruned W4A16 layer over one packed row of
+32768 tokens (256 of 512 experts kept, top-10, hidden 2560, width 640), the
+largest configuration that fits one GPU.
 """
 from __future__ import annotations
 
@@ -54,7 +61,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="decode_bf16",
+    p.add_argument("--workload", default="pruned_awq",
                    help="tiny_bf16, decode_bf16, decode_awq, decode_fp8, decode_nvfp4, prefill_awq, "
                         "prefill_fp8, prefill_nvfp4, pruned_awq, refill_bf16")
     p.add_argument("--copies", type=int, default=0, help="weight copies to cycle (0: auto)")
@@ -64,33 +71,41 @@ def parse():
     p.add_argument("--graph", choices=["on", "off"], default="off",
                    help="replay each step from HIP graphs ([route, permute], [routed experts], "
                         "[combine]; the shared expert stays on its side stream)")
+    p.add_argument("--secondary", default="decode_awq",
+                   help="a second workload measured in the same process ('none' skips it)")
+    p.add_argument("--secondary-steps", type=int, default=200)
     return p.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is measured on "
-              "a single MI355X.", file=sys.stderr)
-        sys.exit(2)
+def roofline(bytes_, flops, ms):
+    """Roofline position of `bytes_` algorithmic bytes and `flops` algorithmic
+    flops done in `ms` milliseconds, against whichever MI355X peak bounds them."""
+    hbm_bound = bytes_ / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12)
+    if hbm_bound:
+        achieved = bytes_ / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+
+
+def measure(moe, w, steps, warmup, copies_arg, seed, graph):
+    """Times `steps` layer steps of workload `w` (after `warmup` untimed ones).
+    Returns the figures of the JSON line and the first weight copy's inputs."""
     import numpy as np
     import torch
 
-    import sparse_moe_expert_router_amd as moe
     import workloads
 
-    w = workloads.get(args.workload)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    moe.lib()
-
     # ---- inputs: independent weight copies, each > 256 MB unless tiny
     per_copy = w.E * expert_bytes(w, w.fmt)
-    copies = args.copies or (1 if per_copy < 64e6 else max(2, int(np.ceil(1.2e9 / per_copy))))
+    copies = copies_arg or (1 if per_copy < 64e6 else max(2, int(np.ceil(1.2e9 / per_copy))))
     copies = min(copies, 8)
     sets = []
     for c in range(copies):
-        d = workloads.generate(w, seed=args.seed, device=dev, copy=c)
+        d = workloads.generate(w, seed=seed, device=dev, copy=c)
         if w.E_base:
             keep = d["keep_idx"].to(dev)
             wr, ex = moe.prune_slice(keep, d["router"], d["experts"])
@@ -117,7 +132,7 @@ def main():
             rows = moe.grouped_ffn(x, w.k + 1, d["experts"], off, sp, out_dtype=moe.OUT_F32, ws=ws)
             if ev: ev[1].record(stream)
             s, c = stats[i % copies]
-            moe.refill_score(rows, off, sp, p2r, idx, tl, s, c, ws=ws)
+            moe.refill_score(rows, off, sp, p2r, tl, s, c, ws=ws)
             moe.refill_finalize(s, c, w.H, w.keep)
             return idx
         side.wait_stream(stream)
@@ -132,25 +147,23 @@ def main():
         moe.combine(rows, p2r, gate, s)
         return idx
 
-    use_graph = args.graph == "on"
-    if use_graph:
+    if graph:
         step = graph_steps(moe, w, sets, ws, side, side_ws, stream, step)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
     ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    ms_per_step = 1e3 * elapsed / args.steps
-    value = w.T * args.steps / elapsed
+    ms_per_step = 1e3 * elapsed / steps
 
     # ---- algorithmic work of the dominant call (routed grouped experts), per call
     kk = w.k + (1 if w.refill else 0)
@@ -165,15 +178,7 @@ def main():
     out_bytes = 4 if w.refill else 2
     bytes_call = n_touched * expert_bytes(w, w.fmt) + w.T * w.H * 2 + P * w.H * out_bytes
     flops_call = 2.0 * P * 3 * w.H * w.F
-    hbm_bound = bytes_call / (PEAK_HBM_GBS * 1e9) >= flops_call / (PEAK_BF16_TFLOPS * 1e12)
-    if hbm_bound:
-        achieved = bytes_call / (ffn_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        achieved = flops_call / (ffn_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roof = roofline(bytes_call, flops_call, ffn_ms)
     roof["kernel"] = "moe_grouped_ffn (routed): gate/up + down kernels"
     roof["avg_ms"] = round(ffn_ms, 4)
     roof["algorithmic_bytes"] = int(bytes_call)
@@ -185,21 +190,68 @@ def main():
         if t.get("source_hash") == source_hash():
             roof["traffic"] = t.get("bytes_per_call")
 
-    result = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-              "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+    # ---- the whole layer: router, routed experts, shared expert (not in the
+    # Refill-RMS pass, where it cancels), activations in and out
+    layer_flops = 2.0 * w.T * w.E * w.H + flops_call
+    layer_bytes = n_touched * expert_bytes(w, w.fmt) + w.E * w.H * 2 + w.T * w.H * 2
+    if not w.refill:
+        layer_flops += 2.0 * w.T * 3 * w.H * w.Fs
+        layer_bytes += 3 * w.H * w.Fs * 2 + w.T * w.H * 2
+    layer = roofline(layer_bytes, layer_flops, ms_per_step)
+    layer["ms"] = round(ms_per_step, 4)
+    layer["algorithmic_bytes"] = int(layer_bytes)
+    layer["algorithmic_flops"] = int(layer_flops)
+
+    config = {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
+              "experts_base": w.E_base or w.E, "top_k": w.k, "expert_width": w.F,
+              "shared_width": w.Fs, "weights": w.fmt, "weight_copies": copies,
+              "touched_experts": n_touched, "hip_graphs": bool(graph)}
+    out = {"value": round(w.T * steps / elapsed, 1), "ms_per_step": round(ms_per_step, 4),
+           "config": config, "roofline": roof, "layer_roofline": layer}
+    first = sets[0]
+    del sets
+    return out, first
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is measured on "
+              "a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_moe_expert_router_amd as moe
+    import workloads
+
+    w = workloads.get(args.workload)
+    torch.cuda.set_device(torch.device("cuda:0"))
+    moe.lib()
+
+    main_fig, first = measure(moe, w, args.steps, args.warmup, args.copies, args.seed, args.graph == "on")
+    result = {"metric": METRIC, "value": main_fig["value"], "unit": "tokens/s", "n_gpus": 1,
+              "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_fig["ms_per_step"],
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": {"bf16": "bf16", "awq": "w4a16_g32/bf16", "fp8": "w8a16_e4m3_block128/bf16",
                         "nvfp4": "w4a4_nvfp4_g16/bf16"}[w.fmt],
               "data": "synthetic (seeded)",
-              "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
-                         "experts_base": w.E_base or w.E, "top_k": w.k, "expert_width": w.F,
-                         "shared_width": w.Fs, "weights": w.fmt, "weight_copies": copies,
-                         "touched_experts": n_touched, "hip_graphs": use_graph},
-              "roofline": roof}
+              "config": main_fig["config"],
+              "roofline": main_fig["roofline"],
+              "layer_roofline": main_fig["layer_roofline"]}
+
+    # ---- the 16-token W4A16 decode layer, in the same process
+    if args.secondary != "none" and args.secondary != w.name:
+        sw = workloads.get(args.secondary)
+        sec, _ = measure(moe, sw, args.secondary_steps, args.warmup, 0, args.seed, False)
+        torch.cuda.empty_cache()
+        result["secondary"] = {"workload": sw.name, "steps": args.secondary_steps,
+                               "tokens_per_s": sec["value"], "ms_per_step": sec["ms_per_step"],
+                               "config": sec["config"], "roofline": sec["roofline"],
+                               "layer_roofline": sec["layer_roofline"]}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, sets[0], args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, first, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
