@@ -193,6 +193,29 @@ moe_status moe_grouped_ffn(const uint16_t *x, int32_t T, int32_t k, const moe_ex
                            void *stream);
 
 /*
+ * moe_grouped_ffn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * moe_grouped_ffn; the scratch it needs lives in a device array of
+ * moe_grouped_ffn_noalloc_max_bytes() bytes (16 MiB) that the library holds
+ * on every GPU it runs on until the process ends.  A call whose scratch need,
+ * moe_workspace_bytes(MOE_OP_GROUPED_FFN or MOE_OP_GROUPED_FFN_NVFP4, ...),
+ * exceeds that size returns MOE_ERR_WORKSPACE and enqueues nothing (at the
+ * full layer geometry, hidden 2560, width 640, 512 experts, top-10: up to
+ * about 40 tokens).  The call allocates nothing.  Every call on one GPU uses
+ * that GPU's one array, so calls that may run at the same time on one GPU
+ * (on different streams, or from different threads) race and give undefined
+ * results; serialise them.  The first call on a device looks the array's
+ * address up (a HIP symbol query, no allocation) with that device current.
+ */
+moe_status moe_grouped_ffn_noalloc(const uint16_t *x, int32_t T, int32_t k, const moe_experts *ex,
+                                   const int32_t *expert_offsets, const int32_t *sorted_pair,
+                                   int32_t out_dtype, void *rows, void *stream);
+
+/* Bytes of the per-GPU scratch array of moe_grouped_ffn_noalloc. */
+size_t moe_grouped_ffn_noalloc_max_bytes(void);
+
+/*
  * Weighted combine (architecture sheet: routed outputs weighted by the
  * renormalised gates, plus the always-on shared expert):
  *   y[t] = sum_{j<k} topk_gate[t][j] * rows[pair_to_row[t*k+j]]

@@ -31,7 +31,8 @@ OP_ROUTE, OP_PERMUTE, OP_GROUPED_FFN, OP_REFILL_SCORE, OP_GROUPED_FFN_NVFP4, OP_
 W_BF16, W_AWQ, W_FP8, W_NVFP4 = 0, 1, 2, 3
 OUT_BF16, OUT_F32 = 0, 1
 
-EXPORTS = ["moe_route", "moe_permute", "moe_route_permute", "moe_grouped_ffn", "moe_combine", "moe_refill_score",
+EXPORTS = ["moe_route", "moe_permute", "moe_route_permute", "moe_grouped_ffn", "moe_grouped_ffn_noalloc",
+           "moe_grouped_ffn_noalloc_max_bytes", "moe_combine", "moe_refill_score",
            "moe_refill_finalize", "moe_prune_slice", "moe_router_norm_keep",
            "moe_nvfp4_quantize", "moe_workspace_bytes", "moe_status_string", "moe_last_hip_error"]
 
@@ -72,6 +73,7 @@ def lib():
         "moe_permute": [P, i32, i32, i32, P, P, P, P, sz, P],
         "moe_route_permute": [P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P],
         "moe_grouped_ffn": [P, i32, i32, ctypes.POINTER(_Experts), P, P, i32, P, P, sz, P],
+        "moe_grouped_ffn_noalloc": [P, i32, i32, ctypes.POINTER(_Experts), P, P, i32, P, P],
         "moe_combine": [P, i32, P, P, i32, i32, i32, P, P, P, P],
         "moe_refill_score": [P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, sz, P],
         "moe_refill_finalize": [P, P, i32, i32, i32, P, P, P, P],
@@ -83,6 +85,8 @@ def lib():
         f = getattr(L, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    L.moe_grouped_ffn_noalloc_max_bytes.argtypes = []
+    L.moe_grouped_ffn_noalloc_max_bytes.restype = ctypes.c_size_t
     L.moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.moe_workspace_bytes.restype = ctypes.c_size_t
     L.moe_status_string.argtypes = [ctypes.c_int]
@@ -245,6 +249,26 @@ def grouped_ffn(x, k: int, bank: dict, offsets=None, sorted_pair=None, out_dtype
                                                     _ptr(sorted_pair), out_dtype, _ptr(rows),
                                                     _ptr(buf), n, _stream()))
     return rows
+
+
+def grouped_ffn_noalloc(x, k: int, bank: dict, offsets=None, sorted_pair=None, out_dtype=OUT_BF16,
+                        rows=None):
+    """grouped_ffn through the allocation-free entry point: the library's own
+    per-GPU scratch array instead of a workspace (at most
+    noalloc_max_bytes() of scratch; larger calls raise)."""
+    T, H = x.shape
+    dev = x.device
+    if rows is None:
+        rows = torch.empty((T * k, H), dtype=torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
+                           device=dev)
+    st = experts_struct(bank)
+    _check("moe_grouped_ffn_noalloc", lib().moe_grouped_ffn_noalloc(
+        _ptr(x), T, k, ctypes.byref(st), _ptr(offsets), _ptr(sorted_pair), out_dtype, _ptr(rows), _stream()))
+    return rows
+
+
+def noalloc_max_bytes() -> int:
+    return int(lib().moe_grouped_ffn_noalloc_max_bytes())
 
 
 def combine(rows, pair_to_row, gate, shared=None, shared_scale=None, y=None):

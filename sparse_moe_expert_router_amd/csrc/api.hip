@@ -3,8 +3,13 @@
 // enqueued unless every check passes.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "moe.h"
+
+// Device scratch of moe_grouped_ffn_noalloc (16 MiB per GPU; see below).
+static __device__ __align__(256) unsigned char scratch[(size_t)16 << 20];
 
 namespace {
 
@@ -82,6 +87,73 @@ bool bank_ok(const moe_experts* ex, moe_status* st) {
         return false;
     if (fmt == MOE_W_NVFP4 && ex->gate.act_scale != ex->up.act_scale) { *st = MOE_ERR_SHAPE; return false; }
     return true;
+}
+
+// Validation shared by moe_grouped_ffn and moe_grouped_ffn_noalloc: fills the
+// launch arguments and the scratch bytes the call needs.  T == 0 passes.
+moe_status ffn_prepare(const uint16_t* x, int32_t T, int32_t k, const moe_experts* ex,
+                       const int32_t* expert_offsets, const int32_t* sorted_pair, int32_t out_dtype,
+                       void* rows, moe::FfnArgs* f, size_t* need) {
+    moe_status st = MOE_OK;
+    if (T < 0 || k < 1) return MOE_ERR_SHAPE;
+    if (!bank_ok(ex, &st)) return st;
+    if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
+    const bool identity = expert_offsets == nullptr && sorted_pair == nullptr;
+    if (!identity && (expert_offsets == nullptr || sorted_pair == nullptr)) return MOE_ERR_NULL;
+    if (identity && (ex->num_experts != 1 || k != 1)) return MOE_ERR_SHAPE;
+    if ((int64_t)T * k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !rows) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(rows)) return MOE_ERR_UNSUPPORTED;
+    const int E = ex->num_experts, H = ex->hidden, F = ex->inter;
+    *need = moe::ffn_ws_bytes(T, k, E, H, F, ex->gate.fmt == MOE_W_NVFP4);
+    f->x = x;
+    f->T = T;
+    f->k = k;
+    f->H = H;
+    f->F = F;
+    f->E = E;
+    f->ex = ex;
+    f->offsets = expert_offsets;
+    f->sorted_pair = sorted_pair;
+    f->out_f32 = out_dtype == MOE_OUT_F32;
+    f->rows = rows;
+    return MOE_OK;
+}
+
+// Scratch of moe_grouped_ffn_noalloc: one array per GPU, resident for the life
+// of the process.  Host code never uses the array's name as an address (on
+// the host it is only a handle); each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = sizeof(scratch);
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_address(hipStream_t s, void** out) {
+    int dev = -1;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return hip_status(e);
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
 }
 
 // Workspace of moe_route_permute: the two calls run one after the other on
@@ -167,36 +239,32 @@ moe_status moe_grouped_ffn(const uint16_t* x, int32_t T, int32_t k, const moe_ex
                            const int32_t* expert_offsets, const int32_t* sorted_pair,
                            int32_t out_dtype, void* rows, void* ws, size_t ws_bytes,
                            void* stream) {
-    moe_status st = MOE_OK;
-    if (T < 0 || k < 1) return MOE_ERR_SHAPE;
-    if (!bank_ok(ex, &st)) return st;
-    if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
-    const bool identity = expert_offsets == nullptr && sorted_pair == nullptr;
-    if (!identity && (expert_offsets == nullptr || sorted_pair == nullptr)) return MOE_ERR_NULL;
-    if (identity && (ex->num_experts != 1 || k != 1)) return MOE_ERR_SHAPE;
-    if ((int64_t)T * k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
-    if (T == 0) return MOE_OK;
-    if (!x || !rows) return MOE_ERR_NULL;
-    if (!aligned16(x) || !aligned16(rows)) return MOE_ERR_UNSUPPORTED;
-    const int E = ex->num_experts, H = ex->hidden, F = ex->inter;
-    const size_t need = moe::ffn_ws_bytes(T, k, E, H, F, ex->gate.fmt == MOE_W_NVFP4);
+    moe::FfnArgs f;
+    size_t need = 0;
+    moe_status st = ffn_prepare(x, T, k, ex, expert_offsets, sorted_pair, out_dtype, rows, &f, &need);
+    if (st != MOE_OK || T == 0) return st;
     if (ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (need && !ws) return MOE_ERR_NULL;
     if (!aligned16(ws)) return MOE_ERR_UNSUPPORTED;
-    moe::FfnArgs f;
-    f.x = x;
-    f.T = T;
-    f.k = k;
-    f.H = H;
-    f.F = F;
-    f.E = E;
-    f.ex = ex;
-    f.offsets = expert_offsets;
-    f.sorted_pair = sorted_pair;
-    f.out_f32 = out_dtype == MOE_OUT_F32;
-    f.rows = rows;
     return hip_status(moe::launch_ffn(f, ws, static_cast<hipStream_t>(stream)));
 }
+
+moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int32_t T, int32_t k, const moe_experts* ex,
+                                   const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                   int32_t out_dtype, void* rows, void* stream) {
+    moe::FfnArgs f;
+    size_t need = 0;
+    moe_status st = ffn_prepare(x, T, k, ex, expert_offsets, sorted_pair, out_dtype, rows, &f, &need);
+    if (st != MOE_OK || T == 0) return st;
+    if (need > kScratchBytes) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    st = scratch_address(s, &ws);
+    if (st != MOE_OK) return st;
+    return hip_status(moe::launch_ffn(f, ws, s));
+}
+
+size_t moe_grouped_ffn_noalloc_max_bytes(void) { return kScratchBytes; }
 
 moe_status moe_combine(const void* rows, int32_t rows_dtype, const int32_t* pair_to_row,
                        const float* topk_gate, int32_t T, int32_t k, int32_t H,

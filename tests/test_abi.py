@@ -171,3 +171,15 @@ def test_streaming_workspace_covers_every_row_when_the_gemm_cannot_run():
     sizes = [moe.workspace_bytes(moe.OP_GROUPED_FFN, T, 2, 8, 256, 96) for T in (100, 1000, 10000)]
     assert sizes[0] < sizes[1] < sizes[2]
     assert sizes[2] >= 9 * sizes[1]
+
+
+def test_grouped_ffn_noalloc_validation():
+    L = moe.lib()
+    assert L.moe_grouped_ffn_noalloc_max_bytes() == 16 << 20
+    fake = ctypes.c_void_p(256)
+    b = _bank(E=512, H=2560, F=640)
+    # a decode batch far beyond the scratch array is refused before any HIP call
+    assert L.moe_grouped_ffn_noalloc(fake, 4096, 10, ctypes.byref(b), fake, fake, 0, fake, None) == WS
+    assert L.moe_grouped_ffn_noalloc(fake, -1, 10, ctypes.byref(b), fake, fake, 0, fake, None) == SHAPE
+    assert L.moe_grouped_ffn_noalloc(fake, 16, 10, None, fake, fake, 0, fake, None) == NULL
+    assert L.moe_grouped_ffn_noalloc(None, 0, 10, ctypes.byref(b), fake, fake, 0, None, None) == OK
