@@ -30,7 +30,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-BF16, AWQ, FP8, NVFP4 = 0, 1, 2, 3
+BF16, AWQ, FP8, NVFP4, AWQ_OM = 0, 1, 2, 3, 4
 
 
 def build(verbose: bool = False) -> str:
@@ -189,9 +189,17 @@ def bank_from_tensors(d: dict, prefix: str = "") -> Bank:
         mk = lambda n, i, o: Proj(FP8, i, o, codes=d[prefix + n + "_codes"],
                                   bscales=d[prefix + n + "_bscales"])
         return Bank(E, H, F, mk("gate", H, F), mk("up", H, F), mk("down", F, H))
-    E, H, F8 = d[prefix + "gate_qweight"].shape
-    F = F8 * 8
-    mk = lambda n, i, o: Proj(AWQ, i, o, qweight=d[prefix + n + "_qweight"],
+    if fmt == "awq_om":
+        # AWQ codes stored output-major: qweight [E][out][in/8], nibble j of
+        # word w = input 8w + j; zeros and scales as in the AWQ layout
+        E, F, H8 = d[prefix + "gate_qweight"].shape
+        H = H8 * 8
+        fmt_id = AWQ_OM
+    else:
+        E, H, F8 = d[prefix + "gate_qweight"].shape
+        F = F8 * 8
+        fmt_id = AWQ
+    mk = lambda n, i, o: Proj(fmt_id, i, o, qweight=d[prefix + n + "_qweight"],
                               qzeros=d[prefix + n + "_qzeros"], scales=d[prefix + n + "_scales"])
     return Bank(E, H, F, mk("gate", H, F), mk("up", H, F), mk("down", F, H))
 

@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import AWQ, BF16, Bank, Proj, rank
+from . import AWQ, AWQ_OM, BF16, Bank, Proj, rank
 
 # Nibble j of an AWQ word holds column 8c + _AWQ_COL[j] (include/moe.h, AWQ layout).
 _AWQ_COL = (0, 2, 4, 6, 1, 3, 5, 7)
@@ -40,20 +40,26 @@ def proj_matrix(p: Proj, e: int) -> np.ndarray:
     """Dequantised weight matrix [out, in] (fp64, exact) of expert e of projection p."""
     if p.fmt == BF16:
         return _bf16_f64(p.w[e])
-    if p.fmt == AWQ:
+    if p.fmt in (AWQ, AWQ_OM):
         I, O = p.in_dim, p.out_dim
-        words = p.qweight[e].view(np.uint32)           # [I][O/8]
         zwords = p.qzeros[e].view(np.uint32)           # [I/32][O/8]
         q = np.empty((I, O), np.int64)
         z = np.empty((I // 32, O), np.int64)
+        if p.fmt == AWQ:
+            words = p.qweight[e].view(np.uint32)       # [I][O/8]
+            for j, col in enumerate(_AWQ_COL):
+                q[:, col::8] = (words >> np.uint32(4 * j)) & np.uint32(15)
+        else:
+            words = p.qweight[e].view(np.uint32)       # [O][I/8]: nibble j = input 8w + j
+            for j in range(8):
+                q[j::8, :] = ((words >> np.uint32(4 * j)) & np.uint32(15)).T
         for j, col in enumerate(_AWQ_COL):
-            q[:, col::8] = (words >> np.uint32(4 * j)) & np.uint32(15)
             z[:, col::8] = (zwords >> np.uint32(4 * j)) & np.uint32(15)
         s = p.scales[e].view(np.float16).astype(np.float64)  # [I/32][O]
         g = np.arange(I) // 32
         w = (q - z[g]).astype(np.float64) * s[g]           # [I][O]
         return np.ascontiguousarray(w.T)
-    raise NotImplementedError("grouped evaluation covers bf16 and AWQ banks")
+    raise NotImplementedError("grouped evaluation covers bf16 and AWQ banks (both code layouts)")
 
 
 def _silu(a):

@@ -358,7 +358,7 @@ void oracle_permute(const int32_t *idx, int64_t T, int64_t k, int64_t E,
 /* O5/O6: one SwiGLU expert, bf16 or AWQ W4 weights                           */
 /* ------------------------------------------------------------------------- */
 
-enum { ORA_BF16 = 0, ORA_AWQ = 1, ORA_FP8 = 2, ORA_NVFP4 = 3 };
+enum { ORA_BF16 = 0, ORA_AWQ = 1, ORA_FP8 = 2, ORA_NVFP4 = 3, ORA_AWQ_OM = 4 };
 
 /* One projection of a bank of experts (out x in per expert). */
 typedef struct {
@@ -366,6 +366,8 @@ typedef struct {
     int32_t in_dim, out_dim;
     const uint16_t *w;       /* bf16: [E][out][in]                  */
     const int32_t *qweight;  /* awq:  [E][in][out/8]                */
+                             /* awq, output-major codes: [E][out][in/8], nibble j
+                                of word w holds input 8w + j            */
     const int32_t *qzeros;   /* awq:  [E][in/32][out/8]             */
     const uint16_t *scales;  /* awq:  [E][in/32][out] fp16          */
     const uint8_t *codes;    /* fp8:  [E][out][in] E4M3              */
@@ -519,9 +521,18 @@ static double proj_weight(const ora_proj *p, int64_t e, int64_t o, int64_t i)
     }
     int64_t words = p->out_dim / 8, groups = p->in_dim / 32;
     int nib = awq_nibble_of_column((int)(o % 8));
-    uint32_t qw = (uint32_t)p->qweight[(e * p->in_dim + i) * words + o / 8];
+    uint32_t qw;
+    int qnib = nib;
+    if (p->fmt == ORA_AWQ_OM) {
+        /* the same codes stored with one word per 8 consecutive inputs of an
+         * output column; zeros and scales as in the AWQ layout */
+        qw = (uint32_t)p->qweight[(e * p->out_dim + o) * (p->in_dim / 8) + i / 8];
+        qnib = (int)(i % 8);
+    } else {
+        qw = (uint32_t)p->qweight[(e * p->in_dim + i) * words + o / 8];
+    }
     uint32_t zw = (uint32_t)p->qzeros[(e * groups + i / 32) * words + o / 8];
-    int q = (int)((qw >> (4 * nib)) & 15u);
+    int q = (int)((qw >> (4 * qnib)) & 15u);
     int z = (int)((zw >> (4 * nib)) & 15u);
     double s = fp16_value(p->scales[(e * groups + i / 32) * p->out_dim + o]);
     return (double)(q - z) * s;

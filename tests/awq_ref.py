@@ -40,3 +40,15 @@ def dequant_dense(qweight, qzeros, scales) -> np.ndarray:
     z = np.repeat(unpack_nibbles(qzeros), 32, axis=1)  # [E][in][out]
     s = np.repeat(np.asarray(scales, np.uint16).view(np.float16).astype(np.float64), 32, axis=1)
     return np.transpose((q - z) * s, (0, 2, 1))
+
+
+def to_output_major(qweight: np.ndarray) -> np.ndarray:
+    """AWQ codes [E][in][out/8] -> the same codes output-major [E][out][in/8]:
+    word w of output column o holds inputs 8w..8w+7, input 8w + j in nibble j."""
+    q = unpack_nibbles(qweight)                       # [E][in][out]
+    E, I, O = q.shape
+    qt = np.transpose(q, (0, 2, 1)).reshape(E, O, I // 8, 8).astype(np.uint64)
+    word = np.zeros((E, O, I // 8), np.uint64)
+    for j in range(8):
+        word |= qt[..., j] << np.uint64(4 * j)
+    return word.astype(np.uint32).view(np.int32)

@@ -72,3 +72,28 @@ def test_refill_equals_c_oracle(fmt):
     O.refill_accumulate(x[toks], logits[toks], k, bank, None, rs2, rc2)
     np.testing.assert_array_equal(sc, rc2)
     np.testing.assert_allclose(ss, rs2, rtol=1e-10, atol=1e-14 * max(rs2.max(), 1e-300))
+
+
+def test_output_major_awq_decodes_like_awq():
+    """The output-major code layout holds the same codes: every weight the
+    oracle decodes from it equals the AWQ decode (itself pinned by the
+    independent unpacker and dense brute force), and so do the grouped
+    matrices."""
+    from tests import awq_ref
+    rng = np.random.default_rng(8)
+    E, H, F = 2, 64, 96
+    a = _awq_bank(rng, E, H, F)
+    om = {}
+    for n, p in (("gate", a.gate), ("up", a.up), ("down", a.down)):
+        om[n] = O.Proj(O.AWQ_OM, p.in_dim, p.out_dim, qweight=awq_ref.to_output_major(p.qweight),
+                       qzeros=p.qzeros, scales=p.scales)
+    b = O.Bank(E, H, F, om["gate"], om["up"], om["down"])
+    for pa, pb in ((a.gate, b.gate), (a.up, b.up), (a.down, b.down)):
+        for e in range(E):
+            for o in range(pa.out_dim):
+                for i in range(0, pa.in_dim, 7):
+                    assert O.proj_weight(pa, e, o, i) == O.proj_weight(pb, e, o, i)
+            np.testing.assert_array_equal(G.proj_matrix(pa, e), G.proj_matrix(pb, e))
+    x = random_bf16(rng, (5, H))
+    idx = np.array([[0, 1]] * 5, np.int32)
+    np.testing.assert_array_equal(O.pair_outputs(x, idx, a), O.pair_outputs(x, idx, b))
