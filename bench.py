@@ -74,6 +74,9 @@ def parse():
     p.add_argument("--secondary", default="decode_awq",
                    help="a second workload measured in the same process ('none' skips it)")
     p.add_argument("--secondary-steps", type=int, default=200)
+    p.add_argument("--awq-layout", choices=["auto", "awq", "om"], default="auto",
+                   help="AWQ code layout: auto = output-major (converted at setup) when the layer sees "
+                        ">= 32 rows per expert, else the AWQ layout")
     return p.parse_args()
 
 
@@ -90,7 +93,16 @@ def roofline(bytes_, flops, ms):
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
 
 
-def measure(moe, w, steps, warmup, copies_arg, seed, graph):
+def use_output_major(w, layout):
+    """AWQ banks run on output-major codes (converted once at setup) when the
+    layer sees many rows per expert; decode batches keep the AWQ layout, whose
+    streaming kernels read it directly."""
+    if w.fmt != "awq" or layout == "awq":
+        return False
+    return layout == "om" or w.T * w.k >= 32 * w.E
+
+
+def measure(moe, w, steps, warmup, copies_arg, seed, graph, layout="auto"):
     """Times `steps` layer steps of workload `w` (after `warmup` untimed ones).
     Returns the figures of the JSON line and the first weight copy's inputs."""
     import numpy as np
@@ -110,6 +122,8 @@ def measure(moe, w, steps, warmup, copies_arg, seed, graph):
             keep = d["keep_idx"].to(dev)
             wr, ex = moe.prune_slice(keep, d["router"], d["experts"])
             d["router"], d["experts"] = wr, ex
+        if use_output_major(w, layout):
+            d["experts"] = moe.awq_to_output_major(d["experts"])
         sets.append(d)
     torch.cuda.synchronize()
     ws = moe.Workspace(dev)
@@ -205,7 +219,8 @@ def measure(moe, w, steps, warmup, copies_arg, seed, graph):
     config = {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
               "experts_base": w.E_base or w.E, "top_k": w.k, "expert_width": w.F,
               "shared_width": w.Fs, "weights": w.fmt, "weight_copies": copies,
-              "touched_experts": n_touched, "hip_graphs": bool(graph)}
+              "touched_experts": n_touched, "hip_graphs": bool(graph),
+              "awq_codes": ("output-major" if use_output_major(w, layout) else "awq") if w.fmt == "awq" else None}
     out = {"value": round(w.T * steps / elapsed, 1), "ms_per_step": round(ms_per_step, 4),
            "config": config, "roofline": roof, "layer_roofline": layer}
     first = sets[0]
@@ -228,7 +243,8 @@ def main():
     torch.cuda.set_device(torch.device("cuda:0"))
     moe.lib()
 
-    main_fig, first = measure(moe, w, args.steps, args.warmup, args.copies, args.seed, args.graph == "on")
+    main_fig, first = measure(moe, w, args.steps, args.warmup, args.copies, args.seed, args.graph == "on",
+                              args.awq_layout)
     result = {"metric": METRIC, "value": main_fig["value"], "unit": "tokens/s", "n_gpus": 1,
               "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_fig["ms_per_step"],
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -242,7 +258,7 @@ def main():
     # ---- the 16-token W4A16 decode layer, in the same process
     if args.secondary != "none" and args.secondary != w.name:
         sw = workloads.get(args.secondary)
-        sec, _ = measure(moe, sw, args.secondary_steps, args.warmup, 0, args.seed, False)
+        sec, _ = measure(moe, sw, args.secondary_steps, args.warmup, 0, args.seed, False, args.awq_layout)
         torch.cuda.empty_cache()
         result["secondary"] = {"workload": sw.name, "steps": args.secondary_steps,
                                "tokens_per_s": sec["value"], "ms_per_step": sec["ms_per_step"],

@@ -69,6 +69,17 @@
  *                  scales [E][I/32][O] fp16;
  *                nibble j (bits 4j..4j+3) of word c holds column
  *                8c + {0,2,4,6,1,3,5,7}[j];  w[e][o][i] = (q - z) * s.
+ *  AWQ experts, output-major codes (MOE_W_AWQ_G32_OM): the same codes,
+ *                zeros and scales, with only the codes rearranged so that
+ *                one word holds 8 consecutive inputs of one output column:
+ *                  qweight [E][O][I/8] int32, nibble j of word w = code of
+ *                  input 8w + j;  qzeros and scales as above.
+ *                The bytes per expert are those of the AWQ layout.  This is
+ *                the layout the MFMA path reads without restaging: one word
+ *                is one lane's operand of a bf16 MFMA.  moe_awq_to_output_major
+ *                converts an AWQ bank.  Requires I and O multiples of 64,
+ *                hidden % 256 == 0 and inter % 128 == 0, and every tensor, x
+ *                and the intermediate [T*k][inter] bf16 product below 4 GiB.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -89,7 +100,8 @@ typedef enum {
     MOE_ERR_HIP = 5          /* a HIP call failed; see moe_last_hip_error()   */
 } moe_status;
 
-typedef enum { MOE_W_BF16 = 0, MOE_W_AWQ_G32 = 1, MOE_W_FP8_BLOCK = 2, MOE_W_NVFP4 = 3 } moe_wfmt;
+typedef enum { MOE_W_BF16 = 0, MOE_W_AWQ_G32 = 1, MOE_W_FP8_BLOCK = 2, MOE_W_NVFP4 = 3,
+               MOE_W_AWQ_G32_OM = 4 } moe_wfmt;
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_dtype;
 
 /* One projection of a bank of experts, input dim in_dim, output dim out_dim. */
@@ -180,6 +192,9 @@ moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, int32_
  * rows is [T*k][H] of out_dtype.  Intermediates: fp32 accumulation, the
  * SwiGLU product rounded to bf16 before the down projection (NVFP4: x and
  * the SwiGLU product are quantised as described under "NVFP4 experts").
+ * An AWQ_OM bank always runs the MFMA path (any number of rows per expert;
+ * for one or two rows per expert the AWQ layout's streaming kernels are the
+ * faster choice).
  * AWQ and NVFP4 require hidden % 32 == 0 and inter % 32 == 0, FP8 multiples
  * of 128.  x, rows, ws and the bf16 / AWQ / FP8 / NVFP4 code arrays must be
  * 16-byte aligned, FP8 block scales and NVFP4 global scales 4-byte aligned,
@@ -282,6 +297,22 @@ moe_status moe_refill_finalize(const float *stat_sum, const uint32_t *stat_count
 moe_status moe_prune_slice(const int32_t *keep_idx, int32_t n_keep, const uint16_t *w_router_src,
                            uint16_t *w_router_dst, int32_t H, const moe_experts *src,
                            const moe_experts *dst, void *stream);
+
+/*
+ * Rearranges the codes of an AWQ bank (MOE_W_AWQ_G32) into the output-major
+ * layout (MOE_W_AWQ_G32_OM, see Layouts): for each projection, dst qweight
+ * [E][O][I/8] gets, in nibble j of word w of column o, the code of input
+ * 8w + j, exactly (a bit permutation).  dst qzeros and scales must hold the
+ * same bytes as src's: they may point to src's own arrays (nothing is
+ * copied) or to arrays of the same size, into which src's are copied.  src
+ * and dst are HOST pointers to structs of device pointers with equal
+ * num_experts, hidden and inter; dst qweight may not overlap src's.  A setup
+ * step (one pass over the codes), not part of the layer's hot path.
+ * Errors: a format other than AWQ / AWQ_OM, or sizes that differ ->
+ * MOE_ERR_SHAPE; sizes the output-major layout does not support ->
+ * MOE_ERR_UNSUPPORTED; a null pointer -> MOE_ERR_NULL.
+ */
+moe_status moe_awq_to_output_major(const moe_experts *src, const moe_experts *dst, void *stream);
 
 /*
  * Router-norm keep policy (RAZOR E256of512 card, "Selection and

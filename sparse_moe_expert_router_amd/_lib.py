@@ -10,6 +10,8 @@ Expert banks are dicts of device tensors:
   awq : {"fmt": "awq", "gate_qweight": [E,H,F/8] int32, "gate_qzeros": [E,H/32,F/8] int32,
          "gate_scales": [E,H/32,F] fp16, and the same for "up_*" and "down_*"
          (down: [E,F,H/8], [E,F/32,H/8], [E,F/32,H])}
+  awq_om: as "awq" with output-major codes: "gate_qweight" [E,F,H/8], "down_qweight" [E,H,F/8]
+         (word w of a column holds inputs 8w..8w+7, input 8w+j in nibble j)
   fp8 : {"fmt": "fp8", "gate_codes": [E,F,H] uint8 E4M3, "gate_bscales": [E,F/128,H/128] f32,
          and the same for "up_*" and "down_*" (down: [E,H,F], [E,H/128,F/128])}
   nvfp4: {"fmt": "nvfp4", "gate_fp4": [E,F,H/2] uint8 (two E2M1 codes, low nibble = even
@@ -28,13 +30,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 OP_ROUTE, OP_PERMUTE, OP_GROUPED_FFN, OP_REFILL_SCORE, OP_GROUPED_FFN_NVFP4, OP_ROUTE_PERMUTE = 0, 1, 2, 3, 4, 5
-W_BF16, W_AWQ, W_FP8, W_NVFP4 = 0, 1, 2, 3
+W_BF16, W_AWQ, W_FP8, W_NVFP4, W_AWQ_OM = 0, 1, 2, 3, 4
 OUT_BF16, OUT_F32 = 0, 1
 
 EXPORTS = ["moe_route", "moe_permute", "moe_route_permute", "moe_grouped_ffn", "moe_grouped_ffn_noalloc",
            "moe_grouped_ffn_noalloc_max_bytes", "moe_combine", "moe_refill_score",
            "moe_refill_finalize", "moe_prune_slice", "moe_router_norm_keep",
-           "moe_nvfp4_quantize", "moe_workspace_bytes", "moe_status_string", "moe_last_hip_error"]
+           "moe_nvfp4_quantize", "moe_awq_to_output_major", "moe_workspace_bytes", "moe_status_string",
+           "moe_last_hip_error"]
 
 
 class MoeError(RuntimeError):
@@ -80,6 +83,7 @@ def lib():
         "moe_prune_slice": [P, i32, P, P, i32, ctypes.POINTER(_Experts), ctypes.POINTER(_Experts), P],
         "moe_router_norm_keep": [P, i32, i32, i32, P, P, P],
         "moe_nvfp4_quantize": [P, i32, i32, ctypes.c_float, P, P],
+        "moe_awq_to_output_major": [ctypes.POINTER(_Experts), ctypes.POINTER(_Experts), P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -163,9 +167,9 @@ def experts_struct(bank: dict):
                                    bank[n + "_fp4scales"].data_ptr(), bank[n + "_wglobal"].data_ptr(),
                                    float(ga[n]))
         return _Experts(E, H, F, mk("gate", H, F), mk("up", H, F), mk("down", F, H))
-    E, H, F8 = bank["gate_qweight"].shape
-    F = F8 * 8
-    mk = lambda n, i, o: _Proj(W_AWQ, i, o, None, bank[n + "_qweight"].data_ptr(),
+    E, H, F = bank_dims(bank)
+    fid = W_AWQ_OM if fmt == "awq_om" else W_AWQ
+    mk = lambda n, i, o: _Proj(fid, i, o, None, bank[n + "_qweight"].data_ptr(),
                                bank[n + "_qzeros"].data_ptr(), bank[n + "_scales"].data_ptr())
     return _Experts(E, H, F, mk("gate", H, F), mk("up", H, F), mk("down", F, H))
 
@@ -178,6 +182,9 @@ def bank_dims(bank: dict):
     elif bank["fmt"] == "nvfp4":
         E, F, H2 = bank["gate_fp4"].shape
         H = H2 * 2
+    elif bank["fmt"] == "awq_om":
+        E, F, H8 = bank["gate_qweight"].shape
+        H = H8 * 8
     else:
         E, H, F8 = bank["gate_qweight"].shape
         F = F8 * 8
@@ -336,6 +343,23 @@ def nvfp4_quantize(x, act_scale: float, out=None):
         out = torch.empty_like(x)
     _check("moe_nvfp4_quantize", lib().moe_nvfp4_quantize(_ptr(x), T, n, float(act_scale), _ptr(out),
                                                           _stream()))
+    return out
+
+
+def awq_to_output_major(bank: dict) -> dict:
+    """The AWQ bank with its codes rearranged output-major (format "awq_om"); the
+    zeros and scales tensors are shared with `bank`, not copied."""
+    assert bank["fmt"] == "awq"
+    E, H, F = bank_dims(bank)
+    out = {"fmt": "awq_om"}
+    for n, (i, o) in (("gate", (H, F)), ("up", (H, F)), ("down", (F, H))):
+        q = bank[n + "_qweight"]
+        out[n + "_qweight"] = torch.empty((E, o, i // 8), dtype=torch.int32, device=q.device)
+        out[n + "_qzeros"] = bank[n + "_qzeros"]
+        out[n + "_scales"] = bank[n + "_scales"]
+    src, dst = experts_struct(bank), experts_struct(out)
+    _check("moe_awq_to_output_major", lib().moe_awq_to_output_major(ctypes.byref(src), ctypes.byref(dst),
+                                                                    _stream()))
     return out
 
 

@@ -46,9 +46,14 @@ bool proj_ok(const moe_proj& p, int fmt, int in_dim, int out_dim, int E, moe_sta
     if (fmt == MOE_W_BF16) {
         if (!p.w) { *st = MOE_ERR_NULL; return false; }
         if (!aligned16(p.w)) { *st = MOE_ERR_UNSUPPORTED; return false; }
-    } else if (fmt == MOE_W_AWQ_G32) {
+    } else if (fmt == MOE_W_AWQ_G32 || fmt == MOE_W_AWQ_G32_OM) {
         if (!p.qweight || !p.qzeros || !p.scales) { *st = MOE_ERR_NULL; return false; }
         if (in_dim % 32 || out_dim % 32) { *st = MOE_ERR_UNSUPPORTED; return false; }
+        if (fmt == MOE_W_AWQ_G32_OM &&
+            (in_dim % 64 || out_dim % 64 || (uint64_t)E * in_dim * out_dim / 2 >= (1ull << 32))) {
+            *st = MOE_ERR_UNSUPPORTED;
+            return false;
+        }
         if (!aligned16(p.qweight) || !aligned16(p.scales) || ((uintptr_t)p.qzeros % 4)) {
             *st = MOE_ERR_UNSUPPORTED;
             return false;
@@ -86,6 +91,7 @@ bool bank_ok(const moe_experts* ex, moe_status* st) {
           proj_ok(ex->down, fmt, F, H, E, st)))
         return false;
     if (fmt == MOE_W_NVFP4 && ex->gate.act_scale != ex->up.act_scale) { *st = MOE_ERR_SHAPE; return false; }
+    if (fmt == MOE_W_AWQ_G32_OM && !moe::om_gemm_supported(H, F)) { *st = MOE_ERR_UNSUPPORTED; return false; }
     return true;
 }
 
@@ -106,7 +112,10 @@ moe_status ffn_prepare(const uint16_t* x, int32_t T, int32_t k, const moe_expert
     if (!x || !rows) return MOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(rows)) return MOE_ERR_UNSUPPORTED;
     const int E = ex->num_experts, H = ex->hidden, F = ex->inter;
-    *need = moe::ffn_ws_bytes(T, k, E, H, F, ex->gate.fmt == MOE_W_NVFP4);
+    if (ex->gate.fmt == MOE_W_AWQ_G32_OM &&
+        ((uint64_t)T * H * 2 >= (1ull << 32) || (uint64_t)T * k * F * 2 >= (1ull << 32)))
+        return MOE_ERR_UNSUPPORTED;
+    *need = moe::ffn_ws_bytes(T, k, E, H, F, ex->gate.fmt);
     f->x = x;
     f->T = T;
     f->k = k;
@@ -378,6 +387,44 @@ moe_status moe_prune_slice(const int32_t* keep_idx, int32_t n_keep, const uint16
     return MOE_OK;
 }
 
+moe_status moe_awq_to_output_major(const moe_experts* src, const moe_experts* dst, void* stream) {
+    moe_status st = MOE_OK;
+    if (!src || !dst) return MOE_ERR_NULL;
+    if (src->gate.fmt != MOE_W_AWQ_G32 || dst->gate.fmt != MOE_W_AWQ_G32_OM) return MOE_ERR_SHAPE;
+    if (src->num_experts != dst->num_experts || src->hidden != dst->hidden || src->inter != dst->inter)
+        return MOE_ERR_SHAPE;
+    if (!bank_ok(src, &st) || !bank_ok(dst, &st)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int E = src->num_experts;
+    const moe_proj* sp[3] = {&src->gate, &src->up, &src->down};
+    const moe_proj* dp[3] = {&dst->gate, &dst->up, &dst->down};
+    for (int m = 0; m < 3; ++m) {
+        const size_t I = sp[m]->in_dim, O = sp[m]->out_dim;
+        const size_t qb = (size_t)E * I * O / 2;
+        const char* sq = reinterpret_cast<const char*>(sp[m]->qweight);
+        const char* dq = reinterpret_cast<const char*>(dp[m]->qweight);
+        if (sq < dq + qb && dq < sq + qb) return MOE_ERR_SHAPE;  // overlapping codes
+    }
+    for (int m = 0; m < 3; ++m) {
+        const int I = sp[m]->in_dim, O = sp[m]->out_dim;
+        st = hip_status(moe::launch_awq_to_om(sp[m]->qweight, const_cast<int32_t*>(dp[m]->qweight), E, I, O, s));
+        if (st != MOE_OK) return st;
+        const size_t zb = (size_t)E * (I / 32) * (O / 8) * sizeof(int32_t);
+        const size_t sb = (size_t)E * (I / 32) * O * sizeof(uint16_t);
+        if (dp[m]->qzeros != sp[m]->qzeros) {
+            st = hip_status(hipMemcpyAsync(const_cast<int32_t*>(dp[m]->qzeros), sp[m]->qzeros, zb,
+                                           hipMemcpyDeviceToDevice, s));
+            if (st != MOE_OK) return st;
+        }
+        if (dp[m]->scales != sp[m]->scales) {
+            st = hip_status(hipMemcpyAsync(const_cast<uint16_t*>(dp[m]->scales), sp[m]->scales, sb,
+                                           hipMemcpyDeviceToDevice, s));
+            if (st != MOE_OK) return st;
+        }
+    }
+    return MOE_OK;
+}
+
 moe_status moe_router_norm_keep(const uint16_t* w_router, int32_t E, int32_t H, int32_t keep,
                                 float* norm, int32_t* keep_idx, void* stream) {
     if (E < 1 || H < 1 || keep < 0 || keep > E) return MOE_ERR_SHAPE;
@@ -403,8 +450,8 @@ size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t k, int32_t E, int32_t 
     switch (op) {
         case MOE_OP_ROUTE: return route_ws(T, E, H);
         case MOE_OP_PERMUTE: return moe::permute_ws_bytes(T, k, E);
-        case MOE_OP_GROUPED_FFN: return moe::ffn_ws_bytes(T, k, E, H, F, false);
-        case MOE_OP_GROUPED_FFN_NVFP4: return moe::ffn_ws_bytes(T, k, E, H, F, true);
+        case MOE_OP_GROUPED_FFN: return moe::ffn_ws_bytes(T, k, E, H, F, MOE_W_AWQ_G32_OM);
+        case MOE_OP_GROUPED_FFN_NVFP4: return moe::ffn_ws_bytes(T, k, E, H, F, MOE_W_NVFP4);
         case MOE_OP_ROUTE_PERMUTE: return route_permute_ws(T, k, E, H);
         case MOE_OP_REFILL_SCORE: return moe::refill_ws_bytes(T, k);
         default: return 0;

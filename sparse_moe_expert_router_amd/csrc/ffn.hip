@@ -19,8 +19,14 @@ static bool use_gemm(int P, int E, int H, int F) {
 // An NVFP4 bank adds the quantised input rows [T][H] bf16 in front.
 static size_t quant_x_bytes(int T, int H) { return ((size_t)T * H * sizeof(uint16_t) + 255) & ~(size_t)255; }
 
-size_t ffn_ws_bytes(int T, int k, int E, int H, int F, bool nvfp4) {
-    if (nvfp4) return quant_x_bytes(T, H) + ffn_ws_bytes(T, k, E, H, F, false);
+size_t ffn_ws_bytes(int T, int k, int E, int H, int F, int fmt) {
+    if (fmt == MOE_W_NVFP4) return quant_x_bytes(T, H) + ffn_ws_bytes(T, k, E, H, F, MOE_W_BF16);
+    if (fmt == MOE_W_AWQ_G32_OM) {
+        // the MFMA path at any size; the other formats' bound covers it
+        const size_t om = om_gemm_ws_bytes((int)((long)T * k), F, E);
+        const size_t other = ffn_ws_bytes(T, k, E, H, F, MOE_W_BF16);
+        return om > other ? om : other;
+    }
     const long P = (long)T * k;
     // shapes the GEMM does not take stream every row through the GEMV
     const bool gemm_ok = F % 128 == 0 && H % 256 == 0;
@@ -74,6 +80,7 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
         a.x = xq;
         ws = static_cast<char*>(ws) + quant_x_bytes(f.T, f.H);
     }
+    if (f.ex->gate.fmt == MOE_W_AWQ_G32_OM) return launch_om_gemm(a, ws, s);
     if (use_gemm(a.P, a.offsets ? a.E : 1, a.H, a.F)) return launch_gemm(a, ws, s);
     return launch_gemv(a, ws, s);
 }

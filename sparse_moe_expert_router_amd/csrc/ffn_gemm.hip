@@ -57,7 +57,6 @@ __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 32 + (
 // AWQ B tiles store B-column c at LDS row c ^ ((c >> 3) & 3): the 8-byte stores
 // of four adjacent packed words (columns 8 apart) then land in four different
 // row classes.  The permutation stays inside aligned groups of 8 columns.
-constexpr int kXcd = 8;
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
@@ -101,20 +100,6 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
         tiles[2 + 2 * (start + i)] = r0 + i * BM;
     }
     if (e == 1023) tiles[0] = scan[1023];
-}
-
-// Workgroup b runs on XCD b % 8.  The grid is an upper bound on the work (the
-// tile count is only known on the device); the `total` real work items are
-// split into 8 contiguous ranges, XCD x taking range x with its lowest-numbered
-// workgroups, so every XCD gets an equal share and the surplus workgroups of
-// every XCD exit.  Returns -1 for a surplus workgroup.  Needs gridDim a
-// multiple of 8 and at least total rounded up to a multiple of 8.
-__device__ __forceinline__ int xcd_remap(int b, int total) {
-    const int q = (total + kXcd - 1) / kXcd;
-    const int x = b % kXcd, i = b / kXcd;
-    if (i >= q) return -1;
-    const int l = x * q + i;
-    return l < total ? l : -1;
 }
 
 // Packing order {0,2,4,6,1,3,5,7}: nibble j holds column awq_perm(j) of its word.
@@ -766,8 +751,12 @@ static int pick_bm_dense(int M, int ncol) {
     return 64;
 }
 
-static size_t tiles_bytes(int P, int E) {
+size_t tiles_bytes(int P, int E) {
     return (((size_t)(1 + 2 * max_tiles(P, E, 64)) * sizeof(int32_t)) + 255) & ~(size_t)255;
+}
+
+void launch_tile_table(const int32_t* offsets, int E, int P, int BM, int32_t* tiles, hipStream_t s) {
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, P, BM, tiles);
 }
 
 size_t gemm_ws_bytes(int P, int F, int E) { return tiles_bytes(P, E) + (size_t)P * F * sizeof(uint16_t); }

@@ -1,0 +1,438 @@
+// Grouped SwiGLU experts for many rows per expert on AWQ W4A16 g32 codes
+// stored output-major: bf16 MFMA with the weights dequantised in registers.
+//
+// Qwen3.8-Flash-Next architecture sheet, FFN / MoE entries: SwiGLU experts
+// (gate, up, down), no bias, no clamp.  AWQ-g32 card, "Checkpoint": asymmetric
+// W4A16, group 32 along the input, integer zeros, fp16 scales, w = (q - z) s.
+//
+// Code layout: qweight [E][out][in/8] int32, nibble j of word w holds input
+// 8w + j of that output column (the AWQ codes rearranged once by
+// moe_awq_to_output_major); zeros [E][in/32][out/8] and scales [E][in/32][out]
+// keep the AWQ layout.  A lane of the B operand of a 32x32x16 bf16 MFMA holds
+// 8 consecutive inputs of one output column: exactly one code word, so B goes
+// from HBM straight into registers and is dequantised there; no B tile passes
+// through LDS.
+//
+// Workgroup: 256 threads, 4 waves (one per SIMD).  Tile: BM = 32 TM rows x
+// 256 B-columns (gate/up: 128 gate columns and the same 128 up columns; down:
+// 256 output columns); wave w takes all BM rows x its 64 B-columns (gate/up:
+// 32 gate + the matching 32 up columns, so SwiGLU is applied in registers),
+// TM x 2 MFMA tiles of 32 x 32 (256 fp32 accumulators a lane at TM = 8).
+//
+// K advances 64 inputs (two AWQ groups) per step, in four MFMA k-chunks of 16.
+// In k-chunk h, lane group g = lane / 32 of both operands takes inputs
+// 32 g + 8 h .. +7 of the step (any assignment of inputs to lanes gives the
+// same dot products as long as A and B agree): a lane's B words for the four
+// k-chunks are the consecutive words 8 j + 4 g .. +3 of its column (one 16-byte
+// load per step and fragment), all in AWQ group 2 j + g.
+//
+// Dequantisation of a code q with scale s and zero z: the nibble placed in the
+// top mantissa bits of an fp32 of exponent 2^4 is 16 + q exactly (one v_perm);
+// fma(16 + q, s, -(16 + z) s) = (q - z) s exactly (5 x 11 bits), then one RNE
+// to bf16 for the MFMA.
+//
+// A (token rows gathered through sorted_pair, or h rows) goes global -> VGPR ->
+// LDS, three stages, one barrier a step.  LDS rows are 128 bytes (64 inputs);
+// the 16-byte chunk c of row r sits at chunk c ^ (r & 7), so the eight lanes of
+// a fragment read that hold eight consecutive rows at one chunk touch eight
+// different 16-byte bank groups, as do the eight lanes that store one row.
+//
+// Pipeline: a step is 4 TM pieces (k-chunk h = piece / TM, A fragment mi =
+// piece % TM), each 2 MFMAs plus a share of the dequantisation of the next
+// k-chunk's B words (k-chunk 3: step j+1's first), with the A fragment of the
+// piece three ahead read from LDS, across k-chunk and step boundaries.  After
+// k-chunk 1 of step j the A registers of step j+1 are stored to their LDS
+// stage, the A loads of step j+2 go out and one barrier publishes the stage, so
+// the last pieces of step j can already read step j+1's fragments; after
+// k-chunk 2 the B words of step j+2 are requested.  Loads use raw buffer resources: a per-lane 32-bit
+// offset fixed for the whole loop plus a uniform step offset.
+#include "ffn_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kOmThreads = 256;
+constexpr int kOmBN = 256;  // B-columns per workgroup
+constexpr int kOmKS = 64;   // inputs per step
+constexpr int kOmTN = 2;    // 32-column MFMA tiles per wave
+
+enum { OM_GATEUP = 0, OM_DOWN = 1 };
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int TM>
+struct OmShape {
+    static constexpr int BM = 32 * TM;           // rows per tile
+    static constexpr int AP = TM;                // 16-byte A chunks per thread per step
+    static constexpr int STAGE = BM * kOmKS;     // bf16 elements per LDS stage
+    // epilogue staging: 4 waves x 32 rows x (64 + 4) floats, in bf16 elements
+    static constexpr int STG = 4 * 32 * (64 + 4) * 2;
+    static constexpr int SMEM = 3 * STAGE > STG ? 3 * STAGE : STG;
+};
+
+// LDS row swizzle: the 16-byte chunk c of row r sits at chunk c ^ om_swz(r).
+// om_swz(r + 32 i) == om_swz(r) for every i.
+#ifndef OM_SWZ
+#define OM_SWZ 3
+#endif
+__device__ __forceinline__ int om_swz(int r) {
+    if (OM_SWZ == 1) return (r >> 1) & 7;
+    if (OM_SWZ == 3) return (r & 7) ^ ((r >> 3) & 1);
+    return r & 7;
+}
+// LDS element offset of 16-byte chunk c of row r (128-byte rows).
+__device__ __forceinline__ int om_lds(int r, int c) { return r * kOmKS + ((c ^ om_swz(r)) << 3); }
+
+// Nibble position of column (c mod 8) in an AWQ zero word (packing order
+// {0,2,4,6,1,3,5,7}: nibble j holds column perm(j)).
+__device__ __forceinline__ int awq_nib(int c8) { return (c8 & 1) ? 4 + (c8 >> 1) : (c8 >> 1); }
+
+// One code word (8 consecutive inputs) -> 8 bf16 (q - z) s, input i in element
+// i, in parts: om_split once, then om_pair(b) for the inputs 2b, 2b+1.
+__device__ __forceinline__ void om_split(uint32_t w, uint32_t& even, uint32_t& odd) {
+    even = ((w << 3) & 0x78787878u) | 0x80808080u;  // byte b: 1 q_{2b} 000
+    odd = ((w >> 1) & 0x78787878u) | 0x80808080u;   // byte b: 1 q_{2b+1} 000
+}
+__device__ __forceinline__ uint32_t om_pair(int b, uint32_t even, uint32_t odd, float s, float c) {
+    const uint32_t sel = 0x07000C0Cu | ((uint32_t)b << 16);  // 0x41 | byte b | 0 | 0
+    const float lo = fmaf(__uint_as_float(__builtin_amdgcn_perm(0x41000000u, even, sel)), s, c);
+    const float hi = fmaf(__uint_as_float(__builtin_amdgcn_perm(0x41000000u, odd, sel)), s, c);
+    return pack_bf16x2(lo, hi);
+}
+
+// Raw buffer resource over `bytes` bytes at p (gfx9 family: word 3 = 0x00020000,
+// 32-bit data, no stride).  Loads through it take a per-lane 32-bit byte
+// offset and a uniform byte offset; an offset past `bytes` reads 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t om_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// (s, -(16 + z) s) of a lane's column from its raw scale bits and zero word.
+__device__ __forceinline__ void om_params(uint32_t sbits, uint32_t zw, int znib, float& s, float& c) {
+    s = f16_to_f32(sbits & 0xFFFFu);
+    const float z = (float)((zw >> (4 * znib)) & 15u);
+    c = -(16.0f + z) * s;
+}
+
+template <int MODE, int TM>
+__global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* __restrict__ hbuf, int NT) {
+    using S = OmShape<TM>;
+    constexpr int BM = S::BM, AP = S::AP;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[S::SMEM];
+
+    const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
+    if (l < 0) return;
+    const int tile = l / NT, nt = l % NT;
+    const int e = tiles[1 + 2 * tile];
+    const int m0 = tiles[2 + 2 * tile];
+    const int m1 = a.offsets ? min(m0 + BM, (int)a.offsets[e + 1]) : min(m0 + BM, a.P);
+
+    const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
+    const int H = a.H, F = a.F;
+    const int K = MODE == OM_GATEUP ? H : F;      // inputs of the projection(s)
+    const int N = MODE == OM_GATEUP ? F : H;      // outputs of one projection
+    const int NJ = K / kOmKS;
+
+    // ---- A: chunk q = tid + 256 i is row (tid >> 3) + 32 i, chunk tid & 7 of the step
+    const rsrc_t ra = MODE == OM_GATEUP ? om_rsrc(a.x, (uint32_t)a.T * (uint32_t)H * 2u)
+                                        : om_rsrc(hbuf, (uint32_t)a.P * (uint32_t)F * 2u);
+    uint32_t aoff[AP];  // byte offset of the chunk in step 0
+#pragma unroll
+    for (int i = 0; i < AP; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        const int gr = min(m0 + r, m1 - 1);
+        uint32_t row;
+        if (MODE == OM_GATEUP) row = (uint32_t)(a.sorted_pair ? a.sorted_pair[gr] / a.k : gr);
+        else row = (uint32_t)gr;
+        aoff[i] = row * (uint32_t)K * 2u + (uint32_t)((tid & 7) * 16);
+    }
+    const int a_st = om_lds(tid >> 3, tid & 7);  // LDS offset of chunk 0 (rows +32 i keep r & 7)
+
+    // ---- B: fragment f of the wave (32 columns), lane column lane & 31,
+    // lane group g = lane / 32.  Gate/up: fragment 0 reads the gate tensors,
+    // fragment 1 the up tensors.
+    const int g = lane >> 5;
+    const ProjDev& p0 = MODE == OM_GATEUP ? a.gate : a.down;
+    const ProjDev& p1 = MODE == OM_GATEUP ? a.up : a.down;
+    const uint32_t qbytes = (uint32_t)a.E * (uint32_t)N * (uint32_t)(K / 2);
+    const uint32_t sbytes = (uint32_t)a.E * (uint32_t)(K / 32) * (uint32_t)N * 2u;
+    const uint32_t zbytes = sbytes / 4u;
+    const rsrc_t rq0 = om_rsrc(p0.qweight, qbytes), rq1 = om_rsrc(p1.qweight, qbytes);
+    const rsrc_t rs0 = om_rsrc(p0.scales, sbytes), rs1 = om_rsrc(p1.scales, sbytes);
+    const rsrc_t rz0 = om_rsrc(p0.qzeros, zbytes), rz1 = om_rsrc(p1.qzeros, zbytes);
+    uint32_t boff[kOmTN];   // byte offset of the lane's four code words in step 0
+    uint32_t soff[kOmTN];   // byte offset of its scale in step 0
+    uint32_t zoff[kOmTN];   // byte offset of its zero word in step 0
+    int znib[kOmTN];
+#pragma unroll
+    for (int f = 0; f < kOmTN; ++f) {
+        const int col = MODE == OM_GATEUP ? nt * (kOmBN / 2) + 32 * wn + (lane & 31)
+                                          : nt * kOmBN + 64 * wn + 32 * f + (lane & 31);
+        const uint32_t grp0 = (uint32_t)e * (uint32_t)(K / 32) + (uint32_t)g;
+        boff[f] = (((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)(K / 8) + 4u * (uint32_t)g) * 4u;
+        soff[f] = (grp0 * (uint32_t)N + (uint32_t)col) * 2u;
+        zoff[f] = (grp0 * (uint32_t)(N / 8) + (uint32_t)(col >> 3)) * 4u;
+        znib[f] = awq_nib(col & 7);
+    }
+    const uint32_t sstep = 4u * (uint32_t)N, zstep = (uint32_t)N;  // bytes per step (two groups)
+
+    f32x16_t acc[TM][kOmTN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int f = 0; f < kOmTN; ++f) acc[i][f] = f32x16_t{};
+
+    // raw B of two steps (buffer = step parity): four code words, scale bits, zero word
+    u32x4_t cw[2][kOmTN];
+    uint32_t sb[2][kOmTN], zw[2][kOmTN];
+    auto load_b = [&](int buf, int j) {
+#pragma unroll
+        for (int f = 0; f < kOmTN; ++f) {
+            const bool hi = MODE == OM_GATEUP && f == 1;
+            cw[buf][f] = __builtin_amdgcn_raw_buffer_load_b128(hi ? rq1 : rq0, (int)boff[f], j * 32, 0);
+            sb[buf][f] = __builtin_amdgcn_raw_buffer_load_b16(hi ? rs1 : rs0, (int)soff[f], (int)(sstep * (uint32_t)j), 0);
+            zw[buf][f] = __builtin_amdgcn_raw_buffer_load_b32(hi ? rz1 : rz0, (int)zoff[f], (int)(zstep * (uint32_t)j), 0);
+        }
+    };
+    u32x4_t ar[AP];
+    auto load_a = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < AP; ++i) ar[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)aoff[i], j * kOmKS * 2, 0);
+    };
+    auto store_a = [&](uint16_t* st) {
+#pragma unroll
+        for (int i = 0; i < AP; ++i) *reinterpret_cast<u32x4_t*>(st + a_st + 32 * i * kOmKS) = ar[i];
+    };
+    // A fragment (h, mi): row 32 mi + (lane & 31), logical chunk 4 g + h
+    int afr[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) afr[h] = (lane & 31) * kOmKS + (((4 * g + h) ^ om_swz(lane & 31)) << 3);
+
+    u32x4_t bfr[2][kOmTN];        // dequantised B of two k-chunks (bf16 pairs)
+    float ps[kOmTN], pc[kOmTN];   // (s, c) of the step being dequantised
+    uint32_t ev[kOmTN], od[kOmTN];
+
+    // A fragments of the pieces in flight: piece p uses af[p % 4]; the read of
+    // piece p + kAD is issued in piece p.
+    constexpr int kAD = 3;
+    constexpr int NP = 4 * TM;                      // pieces per step
+    constexpr int PPC = (4 * kOmTN + TM - 1) / TM;  // dequant parts per piece (8 per k-chunk)
+    bf16x8_t af[4];
+    auto read_af = [&](const uint16_t* A, int q) {
+        af[q % 4] = *reinterpret_cast<const bf16x8_t*>(A + 32 * (q % TM) * kOmKS + afr[q / TM]);
+    };
+
+    // ---- prologue: B of steps 0 and 1, A of step 0 in LDS stage 0, A of step 1
+    // in registers, k-chunk 0 of step 0 dequantised, the first fragments read
+    load_b(0, 0);
+    load_b(1, min(1, NJ - 1));
+    load_a(0);
+    store_a(smem);
+    load_a(min(1, NJ - 1));
+#pragma unroll
+    for (int f = 0; f < kOmTN; ++f) {
+        om_params(sb[0][f], zw[0][f], znib[f], ps[f], pc[f]);
+        om_split(cw[0][f][0], ev[f], od[f]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bfr[0][f][b] = om_pair(b, ev[f], od[f], ps[f], pc[f]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kAD; ++q) read_af(smem, q);
+
+    int stage = 0;  // LDS stage of step j
+    auto step = [&](int j, int cur) {
+        const int nxt = cur ^ 1;
+        const int st1 = stage == 2 ? 0 : stage + 1;
+        const uint16_t* A = smem + stage * S::STAGE;
+        uint16_t* An = smem + st1 * S::STAGE;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int h = p / TM, mi = p % TM;
+            const int q = p + kAD;
+            if (q < NP) read_af(A, q);
+            else read_af(An, q - NP);  // published by this step's barrier (q - NP < kAD <= 2 TM)
+#pragma unroll
+            for (int f = 0; f < kOmTN; ++f)
+                acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p % 4], __builtin_bit_cast(bf16x8_t, bfr[h & 1][f]),
+                                                                     acc[mi][f], 0, 0, 0);
+            // a share of the next k-chunk's B: words h + 1 of step j, or word 0 of step j+1
+#pragma unroll
+            for (int u = mi * PPC; u < (mi + 1) * PPC && u < 4 * kOmTN; ++u) {
+                const int f = u / 4, b = u % 4;
+                if (b == 0) om_split(h < 3 ? cw[cur][f][h + 1] : cw[nxt][f][0], ev[f], od[f]);
+                bfr[(h + 1) & 1][f][b] = om_pair(b, ev[f], od[f], ps[f], pc[f]);
+            }
+            if (p == 2 * TM - 1) {
+                // A of step j+1 to its stage (last read in step j-2), the loads of
+                // step j+2, then publish
+                store_a(An);
+                load_a(min(j + 2, NJ - 1));
+                __syncthreads();
+            }
+            if (p == 3 * TM - 1) {
+                // step j's words are all dequantised: request step j+2's; step
+                // j+1's parameters for k-chunk 3's share
+                load_b(cur, min(j + 2, NJ - 1));
+#pragma unroll
+                for (int f = 0; f < kOmTN; ++f) om_params(sb[nxt][f], zw[nxt][f], znib[f], ps[f], pc[f]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        stage = st1;
+    };
+    // two steps per trip so that the register buffers are addressed statically
+    int j = 0;
+    for (; j + 1 < NJ; j += 2) {
+        step(j, 0);
+        step(j + 1, 1);
+    }
+    if (j < NJ) step(j, 0);
+    __syncthreads();
+
+    // ---- epilogue: element 4 i + r of a lane's 32 x 32 tile is
+    // C[8 i + 4 (lane / 32) + r][lane % 32].  Each wave passes 32 rows at a
+    // time through its own LDS region (the A stages are free after the last
+    // barrier) as fp32 and writes whole 16-byte vectors of a row.
+    constexpr int LD = 64 + 4;  // floats per staged row
+    float* st = reinterpret_cast<float*>(smem) + wn * 32 * LD;
+    static_assert(S::SMEM * sizeof(uint16_t) >= 4 * 32 * LD * sizeof(float), "epilogue staging");
+    const int nrows = m1 - m0;
+    const int col = lane & 31;
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+        if (MODE == OM_GATEUP) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                st[(8 * (k >> 2) + 4 * g + (k & 3)) * LD + col] = silu(acc[mi][0][k]) * acc[mi][1][k];
+        } else {
+#pragma unroll
+            for (int f = 0; f < kOmTN; ++f)
+#pragma unroll
+                for (int k = 0; k < 16; ++k) st[(8 * (k >> 2) + 4 * g + (k & 3)) * LD + 32 * f + col] = acc[mi][f][k];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (MODE == OM_GATEUP) {
+            const int hcol = nt * (kOmBN / 2) + 32 * wn;
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {  // 16 rows x 4 chunks of 8 h columns
+                const int rr = pass * 16 + (lane >> 2), ch = lane & 3;
+                const int row = 32 * mi + rr;
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
+                if (row < nrows)
+                    *reinterpret_cast<uint4*>(&hbuf[(size_t)(m0 + row) * F + hcol + ch * 8]) =
+                        make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
+                                   pack_bf16x2(v1.z, v1.w));
+            }
+        } else if (a.out_f32) {
+            float* out = static_cast<float*>(a.rows);
+            const int ocol = nt * kOmBN + 64 * wn;
+#pragma unroll
+            for (int pass = 0; pass < 8; ++pass) {  // 4 rows x 16 chunks of 4 floats
+                const int rr = pass * 4 + (lane >> 4), ch = lane & 15;
+                const int row = 32 * mi + rr;
+                const float4 v = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 4]);
+                if (row < nrows) *reinterpret_cast<float4*>(&out[(size_t)(m0 + row) * H + ocol + ch * 4]) = v;
+            }
+        } else {
+            uint16_t* out = static_cast<uint16_t*>(a.rows);
+            const int ocol = nt * kOmBN + 64 * wn;
+#pragma unroll
+            for (int pass = 0; pass < 4; ++pass) {  // 8 rows x 8 chunks of 8 values
+                const int rr = pass * 8 + (lane >> 3), ch = lane & 7;
+                const int row = 32 * mi + rr;
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
+                if (row < nrows)
+                    *reinterpret_cast<uint4*>(&out[(size_t)(m0 + row) * H + ocol + ch * 8]) =
+                        make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
+                                   pack_bf16x2(v1.z, v1.w));
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// Output-major code words from AWQ codes: word w of column o of expert e holds
+// inputs 8w..8w+7, input 8w + j in nibble j.  One thread per output word.
+__global__ __launch_bounds__(256) void awq_to_om_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                                                        int E, int K, int N) {
+    const size_t words = (size_t)E * N * (K / 8);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x) {
+        const int w = (int)(i % (K / 8));
+        const size_t en = i / (K / 8);
+        const int n = (int)(en % N);
+        const size_t e = en / N;
+        const int sh = 4 * awq_nib(n & 7);
+        const uint32_t* s = src + (e * K + 8 * (size_t)w) * (N / 8) + n / 8;
+        uint32_t out = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) out |= ((s[(size_t)j * (N / 8)] >> sh) & 15u) << (4 * j);
+        dst[i] = out;
+    }
+}
+
+template <int TM>
+dim3 om_grid(int P, int E, int ntile) {
+    const long mt = (long)(P + 32 * TM - 1) / (32 * TM) + E;
+    return dim3((unsigned)((mt * ntile + kXcd - 1) / kXcd * kXcd));
+}
+
+template <int TM>
+void launch_om_tm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int E, hipStream_t s) {
+    const int NT1 = a.F / (kOmBN / 2), NT2 = a.H / kOmBN;
+    hipLaunchKernelGGL((om_gemm_kernel<OM_GATEUP, TM>), om_grid<TM>(a.P, E, NT1), dim3(kOmThreads), 0, s, a,
+                       tiles, hbuf, NT1);
+    hipLaunchKernelGGL((om_gemm_kernel<OM_DOWN, TM>), om_grid<TM>(a.P, E, NT2), dim3(kOmThreads), 0, s, a, tiles,
+                       hbuf, NT2);
+}
+
+// Rows per tile from the average rows per non-empty expert: one tile should
+// hold most experts whole.
+int om_pick_tm(int P, int E) {
+    const int active = P < E ? P : E;
+    const int avg = active > 0 ? P / active : 0;
+    return avg >= 192 ? 8 : avg >= 128 ? 6 : avg >= 96 ? 4 : avg >= 64 ? 3 : 2;
+}
+
+}  // namespace
+
+bool om_gemm_supported(int H, int F) { return H % kOmBN == 0 && F % (kOmBN / 2) == 0 && H % kOmKS == 0 && F % kOmKS == 0; }
+
+size_t om_gemm_ws_bytes(int P, int F, int E) { return tiles_bytes(P, E) + (size_t)P * F * sizeof(uint16_t); }
+
+hipError_t launch_om_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
+    const int E = a.offsets ? a.E : 1;
+    const int TM = om_pick_tm(a.P, E);
+    int32_t* tiles = static_cast<int32_t*>(ws);
+    uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + tiles_bytes(a.P, E));
+    launch_tile_table(a.offsets, E, a.P, 32 * TM, tiles, s);
+    switch (TM) {
+        case 8: launch_om_tm<8>(a, tiles, hbuf, E, s); break;
+        case 6: launch_om_tm<6>(a, tiles, hbuf, E, s); break;
+        case 4: launch_om_tm<4>(a, tiles, hbuf, E, s); break;
+        case 3: launch_om_tm<3>(a, tiles, hbuf, E, s); break;
+        default: launch_om_tm<2>(a, tiles, hbuf, E, s); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_awq_to_om(const int32_t* src, int32_t* dst, int E, int K, int N, hipStream_t s) {
+    const size_t words = (size_t)E * N * (K / 8);
+    if (words == 0) return hipSuccess;
+    size_t blocks = (words + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(awq_to_om_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const uint32_t*>(src),
+                       reinterpret_cast<uint32_t*>(dst), E, K, N);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -45,6 +45,32 @@ hipError_t launch_gemv(const GroupedArgs& a, void* ws, hipStream_t s);
 size_t gemm_ws_bytes(int P, int F, int E);
 hipError_t launch_gemm(const GroupedArgs& a, void* ws, hipStream_t s);
 
+// Tile table of a grouped GEMM (tiles[0] = count, then (expert, first row)
+// pairs, ceil(rows / BM) tiles per expert); tiles_bytes(P, E) bounds its size
+// for any BM >= 64.
+size_t tiles_bytes(int P, int E);
+void launch_tile_table(const int32_t* offsets, int E, int P, int BM, int32_t* tiles, hipStream_t s);
+
+// Workgroup b runs on XCD b % 8.  The grid is an upper bound on the work (the
+// tile count is only known on the device); the `total` real work items are
+// split into 8 contiguous ranges, XCD x taking range x with its lowest-numbered
+// workgroups, so every XCD gets an equal share and the surplus workgroups of
+// every XCD exit.  Returns -1 for a surplus workgroup.  Needs gridDim a
+// multiple of 8 and at least total rounded up to a multiple of 8.
+constexpr int kXcd = 8;
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+    const int q = (total + kXcd - 1) / kXcd;
+    const int x = b % kXcd, i = b / kXcd;
+    if (i >= q) return -1;
+    const int l = x * q + i;
+    return l < total ? l : -1;
+}
+
+// Grouped GEMM on AWQ g32 codes stored output-major (ffn_gemm_om.hip): h [P][F]
+// bf16 in the workspace after the tile table, then rows.
+size_t om_gemm_ws_bytes(int P, int F, int E);
+hipError_t launch_om_gemm(const GroupedArgs& a, void* ws, hipStream_t s);
+
 // Dense fp32 GEMM on the same kernels (used by the router's screening pass).
 size_t dense_gemm_ws_bytes(int M);
 hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t* B, int N, float* C,

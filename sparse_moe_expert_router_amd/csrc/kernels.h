@@ -41,7 +41,10 @@ struct FfnArgs {
     int out_f32;                  // 1: rows are fp32, else bf16
     void* rows;                   // [T*k][H]
 };
-size_t ffn_ws_bytes(int T, int k, int E, int H, int F, bool nvfp4);
+size_t ffn_ws_bytes(int T, int k, int E, int H, int F, int fmt);
+// hidden and inter sizes the output-major AWQ GEMM takes
+bool om_gemm_supported(int H, int F);
+hipError_t launch_awq_to_om(const int32_t* src, int32_t* dst, int E, int K, int N, hipStream_t s);
 
 // ---- NVFP4 activation quantisation (quant.hip)
 hipError_t launch_nvfp4_quantize(const uint16_t* x, int T, int n, float act_scale, uint16_t* out,

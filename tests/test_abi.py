@@ -183,3 +183,17 @@ def test_grouped_ffn_noalloc_validation():
     assert L.moe_grouped_ffn_noalloc(fake, -1, 10, ctypes.byref(b), fake, fake, 0, fake, None) == SHAPE
     assert L.moe_grouped_ffn_noalloc(fake, 16, 10, None, fake, fake, 0, fake, None) == NULL
     assert L.moe_grouped_ffn_noalloc(None, 0, 10, ctypes.byref(b), fake, fake, 0, None, None) == OK
+
+
+def test_awq_to_output_major_validation():
+    L = moe.lib()
+    src, dst = _bank(fmt=1, E=4, H=256, F=128), _bank(fmt=4, E=4, H=256, F=128)
+    assert L.moe_awq_to_output_major(None, ctypes.byref(dst), None) == NULL
+    assert L.moe_awq_to_output_major(ctypes.byref(dst), ctypes.byref(dst), None) == SHAPE   # src not AWQ
+    assert L.moe_awq_to_output_major(ctypes.byref(src), ctypes.byref(src), None) == SHAPE   # dst not AWQ_OM
+    assert L.moe_awq_to_output_major(ctypes.byref(src), ctypes.byref(_bank(fmt=4, E=5)), None) == SHAPE
+    # the output-major layout needs hidden % 256 and inter % 128
+    assert L.moe_awq_to_output_major(ctypes.byref(_bank(fmt=1, H=192, F=128)),
+                                     ctypes.byref(_bank(fmt=4, H=192, F=128)), None) == UNSUP
+    # codes that overlap are refused (the fake banks point every tensor at one address)
+    assert L.moe_awq_to_output_major(ctypes.byref(src), ctypes.byref(dst), None) == SHAPE

@@ -24,9 +24,14 @@ def _sample(n, T, seed):
     return np.sort(np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), n - 2, replace=False)]))
 
 
-@pytest.mark.parametrize("name", ["prefill_awq", "pruned_awq", "prefill_fp8", "prefill_nvfp4"])
+@pytest.mark.parametrize("name", ["prefill_awq", "pruned_awq", "prefill_fp8", "prefill_nvfp4",
+                                  "prefill_awq_om", "pruned_awq_om"])
 def test_fullsize_layer(name):
+    """Layers as bench.py runs them; the *_om cases convert the AWQ codes to the
+    output-major layout after slicing, as bench.py does for those workloads."""
     moe = require_gpu()
+    om = name.endswith("_om")
+    name = name[:-3] if om else name
     w = workloads.get(name)
     d = workloads.generate(w, device="cuda")
     wr, bank = d["router"], d["experts"]
@@ -42,6 +47,8 @@ def test_fullsize_layer(name):
             for a in ("qweight", "qzeros", "scales"):
                 np.testing.assert_array_equal(getattr(getattr(got, p), a), getattr(getattr(ref_bank, p), a))
         del got, ref_bank
+    if om:
+        bank = moe.awq_to_output_major(bank)
     y, mid = moe.moe_layer(d["x"], wr, w.k, bank, d["shared"], keep_intermediates=True)
     torch.cuda.synchronize()
     # every routing decision and the whole permutation
