@@ -34,8 +34,9 @@ size_t ffn_ws_bytes(int T, int k, int E, int H, int F, int fmt) {
     const size_t g1 = gemv_ws_bytes((int)Pg, H, F, 1), g0 = gemv_ws_bytes((int)Pg, H, F, 0);
     size_t need = g1 > g0 ? g1 : g0;
     if (F % 128 == 0 && H % 256 == 0 && P >= (long)kGemmMinRows * E) {
-        const size_t gm = gemm_ws_bytes((int)P, F, E);
+        const size_t gm = gemm_ws_bytes((int)P, F, E), om = om_gemm_ws_bytes((int)P, F, E);
         if (gm > need) need = gm;
+        if (om > need) need = om;  // bf16 banks run the register-B GEMM
     }
     return need;
 }
@@ -49,7 +50,7 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
     a.F = f.F;
     a.E = f.E;
     a.P = f.T * f.k;
-    a.awq = f.ex->gate.fmt == MOE_W_AWQ_G32;
+    a.awq = f.ex->gate.fmt == MOE_W_AWQ_G32 || f.ex->gate.fmt == MOE_W_AWQ_G32_OM;
     a.fp8 = f.ex->gate.fmt == MOE_W_FP8_BLOCK;
     a.nvfp4 = f.ex->gate.fmt == MOE_W_NVFP4;
     a.offsets = f.offsets;
@@ -81,7 +82,11 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
         ws = static_cast<char*>(ws) + quant_x_bytes(f.T, f.H);
     }
     if (f.ex->gate.fmt == MOE_W_AWQ_G32_OM) return launch_om_gemm(a, ws, s);
-    if (use_gemm(a.P, a.offsets ? a.E : 1, a.H, a.F)) return launch_gemm(a, ws, s);
+    if (use_gemm(a.P, a.offsets ? a.E : 1, a.H, a.F)) {
+        // bf16 weights go straight into registers on the register-B GEMM
+        if (f.ex->gate.fmt == MOE_W_BF16 && om_gemm_supported(a.H, a.F)) return launch_om_gemm(a, ws, s);
+        return launch_gemm(a, ws, s);
+    }
     return launch_gemv(a, ws, s);
 }
 

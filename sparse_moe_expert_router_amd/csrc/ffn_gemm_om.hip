@@ -31,21 +31,27 @@
 // fma(16 + q, s, -(16 + z) s) = (q - z) s exactly (5 x 11 bits), then one RNE
 // to bf16 for the MFMA.
 //
-// A (token rows gathered through sorted_pair, or h rows) goes global -> VGPR ->
-// LDS, three stages, one barrier a step.  LDS rows are 128 bytes (64 inputs);
-// the 16-byte chunk c of row r sits at chunk c ^ (r & 7), so the eight lanes of
-// a fragment read that hold eight consecutive rows at one chunk touch eight
-// different 16-byte bank groups, as do the eight lanes that store one row.
+// A (token rows gathered through sorted_pair, or h rows) goes from global
+// memory straight into LDS (16-byte buffer loads to LDS, two steps ahead),
+// four stages, one barrier a step.  LDS rows are 128 bytes (64 inputs), their
+// 16-byte chunks XOR-swizzled by row (om_swz).
+//
+// Row tiles: an expert's rows are split into ceil(rows / BM) tiles of equal
+// size (a multiple of 32), so that no tile is mostly padding.  (Skipping the
+// MFMAs of 32-row blocks past a tile's end with a branch inside the step
+// measured 14% slower than computing them.)
 //
 // Pipeline: a step is 4 TM pieces (k-chunk h = piece / TM, A fragment mi =
 // piece % TM), each 2 MFMAs plus a share of the dequantisation of the next
 // k-chunk's B words (k-chunk 3: step j+1's first), with the A fragment of the
 // piece three ahead read from LDS, across k-chunk and step boundaries.  After
-// k-chunk 1 of step j the A registers of step j+1 are stored to their LDS
-// stage, the A loads of step j+2 go out and one barrier publishes the stage, so
-// the last pieces of step j can already read step j+1's fragments; after
-// k-chunk 2 the B words of step j+2 are requested.  Loads use raw buffer resources: a per-lane 32-bit
+// k-chunk 1 of step j, once this wave's loads of step j+1's A have landed, one
+// barrier publishes that stage (so the last pieces of step j can already read
+// step j+1's fragments) and step j+3's A is requested into the stage step j-1
+// used; after k-chunk 2 the B words of step j+2 are requested.  Loads use raw buffer resources: a per-lane 32-bit
 // offset fixed for the whole loop plus a uniform step offset.
+#include <type_traits>
+
 #include "ffn_internal.h"
 
 namespace moe {
@@ -68,19 +74,16 @@ struct OmShape {
     static constexpr int STAGE = BM * kOmKS;     // bf16 elements per LDS stage
     // epilogue staging: 4 waves x 32 rows x (64 + 4) floats, in bf16 elements
     static constexpr int STG = 4 * 32 * (64 + 4) * 2;
-    static constexpr int SMEM = 3 * STAGE > STG ? 3 * STAGE : STG;
+    static constexpr int SMEM = 4 * STAGE > STG ? 4 * STAGE : STG;
 };
 
-// LDS row swizzle: the 16-byte chunk c of row r sits at chunk c ^ om_swz(r).
+// LDS row swizzle: the 16-byte chunk c of row r sits at chunk c ^ om_swz(r),
+// om_swz(r) = (r & 7) ^ ((r >> 3) & 1).  Eight consecutive rows then take eight
+// different chunks, and so do the eight even (or odd) rows of sixteen
+// consecutive rows, whether the LDS serves a 16-byte read 8 or 16 lanes at a
+// time (rocprofv3: SQ_LDS_BANK_CONFLICT 14x lower than with r & 7 alone).
 // om_swz(r + 32 i) == om_swz(r) for every i.
-#ifndef OM_SWZ
-#define OM_SWZ 3
-#endif
-__device__ __forceinline__ int om_swz(int r) {
-    if (OM_SWZ == 1) return (r >> 1) & 7;
-    if (OM_SWZ == 3) return (r & 7) ^ ((r >> 3) & 1);
-    return r & 7;
-}
+__device__ __forceinline__ int om_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // LDS element offset of 16-byte chunk c of row r (128-byte rows).
 __device__ __forceinline__ int om_lds(int r, int c) { return r * kOmKS + ((c ^ om_swz(r)) << 3); }
 
@@ -91,8 +94,8 @@ __device__ __forceinline__ int awq_nib(int c8) { return (c8 & 1) ? 4 + (c8 >> 1)
 // One code word (8 consecutive inputs) -> 8 bf16 (q - z) s, input i in element
 // i, in parts: om_split once, then om_pair(b) for the inputs 2b, 2b+1.
 __device__ __forceinline__ void om_split(uint32_t w, uint32_t& even, uint32_t& odd) {
-    even = ((w << 3) & 0x78787878u) | 0x80808080u;  // byte b: 1 q_{2b} 000
-    odd = ((w >> 1) & 0x78787878u) | 0x80808080u;   // byte b: 1 q_{2b+1} 000
+    even = and_or(w << 3, 0x78787878u, 0x80808080u);  // byte b: 1 q_{2b} 000
+    odd = and_or(w >> 1, 0x78787878u, 0x80808080u);   // byte b: 1 q_{2b+1} 000
 }
 __device__ __forceinline__ uint32_t om_pair(int b, uint32_t even, uint32_t odd, float s, float c) {
     const uint32_t sel = 0x07000C0Cu | ((uint32_t)b << 16);  // 0x41 | byte b | 0 | 0
@@ -116,19 +119,22 @@ __device__ __forceinline__ void om_params(uint32_t sbits, uint32_t zw, int znib,
     c = -(16.0f + z) * s;
 }
 
-template <int MODE, int TM>
+// WF: weight format, 1 = AWQ g32 codes output-major, 0 = bf16 [E][out][in]
+// (a lane's 8 inputs are 16 contiguous bytes of its weight row; no dequant).
+template <int MODE, int WF, int TM>
 __global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* __restrict__ hbuf, int NT) {
     using S = OmShape<TM>;
     constexpr int BM = S::BM, AP = S::AP;
+    constexpr bool W4 = WF == 1;
     __shared__ __attribute__((aligned(16))) uint16_t smem[S::SMEM];
 
     const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
     if (l < 0) return;
     const int tile = l / NT, nt = l % NT;
-    const int e = tiles[1 + 2 * tile];
-    const int m0 = tiles[2 + 2 * tile];
-    const int m1 = a.offsets ? min(m0 + BM, (int)a.offsets[e + 1]) : min(m0 + BM, a.P);
+    const int e = tiles[1 + 3 * tile];
+    const int m0 = tiles[2 + 3 * tile];
+    const int m1 = tiles[3 + 3 * tile];
 
     const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
     const int H = a.H, F = a.F;
@@ -139,17 +145,19 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     // ---- A: chunk q = tid + 256 i is row (tid >> 3) + 32 i, chunk tid & 7 of the step
     const rsrc_t ra = MODE == OM_GATEUP ? om_rsrc(a.x, (uint32_t)a.T * (uint32_t)H * 2u)
                                         : om_rsrc(hbuf, (uint32_t)a.P * (uint32_t)F * 2u);
-    uint32_t aoff[AP];  // byte offset of the chunk in step 0
+    // Load i of wave wn fills LDS slots 64 (4 i + wn) .. +63 of the stage (one
+    // 16-byte slot a lane): row r = 32 i + 8 wn + lane / 8, physical chunk
+    // lane & 7, so logical chunk (lane & 7) ^ om_swz(r) of that row.
+    uint32_t aoff[AP];  // byte offset of the lane's source chunk in step 0
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
-        const int r = (tid >> 3) + 32 * i;
+        const int r = 32 * i + 8 * wn + (lane >> 3);
         const int gr = min(m0 + r, m1 - 1);
         uint32_t row;
         if (MODE == OM_GATEUP) row = (uint32_t)(a.sorted_pair ? a.sorted_pair[gr] / a.k : gr);
         else row = (uint32_t)gr;
-        aoff[i] = row * (uint32_t)K * 2u + (uint32_t)((tid & 7) * 16);
+        aoff[i] = row * (uint32_t)K * 2u + (uint32_t)((((lane & 7) ^ om_swz(r))) * 16);
     }
-    const int a_st = om_lds(tid >> 3, tid & 7);  // LDS offset of chunk 0 (rows +32 i keep r & 7)
 
     // ---- B: fragment f of the wave (32 columns), lane column lane & 31,
     // lane group g = lane / 32.  Gate/up: fragment 0 reads the gate tensors,
@@ -157,27 +165,31 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     const int g = lane >> 5;
     const ProjDev& p0 = MODE == OM_GATEUP ? a.gate : a.down;
     const ProjDev& p1 = MODE == OM_GATEUP ? a.up : a.down;
-    const uint32_t qbytes = (uint32_t)a.E * (uint32_t)N * (uint32_t)(K / 2);
+    const uint32_t qbytes = W4 ? (uint32_t)a.E * (uint32_t)N * (uint32_t)(K / 2) : (uint32_t)a.E * (uint32_t)N * (uint32_t)K * 2u;
     const uint32_t sbytes = (uint32_t)a.E * (uint32_t)(K / 32) * (uint32_t)N * 2u;
     const uint32_t zbytes = sbytes / 4u;
-    const rsrc_t rq0 = om_rsrc(p0.qweight, qbytes), rq1 = om_rsrc(p1.qweight, qbytes);
-    const rsrc_t rs0 = om_rsrc(p0.scales, sbytes), rs1 = om_rsrc(p1.scales, sbytes);
-    const rsrc_t rz0 = om_rsrc(p0.qzeros, zbytes), rz1 = om_rsrc(p1.qzeros, zbytes);
-    uint32_t boff[kOmTN];   // byte offset of the lane's four code words in step 0
-    uint32_t soff[kOmTN];   // byte offset of its scale in step 0
-    uint32_t zoff[kOmTN];   // byte offset of its zero word in step 0
+    const rsrc_t rq0 = om_rsrc(W4 ? (const void*)p0.qweight : (const void*)p0.w, qbytes);
+    const rsrc_t rq1 = om_rsrc(W4 ? (const void*)p1.qweight : (const void*)p1.w, qbytes);
+    const rsrc_t rs0 = om_rsrc(p0.scales, W4 ? sbytes : 0u), rs1 = om_rsrc(p1.scales, W4 ? sbytes : 0u);
+    const rsrc_t rz0 = om_rsrc(p0.qzeros, W4 ? zbytes : 0u), rz1 = om_rsrc(p1.qzeros, W4 ? zbytes : 0u);
+    uint32_t boff[kOmTN];   // byte offset of the lane's B data in step 0
+    uint32_t soff[kOmTN];   // W4: byte offset of its scale in step 0
+    uint32_t zoff[kOmTN];   // W4: byte offset of its zero word in step 0
     int znib[kOmTN];
 #pragma unroll
     for (int f = 0; f < kOmTN; ++f) {
         const int col = MODE == OM_GATEUP ? nt * (kOmBN / 2) + 32 * wn + (lane & 31)
                                           : nt * kOmBN + 64 * wn + 32 * f + (lane & 31);
         const uint32_t grp0 = (uint32_t)e * (uint32_t)(K / 32) + (uint32_t)g;
-        boff[f] = (((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)(K / 8) + 4u * (uint32_t)g) * 4u;
+        const uint32_t row = (uint32_t)e * (uint32_t)N + (uint32_t)col;
+        boff[f] = W4 ? (row * (uint32_t)(K / 8) + 4u * (uint32_t)g) * 4u      // 4 code words
+                     : (row * (uint32_t)K + 32u * (uint32_t)g) * 2u;          // 32 bf16 inputs
         soff[f] = (grp0 * (uint32_t)N + (uint32_t)col) * 2u;
         zoff[f] = (grp0 * (uint32_t)(N / 8) + (uint32_t)(col >> 3)) * 4u;
         znib[f] = awq_nib(col & 7);
     }
     const uint32_t sstep = 4u * (uint32_t)N, zstep = (uint32_t)N;  // bytes per step (two groups)
+    const int bstep = W4 ? 32 : 2 * kOmKS;                          // B bytes per step and lane
 
     f32x16_t acc[TM][kOmTN];
 #pragma unroll
@@ -185,34 +197,49 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
 #pragma unroll
         for (int f = 0; f < kOmTN; ++f) acc[i][f] = f32x16_t{};
 
-    // raw B of two steps (buffer = step parity): four code words, scale bits, zero word
-    u32x4_t cw[2][kOmTN];
+    // W4: raw B of two steps (buffer = step parity): four code words, scale
+    // bits, zero word.  bf16: the current step's 4 k-chunks of B, each
+    // refilled with the next step's once its MFMAs have issued.
+    u32x4_t cw[W4 ? 2 : 1][kOmTN];
     uint32_t sb[2][kOmTN], zw[2][kOmTN];
+    u32x4_t braw[W4 ? 1 : 4][kOmTN];
     auto load_b = [&](int buf, int j) {
 #pragma unroll
         for (int f = 0; f < kOmTN; ++f) {
             const bool hi = MODE == OM_GATEUP && f == 1;
-            cw[buf][f] = __builtin_amdgcn_raw_buffer_load_b128(hi ? rq1 : rq0, (int)boff[f], j * 32, 0);
+            cw[buf][f] = __builtin_amdgcn_raw_buffer_load_b128(hi ? rq1 : rq0, (int)boff[f], j * bstep, 0);
             sb[buf][f] = __builtin_amdgcn_raw_buffer_load_b16(hi ? rs1 : rs0, (int)soff[f], (int)(sstep * (uint32_t)j), 0);
             zw[buf][f] = __builtin_amdgcn_raw_buffer_load_b32(hi ? rz1 : rz0, (int)zoff[f], (int)(zstep * (uint32_t)j), 0);
         }
     };
-    u32x4_t ar[AP];
-    auto load_a = [&](int j) {
+    auto load_braw = [&](int h, int j) {
 #pragma unroll
-        for (int i = 0; i < AP; ++i) ar[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)aoff[i], j * kOmKS * 2, 0);
+        for (int f = 0; f < kOmTN; ++f) {
+            const bool hi = MODE == OM_GATEUP && f == 1;
+            braw[W4 ? 0 : h][f] = __builtin_amdgcn_raw_buffer_load_b128(hi ? rq1 : rq0, (int)boff[f] + 16 * h, j * bstep, 0);
+        }
     };
-    auto store_a = [&](uint16_t* st) {
+    // A of step j straight into LDS stage st (buffer load to LDS: lane L's 16
+    // bytes land at the wave's base + 16 L)
+    auto load_a = [&](uint16_t* st, int j) {
 #pragma unroll
-        for (int i = 0; i < AP; ++i) *reinterpret_cast<u32x4_t*>(st + a_st + 32 * i * kOmKS) = ar[i];
+        for (int i = 0; i < AP; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(st + (4 * i + wn) * 512),
+                                                     16, (int)aoff[i], j * kOmKS * 2, 0, 0);
+    };
+    // wait until at most n vector-memory loads of this wave are outstanding
+    // (s_waitcnt: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
+    auto wait_vm = [](auto n) {
+        constexpr int v = decltype(n)::value;
+        __builtin_amdgcn_s_waitcnt((v & 15) | ((v >> 4) << 14) | 0x70 | 0xF00);
     };
     // A fragment (h, mi): row 32 mi + (lane & 31), logical chunk 4 g + h
     int afr[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) afr[h] = (lane & 31) * kOmKS + (((4 * g + h) ^ om_swz(lane & 31)) << 3);
 
-    u32x4_t bfr[2][kOmTN];        // dequantised B of two k-chunks (bf16 pairs)
-    float ps[kOmTN], pc[kOmTN];   // (s, c) of the step being dequantised
+    u32x4_t bfr[2][kOmTN];        // W4: dequantised B of two k-chunks (bf16 pairs)
+    float ps[kOmTN], pc[kOmTN];   // W4: (s, c) of the step being dequantised
     uint32_t ev[kOmTN], od[kOmTN];
 
     // A fragments of the pieces in flight: piece p uses af[p % 4]; the read of
@@ -225,30 +252,47 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
         af[q % 4] = *reinterpret_cast<const bf16x8_t*>(A + 32 * (q % TM) * kOmKS + afr[q / TM]);
     };
 
-    // ---- prologue: B of steps 0 and 1, A of step 0 in LDS stage 0, A of step 1
-    // in registers, k-chunk 0 of step 0 dequantised, the first fragments read
-    load_b(0, 0);
-    load_b(1, min(1, NJ - 1));
-    load_a(0);
-    store_a(smem);
-    load_a(min(1, NJ - 1));
+    // ---- prologue.  Vector-memory loads complete in issue order for the
+    // s_waitcnt counter, and each step issues them in one fixed order:
+    //   W4:   [mid step m: A(m+3)] [piece 3 TM - 1: B(m+2)]
+    //   bf16: [k-chunk h end: its B of step m+1] with A(m+3) at mid step
+    // so at the mid-step wait of step j at most 12 + TM loads issued after
+    // A(j+1) can be outstanding.  The prologue issues steps 0..2's loads in the
+    // order the two steps before step 0 would have, so that this holds from
+    // step 0 on.
+    auto stg = [&](int i) { return smem + i * S::STAGE; };
+    load_a(stg(0), 0);
+    load_a(stg(1), min(1, NJ - 1));
+    if (W4) {
+        load_b(0, 0);
+        load_a(stg(2), min(2, NJ - 1));
+        load_b(1, min(1, NJ - 1));
+        wait_vm(std::integral_constant<int, 12 + 2 * TM>{});   // A(0)
+    } else {
+        load_braw(0, 0);
+        load_braw(1, 0);
+        load_a(stg(2), min(2, NJ - 1));
+        load_braw(2, 0);
+        load_braw(3, 0);
+        wait_vm(std::integral_constant<int, 8 + 2 * TM>{});    // A(0)
+    }
+    if (W4) {
 #pragma unroll
-    for (int f = 0; f < kOmTN; ++f) {
-        om_params(sb[0][f], zw[0][f], znib[f], ps[f], pc[f]);
-        om_split(cw[0][f][0], ev[f], od[f]);
+        for (int f = 0; f < kOmTN; ++f) {
+            om_params(sb[0][f], zw[0][f], znib[f], ps[f], pc[f]);
+            om_split(cw[0][f][0], ev[f], od[f]);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) bfr[0][f][b] = om_pair(b, ev[f], od[f], ps[f], pc[f]);
+            for (int b = 0; b < 4; ++b) bfr[0][f][b] = om_pair(b, ev[f], od[f], ps[f], pc[f]);
+        }
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kAD; ++q) read_af(smem, q);
+    for (int q = 0; q < kAD; ++q) read_af(stg(0), q);
 
-    int stage = 0;  // LDS stage of step j
     auto step = [&](int j, int cur) {
         const int nxt = cur ^ 1;
-        const int st1 = stage == 2 ? 0 : stage + 1;
-        const uint16_t* A = smem + stage * S::STAGE;
-        uint16_t* An = smem + st1 * S::STAGE;
+        const uint16_t* A = stg(j & 3);
+        const uint16_t* An = stg((j + 1) & 3);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int h = p / TM, mi = p % TM;
@@ -256,24 +300,28 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
             if (q < NP) read_af(A, q);
             else read_af(An, q - NP);  // published by this step's barrier (q - NP < kAD <= 2 TM)
 #pragma unroll
-            for (int f = 0; f < kOmTN; ++f)
-                acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p % 4], __builtin_bit_cast(bf16x8_t, bfr[h & 1][f]),
-                                                                     acc[mi][f], 0, 0, 0);
-            // a share of the next k-chunk's B: words h + 1 of step j, or word 0 of step j+1
+                for (int f = 0; f < kOmTN; ++f)
+                    acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[p % 4], __builtin_bit_cast(bf16x8_t, W4 ? bfr[h & 1][f] : braw[W4 ? 0 : h][f]), acc[mi][f], 0, 0, 0);
+            if (W4) {
+                // a share of the next k-chunk's B: words h + 1 of step j, or word 0 of step j+1
 #pragma unroll
-            for (int u = mi * PPC; u < (mi + 1) * PPC && u < 4 * kOmTN; ++u) {
-                const int f = u / 4, b = u % 4;
-                if (b == 0) om_split(h < 3 ? cw[cur][f][h + 1] : cw[nxt][f][0], ev[f], od[f]);
-                bfr[(h + 1) & 1][f][b] = om_pair(b, ev[f], od[f], ps[f], pc[f]);
+                for (int u = mi * PPC; u < (mi + 1) * PPC && u < 4 * kOmTN; ++u) {
+                    const int f = u / 4, b = u % 4;
+                    if (b == 0) om_split(h < 3 ? cw[cur][f][h + 1] : cw[W4 ? nxt : 0][f][0], ev[f], od[f]);
+                    bfr[(h + 1) & 1][f][b] = om_pair(b, ev[f], od[f], ps[f], pc[f]);
+                }
+            } else if (mi == TM - 1) {
+                load_braw(h, min(j + 1, NJ - 1));  // k-chunk h of step j+1 into the registers just used
             }
             if (p == 2 * TM - 1) {
-                // A of step j+1 to its stage (last read in step j-2), the loads of
-                // step j+2, then publish
-                store_a(An);
-                load_a(min(j + 2, NJ - 1));
+                // A(j+1) has landed in its stage: publish it, then request A(j+3)
+                // into the stage step j-1 used (every wave is past step j-1 here)
+                wait_vm(std::integral_constant<int, 12 + TM>{});
                 __syncthreads();
+                load_a(stg((j + 3) & 3), min(j + 3, NJ - 1));
             }
-            if (p == 3 * TM - 1) {
+            if (W4 && p == 3 * TM - 1) {
                 // step j's words are all dequantised: request step j+2's; step
                 // j+1's parameters for k-chunk 3's share
                 load_b(cur, min(j + 2, NJ - 1));
@@ -282,7 +330,6 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        stage = st1;
     };
     // two steps per trip so that the register buffers are addressed statically
     int j = 0;
@@ -291,6 +338,8 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
         step(j + 1, 1);
     }
     if (j < NJ) step(j, 0);
+    // no load may still be writing a stage when the epilogue reuses the LDS
+    wait_vm(std::integral_constant<int, 0>{});
     __syncthreads();
 
     // ---- epilogue: element 4 i + r of a lane's 32 x 32 tile is
@@ -361,6 +410,41 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     }
 }
 
+// Tile table: tiles[0] = number of tiles, then (expert, first row, end row)
+// triples.  An expert with n rows gets t = ceil(n / BM) tiles of equal size
+// ceil(n / t) rounded up to 32 (the last one shorter).
+__global__ __launch_bounds__(1024) void om_tile_table_kernel(const int32_t* __restrict__ offsets, int E, int P, int BM,
+                                                             int32_t* __restrict__ tiles) {
+    __shared__ int scan[1024];
+    const int e = threadIdx.x;
+    int cnt = 0, r0 = 0;
+    if (offsets) {
+        if (e < E) {
+            r0 = offsets[e];
+            cnt = offsets[e + 1] - r0;
+        }
+    } else if (e == 0) {
+        cnt = P;
+    }
+    const int nt = (cnt + BM - 1) / BM;
+    const int sz = nt ? ((cnt + nt - 1) / nt + 31) / 32 * 32 : 0;
+    scan[e] = nt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int v = e >= off ? scan[e - off] : 0;
+        __syncthreads();
+        scan[e] += v;
+        __syncthreads();
+    }
+    const int start = scan[e] - nt;
+    for (int i = 0; i < nt; ++i) {
+        tiles[1 + 3 * (start + i)] = e;
+        tiles[2 + 3 * (start + i)] = r0 + i * sz;
+        tiles[3 + 3 * (start + i)] = min(r0 + (i + 1) * sz, r0 + cnt);
+    }
+    if (e == 1023) tiles[0] = scan[1023];
+}
+
 // Output-major code words from AWQ codes: word w of column o of expert e holds
 // inputs 8w..8w+7, input 8w + j in nibble j.  One thread per output word.
 __global__ __launch_bounds__(256) void awq_to_om_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
@@ -386,13 +470,26 @@ dim3 om_grid(int P, int E, int ntile) {
     return dim3((unsigned)((mt * ntile + kXcd - 1) / kXcd * kXcd));
 }
 
-template <int TM>
-void launch_om_tm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int E, hipStream_t s) {
+template <int WF, int TM>
+void launch_om_tm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int E, bool gateup, hipStream_t s) {
     const int NT1 = a.F / (kOmBN / 2), NT2 = a.H / kOmBN;
-    hipLaunchKernelGGL((om_gemm_kernel<OM_GATEUP, TM>), om_grid<TM>(a.P, E, NT1), dim3(kOmThreads), 0, s, a,
-                       tiles, hbuf, NT1);
-    hipLaunchKernelGGL((om_gemm_kernel<OM_DOWN, TM>), om_grid<TM>(a.P, E, NT2), dim3(kOmThreads), 0, s, a, tiles,
-                       hbuf, NT2);
+    if (gateup)
+        hipLaunchKernelGGL((om_gemm_kernel<OM_GATEUP, WF, TM>), om_grid<TM>(a.P, E, NT1), dim3(kOmThreads), 0, s,
+                           a, tiles, hbuf, NT1);
+    hipLaunchKernelGGL((om_gemm_kernel<OM_DOWN, WF, TM>), om_grid<TM>(a.P, E, NT2), dim3(kOmThreads), 0, s, a,
+                       tiles, hbuf, NT2);
+}
+
+template <int WF>
+void launch_om_wf(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int E, int TM, bool gateup,
+                  hipStream_t s) {
+    switch (TM) {
+        case 8: launch_om_tm<WF, 8>(a, tiles, hbuf, E, gateup, s); break;
+        case 6: launch_om_tm<WF, 6>(a, tiles, hbuf, E, gateup, s); break;
+        case 4: launch_om_tm<WF, 4>(a, tiles, hbuf, E, gateup, s); break;
+        case 3: launch_om_tm<WF, 3>(a, tiles, hbuf, E, gateup, s); break;
+        default: launch_om_tm<WF, 2>(a, tiles, hbuf, E, gateup, s); break;
+    }
 }
 
 // Rows per tile from the average rows per non-empty expert: one tile should
@@ -407,21 +504,19 @@ int om_pick_tm(int P, int E) {
 
 bool om_gemm_supported(int H, int F) { return H % kOmBN == 0 && F % (kOmBN / 2) == 0 && H % kOmKS == 0 && F % kOmKS == 0; }
 
-size_t om_gemm_ws_bytes(int P, int F, int E) { return tiles_bytes(P, E) + (size_t)P * F * sizeof(uint16_t); }
+// Tile table bytes: at most P / 64 + E tiles (BM >= 64) of 3 ints, plus the count.
+static size_t om_tiles_bytes(int P, int E) { return (((size_t)(1 + 3 * ((P + 63) / 64 + E)) * sizeof(int32_t)) + 255) & ~(size_t)255; }
+
+size_t om_gemm_ws_bytes(int P, int F, int E) { return om_tiles_bytes(P, E) + (size_t)P * F * sizeof(uint16_t); }
 
 hipError_t launch_om_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
     const int E = a.offsets ? a.E : 1;
     const int TM = om_pick_tm(a.P, E);
     int32_t* tiles = static_cast<int32_t*>(ws);
-    uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + tiles_bytes(a.P, E));
-    launch_tile_table(a.offsets, E, a.P, 32 * TM, tiles, s);
-    switch (TM) {
-        case 8: launch_om_tm<8>(a, tiles, hbuf, E, s); break;
-        case 6: launch_om_tm<6>(a, tiles, hbuf, E, s); break;
-        case 4: launch_om_tm<4>(a, tiles, hbuf, E, s); break;
-        case 3: launch_om_tm<3>(a, tiles, hbuf, E, s); break;
-        default: launch_om_tm<2>(a, tiles, hbuf, E, s); break;
-    }
+    uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + om_tiles_bytes(a.P, E));
+    hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TM, tiles);
+    if (a.awq) launch_om_wf<1>(a, tiles, hbuf, E, TM, true, s);
+    else launch_om_wf<0>(a, tiles, hbuf, E, TM, true, s);
     return hipGetLastError();
 }
 
