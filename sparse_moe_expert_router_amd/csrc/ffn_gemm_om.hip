@@ -13,7 +13,8 @@
 // from HBM straight into registers and is dequantised there; no B tile passes
 // through LDS.
 //
-// Workgroup: 256 threads, 4 waves (one per SIMD).  Tile: BM = 32 TM rows x
+// Workgroup: 256 threads, 4 waves (one per SIMD; two workgroups per compute
+// unit for tiles of up to 128 rows).  Tile: BM = 32 TM rows x
 // 256 B-columns (gate/up: 128 gate columns and the same 128 up columns; down:
 // 256 output columns); wave w takes all BM rows x its 64 B-columns (gate/up:
 // 32 gate + the matching 32 up columns, so SwiGLU is applied in registers),
@@ -72,6 +73,9 @@ struct OmShape {
     static constexpr int BM = 32 * TM;           // rows per tile
     static constexpr int AP = TM;                // 16-byte A chunks per thread per step
     static constexpr int STAGE = BM * kOmKS;     // bf16 elements per LDS stage
+    // waves per SIMD: tiles up to 128 rows keep their accumulators in VGPRs
+    // (at most 256 registers a lane) and run two workgroups per compute unit
+    static constexpr int MINW = TM <= 4 ? 2 : 1;
     // epilogue staging: 4 waves x 32 rows x (64 + 4) floats, in bf16 elements
     static constexpr int STG = 4 * 32 * (64 + 4) * 2;
     static constexpr int SMEM = 4 * STAGE > STG ? 4 * STAGE : STG;
@@ -122,7 +126,7 @@ __device__ __forceinline__ void om_params(uint32_t sbits, uint32_t zw, int znib,
 // WF: weight format, 1 = AWQ g32 codes output-major, 0 = bf16 [E][out][in]
 // (a lane's 8 inputs are 16 contiguous bytes of its weight row; no dequant).
 template <int MODE, int WF, int TM>
-__global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(OmShape<TM>::MINW, OmShape<TM>::MINW)))
 void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* __restrict__ hbuf, int NT) {
     using S = OmShape<TM>;
     constexpr int BM = S::BM, AP = S::AP;
@@ -470,25 +474,21 @@ dim3 om_grid(int P, int E, int ntile) {
     return dim3((unsigned)((mt * ntile + kXcd - 1) / kXcd * kXcd));
 }
 
-template <int WF, int TM>
-void launch_om_tm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int E, bool gateup, hipStream_t s) {
-    const int NT1 = a.F / (kOmBN / 2), NT2 = a.H / kOmBN;
-    if (gateup)
-        hipLaunchKernelGGL((om_gemm_kernel<OM_GATEUP, WF, TM>), om_grid<TM>(a.P, E, NT1), dim3(kOmThreads), 0, s,
-                           a, tiles, hbuf, NT1);
-    hipLaunchKernelGGL((om_gemm_kernel<OM_DOWN, WF, TM>), om_grid<TM>(a.P, E, NT2), dim3(kOmThreads), 0, s, a,
-                       tiles, hbuf, NT2);
+template <int MODE, int WF, int TM>
+void launch_om_tm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int E, hipStream_t s) {
+    const int NT = MODE == OM_GATEUP ? a.F / (kOmBN / 2) : a.H / kOmBN;
+    hipLaunchKernelGGL((om_gemm_kernel<MODE, WF, TM>), om_grid<TM>(a.P, E, NT), dim3(kOmThreads), 0, s, a, tiles,
+                       hbuf, NT);
 }
 
-template <int WF>
-void launch_om_wf(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int E, int TM, bool gateup,
-                  hipStream_t s) {
+template <int MODE, int WF>
+void launch_om_wf(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int E, int TM, hipStream_t s) {
     switch (TM) {
-        case 8: launch_om_tm<WF, 8>(a, tiles, hbuf, E, gateup, s); break;
-        case 6: launch_om_tm<WF, 6>(a, tiles, hbuf, E, gateup, s); break;
-        case 4: launch_om_tm<WF, 4>(a, tiles, hbuf, E, gateup, s); break;
-        case 3: launch_om_tm<WF, 3>(a, tiles, hbuf, E, gateup, s); break;
-        default: launch_om_tm<WF, 2>(a, tiles, hbuf, E, gateup, s); break;
+        case 8: launch_om_tm<MODE, WF, 8>(a, tiles, hbuf, E, s); break;
+        case 6: launch_om_tm<MODE, WF, 6>(a, tiles, hbuf, E, s); break;
+        case 4: launch_om_tm<MODE, WF, 4>(a, tiles, hbuf, E, s); break;
+        case 3: launch_om_tm<MODE, WF, 3>(a, tiles, hbuf, E, s); break;
+        default: launch_om_tm<MODE, WF, 2>(a, tiles, hbuf, E, s); break;
     }
 }
 
@@ -507,16 +507,28 @@ bool om_gemm_supported(int H, int F) { return H % kOmBN == 0 && F % (kOmBN / 2) 
 // Tile table bytes: at most P / 64 + E tiles (BM >= 64) of 3 ints, plus the count.
 static size_t om_tiles_bytes(int P, int E) { return (((size_t)(1 + 3 * ((P + 63) / 64 + E)) * sizeof(int32_t)) + 255) & ~(size_t)255; }
 
-size_t om_gemm_ws_bytes(int P, int F, int E) { return om_tiles_bytes(P, E) + (size_t)P * F * sizeof(uint16_t); }
+size_t om_gemm_ws_bytes(int P, int F, int E) { return 2 * om_tiles_bytes(P, E) + (size_t)P * F * sizeof(uint16_t); }
 
 hipError_t launch_om_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
     const int E = a.offsets ? a.E : 1;
-    const int TM = om_pick_tm(a.P, E);
+    // gate/up: the row tile that holds most experts whole; down (K = inter,
+    // few steps per tile): at most 128 rows, two workgroups per compute unit,
+    // so that one tile's prologue and epilogue overlap another's main loop
+    const int TMG = om_pick_tm(a.P, E);
+    const int TMD = TMG > 4 ? 4 : TMG;
     int32_t* tiles = static_cast<int32_t*>(ws);
-    uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + om_tiles_bytes(a.P, E));
-    hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TM, tiles);
-    if (a.awq) launch_om_wf<1>(a, tiles, hbuf, E, TM, true, s);
-    else launch_om_wf<0>(a, tiles, hbuf, E, TM, true, s);
+    int32_t* tiles_d = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + om_tiles_bytes(a.P, E));
+    uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + 2 * om_tiles_bytes(a.P, E));
+    hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TMG, tiles);
+    if (TMD != TMG) hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TMD, tiles_d);
+    else tiles_d = tiles;
+    if (a.awq) {
+        launch_om_wf<OM_GATEUP, 1>(a, tiles, hbuf, E, TMG, s);
+        launch_om_wf<OM_DOWN, 1>(a, tiles_d, hbuf, E, TMD, s);
+    } else {
+        launch_om_wf<OM_GATEUP, 0>(a, tiles, hbuf, E, TMG, s);
+        launch_om_wf<OM_DOWN, 0>(a, tiles_d, hbuf, E, TMD, s);
+    }
     return hipGetLastError();
 }
 
