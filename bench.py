@@ -2,9 +2,10 @@
 """Throughput of the MoE feed-forward layer on one MI355X.
 
 A step is one pass of the whole layer over one batch of seeded synthetic
-input resident in HBM: route and permute (one call) -> routed experts -> combine, with the
-shared expert on a second stream beside them (for the Refill-RMS workload: route with the 11th expert -> permute ->
-routed experts (fp32 rows) -> refill score -> keep-set).  Steps cycle through
+input resident in HBM: one moe_layer call (route and permute -> routed
+experts -> combine, with the shared expert on a side stream beside them); for
+the Refill-RMS workload: route with the 11th expert -> permute -> routed
+experts (fp32 rows) -> refill score -> keep-set.  Steps cycle through
 several independently generated weight copies so that the weights do not stay
 in the 256 MB on-die cache between steps.
 
@@ -35,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + HBM GB/s (decode) / MFMA TFLOP/s (prefill), % of peak"
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+EV_EVERY = 8                 # timed steps between two recorded pairs of routed-call events
 
 # bytes of one expert's weights (gate + up + down)
 def expert_bytes(w, fmt):
@@ -69,14 +71,18 @@ def parse():
                    help="target wall time of the oracle CPU-baseline sample (0 disables it)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--graph", choices=["on", "off"], default="off",
-                   help="replay each step from HIP graphs ([route, permute], [routed experts], "
-                        "[combine]; the shared expert stays on its side stream)")
+                   help="replay each layer step from one HIP graph (captured moe_layer call, side "
+                        "stream included)")
+    p.add_argument("--shared-stream", choices=["on", "off"], default="on",
+                   help="run the shared expert on a side stream beside the routed path (on) or on "
+                        "the main stream before it (off)")
     p.add_argument("--secondary", default="decode_awq",
                    help="a second workload measured in the same process ('none' skips it)")
     p.add_argument("--secondary-steps", type=int, default=200)
-    p.add_argument("--awq-layout", choices=["auto", "awq", "om"], default="auto",
-                   help="AWQ code layout: auto = output-major (converted at setup) when the layer sees "
-                        ">= 32 rows per expert, else the AWQ layout")
+    p.add_argument("--awq-layout", choices=["om", "awq"], default="om",
+                   help="AWQ code layout: om = output-major (converted once at setup; the MFMA GEMV "
+                        "for decode batches, the MFMA GEMM for prefill), awq = the AWQ GEMM packing as "
+                        "stored (its streaming GEMV for decode; prefill-sized calls run the older GEMM)")
     return p.parse_args()
 
 
@@ -94,15 +100,12 @@ def roofline(bytes_, flops, ms):
 
 
 def use_output_major(w, layout):
-    """AWQ banks run on output-major codes (converted once at setup) when the
-    layer sees many rows per expert; decode batches keep the AWQ layout, whose
-    streaming kernels read it directly."""
-    if w.fmt != "awq" or layout == "awq":
-        return False
-    return layout == "om" or w.T * w.k >= 32 * w.E
+    """AWQ banks run on output-major codes (converted once at setup) unless
+    the AWQ layout is asked for."""
+    return w.fmt == "awq" and layout == "om"
 
 
-def measure(moe, w, steps, warmup, copies_arg, seed, graph, layout="auto"):
+def measure(moe, w, steps, warmup, copies_arg, seed, graph, layout="om", side_stream=True):
     """Times `steps` layer steps of workload `w` (after `warmup` untimed ones).
     Returns the figures of the JSON line and the first weight copy's inputs."""
     import numpy as np
@@ -128,13 +131,19 @@ def measure(moe, w, steps, warmup, copies_arg, seed, graph, layout="auto"):
     torch.cuda.synchronize()
     ws = moe.Workspace(dev)
     stream = torch.cuda.current_stream()
-    # the shared expert needs only x: it runs on a second stream (default
-    # priority) beside routing and the routed experts, with its own workspace
-    side, side_ws = torch.cuda.Stream(dev), moe.Workspace(dev)
+    # the shared expert needs only x: moe_layer runs it on a side stream
+    # (default priority) beside routing and the routed experts
+    side = torch.cuda.Stream(dev)
 
     if w.refill:
         stats = [(torch.zeros(w.E, dtype=torch.float32, device=dev),
                   torch.zeros(w.E, dtype=torch.int32, device=dev)) for _ in sets]
+
+    calls = []
+    if not w.refill:
+        for d in sets:
+            calls.append(moe.LayerCall(d["x"], d["router"], w.k, d["experts"], d["shared"],
+                                       side_stream=side if side_stream else None, ws=ws))
 
     def step(i, ev=None):
         d = sets[i % copies]
@@ -149,34 +158,28 @@ def measure(moe, w, steps, warmup, copies_arg, seed, graph, layout="auto"):
             moe.refill_score(rows, off, sp, p2r, tl, s, c, ws=ws)
             moe.refill_finalize(s, c, w.H, w.keep)
             return idx
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            s = moe.grouped_ffn(x, 1, d["shared"], ws=side_ws)
-        idx, tl, gate, off, sp, p2r = moe.route_permute(x, d["router"], w.k, ws=ws)
-        if ev: ev[0].record(stream)
-        rows = moe.grouped_ffn(x, w.k, d["experts"], off, sp, ws=ws)
-        if ev: ev[1].record(stream)
-        stream.wait_stream(side)
-        s.record_stream(stream)
-        moe.combine(rows, p2r, gate, s)
-        return idx
+        return calls[i % copies](ev)
 
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:  # torch creates the HIP events on first record; the library records them
+        a.record(stream)
+        b.record(stream)
     if graph:
-        step = graph_steps(moe, w, sets, ws, side, side_ws, stream, step)
+        step = graph_steps(w, calls, evs, step)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, evs[i])
+        # the routed-call events are recorded on every EV_EVERY-th step only:
+        # an event record costs the stream a few microseconds of idle time
+        step(i, evs[i] if i % EV_EVERY == 0 else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
-    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ffn_ms = float(np.mean([a.elapsed_time(b) for i, (a, b) in enumerate(evs) if i % EV_EVERY == 0]))
     ms_per_step = 1e3 * elapsed / steps
 
     # ---- algorithmic work of the dominant call (routed grouped experts), per call
@@ -220,6 +223,7 @@ def measure(moe, w, steps, warmup, copies_arg, seed, graph, layout="auto"):
               "experts_base": w.E_base or w.E, "top_k": w.k, "expert_width": w.F,
               "shared_width": w.Fs, "weights": w.fmt, "weight_copies": copies,
               "touched_experts": n_touched, "hip_graphs": bool(graph),
+              "shared_expert_stream": ("side" if side_stream else "main") if not w.refill else None,
               "awq_codes": ("output-major" if use_output_major(w, layout) else "awq") if w.fmt == "awq" else None}
     out = {"value": round(w.T * steps / elapsed, 1), "ms_per_step": round(ms_per_step, 4),
            "config": config, "roofline": roof, "layer_roofline": layer}
@@ -244,7 +248,7 @@ def main():
     moe.lib()
 
     main_fig, first = measure(moe, w, args.steps, args.warmup, args.copies, args.seed, args.graph == "on",
-                              args.awq_layout)
+                              args.awq_layout, args.shared_stream == "on")
     result = {"metric": METRIC, "value": main_fig["value"], "unit": "tokens/s", "n_gpus": 1,
               "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_fig["ms_per_step"],
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -258,7 +262,8 @@ def main():
     # ---- the 16-token W4A16 decode layer, in the same process
     if args.secondary != "none" and args.secondary != w.name:
         sw = workloads.get(args.secondary)
-        sec, _ = measure(moe, sw, args.secondary_steps, args.warmup, 0, args.seed, False, args.awq_layout)
+        sec, _ = measure(moe, sw, args.secondary_steps, args.warmup, 0, args.seed, False, args.awq_layout,
+                         args.shared_stream == "on")
         torch.cuda.empty_cache()
         result["secondary"] = {"workload": sw.name, "steps": args.secondary_steps,
                                "tokens_per_s": sec["value"], "ms_per_step": sec["ms_per_step"],
@@ -271,45 +276,35 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def graph_steps(moe, w, sets, ws, side, side_ws, stream, eager_step):
-    """Steps replayed from HIP graphs, one set per weight copy: [route and permute],
-    [routed experts], [combine] captured separately so that the HIP events
-    around the routed call are recorded between replays.  The shared expert
-    runs on the side stream as in the eager step.  Capture happens after an
-    eager pass, so every workspace already has its final size."""
+def graph_steps(w, calls, evs, eager_step):
+    """Steps replayed from HIP graphs: one captured moe_layer call (side
+    stream and routed-call events included) per weight copy and timing slot.
+    Capture follows an eager pass, so the workspace has its final size."""
     import torch
-    for i in range(len(sets)):
+    if w.refill:
+        raise ValueError("the Refill-RMS pass is not replayed from graphs")
+    for i in range(len(calls)):
         eager_step(i)
     torch.cuda.synchronize()
-    graphs = []
-    for d in sets:
-        x = d["x"]
-        if w.refill:
-            raise ValueError("the Refill-RMS pass is not replayed from graphs")
-        s_buf = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=x.device)
-        g1, g2, g3 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g1):
-            idx, tl, gate, off, sp, p2r = moe.route_permute(x, d["router"], w.k, ws=ws)
-        with torch.cuda.graph(g2):
-            rows = moe.grouped_ffn(x, w.k, d["experts"], off, sp, ws=ws)
-        with torch.cuda.graph(g3):
-            y = moe.combine(rows, p2r, gate, s_buf)
-        graphs.append((g1, g2, g3, s_buf, (idx, tl, gate, off, sp, p2r, rows, y)))
+    graphs = {}
+
+    def get(i, ev):
+        key = (i % len(calls), None if ev is None else id(ev))
+        if key not in graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                calls[key[0]](ev)
+            graphs[key] = g
+        return graphs[key]
+
+    for i in range(len(evs)):  # capture every (copy, events) pair before timing
+        get(i, evs[i])
+    for i in range(len(calls)):
+        get(i, None)
     torch.cuda.synchronize()
 
     def step(i, ev=None):
-        d = sets[i % len(sets)]
-        g1, g2, g3, s_buf, keep = graphs[i % len(sets)]
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            moe.grouped_ffn(d["x"], 1, d["shared"], ws=side_ws, rows=s_buf)
-        g1.replay()
-        if ev: ev[0].record(stream)
-        g2.replay()
-        if ev: ev[1].record(stream)
-        stream.wait_stream(side)
-        g3.replay()
-        return keep[0]
+        get(i, ev).replay()
     return step
 
 

@@ -24,11 +24,13 @@
  *    On any error nothing is enqueued and the status says why.  A failed
  *    launch returns MOE_ERR_HIP; moe_last_hip_error() then gives the
  *    hipError_t of the calling thread's last failed HIP call.
- *  - The library never allocates device memory and keeps no state between
- *    calls except cached device properties.  The caller owns every buffer,
- *    including the scratch workspace `ws` whose size comes from
- *    moe_workspace_bytes().  Calls on different streams need distinct
- *    workspaces.
+ *  - The library never allocates device memory (moe_grouped_ffn_noalloc's
+ *    static array aside) and keeps no state between calls except cached
+ *    device properties and, for moe_layer with a side stream, two HIP events
+ *    per calling thread and device.  The caller owns every buffer, including
+ *    the scratch workspace `ws` whose size comes from moe_workspace_bytes()
+ *    or moe_layer_workspace_bytes().  Calls on different streams need
+ *    distinct workspaces.
  *  - Results are deterministic: the same inputs give the same bits.
  *  - T = 0 is a valid no-op for every call.
  *
@@ -229,6 +231,47 @@ moe_status moe_grouped_ffn_noalloc(const uint16_t *x, int32_t T, int32_t k, cons
 
 /* Bytes of the per-GPU scratch array of moe_grouped_ffn_noalloc. */
 size_t moe_grouped_ffn_noalloc_max_bytes(void);
+
+/*
+ * The whole MoE feed-forward layer of one batch in one call (architecture
+ * sheet, FFN / MoE entries: router top-k with renormalised gates, routed
+ * SwiGLU experts, the always-on shared expert, gate-weighted sum):
+ *   y = moe_combine(rows, pair_to_row, topk_gate, shared(x), shared_scale)
+ * where rows = moe_grouped_ffn(x, k, experts, ...) (bf16 rows) over the
+ * permutation that moe_route_permute(x, w_router, ...) gives.  The results
+ * are bit-identical to those four calls made one after the other; the call
+ * exists so that a decode step costs one host call instead of four and the
+ * small steps between the kernels can be merged (for decode-sized batches
+ * the selection kernel also builds the routed call's work table).
+ *   x [T][H] bf16, w_router [E][H] bf16 with E = experts->num_experts and
+ *   H = experts->hidden, y [T][H] bf16 (may not overlap x).  experts and
+ *   shared are HOST pointers to structs of device pointers; shared (nullable)
+ *   must hold one expert of hidden H (any format, any inter); shared_scale
+ *   (nullable, [T] fp32) needs shared.  topk_idx (nullable, [T][k] int32)
+ *   also receives the routing decisions.
+ *   side_stream (nullable): a hipStream_t other than `stream` on which the
+ *   shared expert runs beside the routed path (it waits for the work already
+ *   on `stream`, and `stream` waits for it before the combine); NULL runs
+ *   everything on `stream`.  The fork and join use two events per calling
+ *   thread and device, created on the first such call.
+ *   routed_events (nullable, HOST array of two hipEvent_t): recorded on
+ *   `stream` right before and right after the routed grouped-expert call,
+ *   for timing it inside the layer; either entry may be NULL.
+ *   ws: moe_layer_workspace_bytes(T, k, experts, shared) bytes, 16-byte
+ *   aligned; it holds every intermediate (routing, permutation, rows).
+ * Requirements and errors: those of the four calls; k <= min(E, 64);
+ * side_stream == stream or a shared bank with more than one expert or a
+ * different hidden size -> MOE_ERR_SHAPE.
+ */
+moe_status moe_layer(const uint16_t *x, int32_t T, const uint16_t *w_router, int32_t k,
+                     const moe_experts *experts, const moe_experts *shared, const float *shared_scale,
+                     uint16_t *y, int32_t *topk_idx, void *ws, size_t ws_bytes, void *stream,
+                     void *side_stream, void *const *routed_events);
+
+/* Workspace bytes of moe_layer (0 for T <= 0 or an invalid bank).  Grows
+ * with T; a workspace sized for the largest T serves every smaller call. */
+size_t moe_layer_workspace_bytes(int32_t T, int32_t k, const moe_experts *experts,
+                                 const moe_experts *shared);
 
 /*
  * Weighted combine (architecture sheet: routed outputs weighted by the

@@ -34,7 +34,8 @@ W_BF16, W_AWQ, W_FP8, W_NVFP4, W_AWQ_OM = 0, 1, 2, 3, 4
 OUT_BF16, OUT_F32 = 0, 1
 
 EXPORTS = ["moe_route", "moe_permute", "moe_route_permute", "moe_grouped_ffn", "moe_grouped_ffn_noalloc",
-           "moe_grouped_ffn_noalloc_max_bytes", "moe_combine", "moe_refill_score",
+           "moe_grouped_ffn_noalloc_max_bytes", "moe_layer", "moe_layer_workspace_bytes", "moe_combine",
+           "moe_refill_score",
            "moe_refill_finalize", "moe_prune_slice", "moe_router_norm_keep",
            "moe_nvfp4_quantize", "moe_awq_to_output_major", "moe_workspace_bytes", "moe_status_string",
            "moe_last_hip_error"]
@@ -84,6 +85,8 @@ def lib():
         "moe_router_norm_keep": [P, i32, i32, i32, P, P, P],
         "moe_nvfp4_quantize": [P, i32, i32, ctypes.c_float, P, P],
         "moe_awq_to_output_major": [ctypes.POINTER(_Experts), ctypes.POINTER(_Experts), P],
+        "moe_layer": [P, i32, P, i32, ctypes.POINTER(_Experts), ctypes.POINTER(_Experts), P, P, P, P, sz, P,
+                      P, ctypes.POINTER(P)],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -91,6 +94,8 @@ def lib():
         f.restype = ctypes.c_int
     L.moe_grouped_ffn_noalloc_max_bytes.argtypes = []
     L.moe_grouped_ffn_noalloc_max_bytes.restype = ctypes.c_size_t
+    L.moe_layer_workspace_bytes.argtypes = [i32, i32, ctypes.POINTER(_Experts), ctypes.POINTER(_Experts)]
+    L.moe_layer_workspace_bytes.restype = ctypes.c_size_t
     L.moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.moe_workspace_bytes.restype = ctypes.c_size_t
     L.moe_status_string.argtypes = [ctypes.c_int]
@@ -373,6 +378,71 @@ def router_norm_keep(w_router, keep: int):
 
 
 # ----------------------------------------------------------------------------- layer
+
+def layer_workspace_bytes(T: int, k: int, bank: dict, shared: dict | None = None) -> int:
+    st = experts_struct(bank)
+    sh = experts_struct(shared) if shared is not None else None
+    return int(lib().moe_layer_workspace_bytes(T, k, ctypes.byref(st), ctypes.byref(sh) if sh else None))
+
+
+def _events_arg(events):
+    if events is None:
+        return None
+    return (ctypes.c_void_p * 2)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events])
+
+
+class LayerCall:
+    """A prepared moe_layer call (the whole layer in one library call): the
+    banks' structs, the workspace, y and every pointer are marshalled once, so
+    that a call costs one ctypes call.  Calling it enqueues one layer step on
+    torch's current stream and returns y (the same tensor every call).
+
+    side_stream (a torch.cuda.Stream, default priority) runs the shared
+    expert beside the routed path.  Timing events passed to __call__ must be
+    torch.cuda.Event objects that have been recorded once (torch creates the
+    underlying HIP event on first record)."""
+
+    def __init__(self, x, w_router, k: int, bank: dict, shared: dict | None = None, shared_scale=None,
+                 side_stream=None, ws=None, topk_idx=None):
+        T, H = x.shape
+        self.x, self.w_router, self.k = x, w_router, k
+        self.bank, self.shared, self.shared_scale = bank, shared, shared_scale
+        self.st = experts_struct(bank)
+        self.sh = experts_struct(shared) if shared is not None else None
+        need = int(lib().moe_layer_workspace_bytes(T, k, ctypes.byref(self.st),
+                                                   ctypes.byref(self.sh) if self.sh else None))
+        if T > 0 and need == 0:
+            raise MoeError("moe_layer_workspace_bytes: invalid bank")
+        self.ws_buf, self.ws_n = (ws or Workspace(x.device)).get(need)
+        self.y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+        self.topk_idx = topk_idx
+        self.side = side_stream
+        self._args = (_ptr(x), T, _ptr(w_router), k, ctypes.byref(self.st),
+                      ctypes.byref(self.sh) if self.sh else None, _ptr(shared_scale), _ptr(self.y),
+                      _ptr(topk_idx), _ptr(self.ws_buf), self.ws_n)
+        self._side = ctypes.c_void_p(side_stream.cuda_stream) if side_stream is not None else None
+
+    def __call__(self, events=None):
+        _check("moe_layer", lib().moe_layer(*self._args, _stream(), self._side, _events_arg(events)))
+        return self.y
+
+
+def layer(x, w_router, k: int, bank: dict, shared: dict | None = None, shared_scale=None, y=None,
+          topk_idx=None, ws=None, side_stream=None, routed_events=None):
+    """moe_layer: the whole layer in one library call; returns y [T, H] bf16."""
+    T, H = x.shape
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    st = experts_struct(bank)
+    sh = experts_struct(shared) if shared is not None else None
+    shp = ctypes.byref(sh) if sh else None
+    buf, n = _ws(ws, x.device).get(int(lib().moe_layer_workspace_bytes(T, k, ctypes.byref(st), shp)))
+    side = ctypes.c_void_p(side_stream.cuda_stream) if side_stream is not None else None
+    _check("moe_layer", lib().moe_layer(_ptr(x), T, _ptr(w_router), k, ctypes.byref(st), shp, _ptr(shared_scale),
+                                        _ptr(y), _ptr(topk_idx), _ptr(buf), n, _stream(), side,
+                                        _events_arg(routed_events)))
+    return y
+
 
 def moe_layer(x, w_router, k: int, bank: dict, shared: dict | None = None, shared_scale=None,
               ws=None, keep_intermediates: bool = False, shared_stream=None, shared_ws=None):

@@ -172,6 +172,77 @@ size_t route_permute_ws(int T, int k, int E, int H) {
     return a > b ? a : b;
 }
 
+// ---- the whole layer in one call (moe_layer)
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace regions of moe_layer, in order; every offset is a multiple of 256.
+struct LayerLayout {
+    size_t idx, tl, gate, off, sp, p2r, slots, rows, srows, rp_ws, ffn_ws, sh_ws, total;
+};
+
+LayerLayout layer_layout(int T, int k, const moe_experts* ex, const moe_experts* sh) {
+    const int E = ex->num_experts, H = ex->hidden, F = ex->inter;
+    const size_t P = (size_t)T * k;
+    LayerLayout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += align256(bytes);
+        return at;
+    };
+    L.idx = take(P * 4);
+    L.tl = take(P * 4);
+    L.gate = take(P * 4);
+    L.off = take(((size_t)E + 1) * 4);
+    L.sp = take(P * 4);
+    L.p2r = take(P * 4);
+    L.slots = take(P * 16);
+    L.rows = take(P * H * 2);
+    L.srows = take(sh ? (size_t)T * H * 2 : 0);
+    L.rp_ws = take(route_permute_ws(T, k, E, H));
+    L.ffn_ws = take(moe::ffn_ws_bytes(T, k, E, H, F, ex->gate.fmt));
+    L.sh_ws = take(sh ? moe::ffn_ws_bytes(T, 1, 1, H, sh->inter, sh->gate.fmt) : 0);
+    L.total = o;
+    return L;
+}
+
+// Fork and join events of the shared expert's side stream, one pair per
+// thread and device (a call records and waits on them from its own thread).
+struct SideEvents {
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+thread_local SideEvents t_side[kMaxDevices];
+
+moe_status side_events(hipStream_t s, SideEvents** out) {
+    int dev = -1;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    SideEvents& ev = t_side[dev];
+    if (!ev.fork) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status(e);
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+        hipEvent_t a = nullptr, b = nullptr;
+        e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) {
+            if (a) (void)hipEventDestroy(a);
+            if (b) (void)hipEventDestroy(b);
+            return hip_status(e);
+        }
+        ev.fork = a;
+        ev.join = b;
+    }
+    *out = &ev;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,7 +307,7 @@ moe_status moe_route_permute(const uint16_t* x, const uint16_t* w_router, int32_
         moe_status st = hip_status(moe::launch_exact_logits(x, w_router, T, H, E, lbuf, s));
         if (st != MOE_OK) return st;
         return hip_status(moe::launch_topk_permute(lbuf, T, E, k, topk_idx, topk_logit, topk_gate,
-                                                   expert_offsets, sorted_pair, pair_to_row, s));
+                                                   expert_offsets, sorted_pair, pair_to_row, nullptr, s));
     }
     moe_status st = moe_route(x, w_router, T, H, E, k, 0, topk_idx, topk_logit, topk_gate, nullptr, ws,
                               ws_bytes, stream);
@@ -274,6 +345,102 @@ moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int32_t T, int32_t k, cons
 }
 
 size_t moe_grouped_ffn_noalloc_max_bytes(void) { return kScratchBytes; }
+
+size_t moe_layer_workspace_bytes(int32_t T, int32_t k, const moe_experts* experts, const moe_experts* shared) {
+    moe_status st = MOE_OK;
+    if (T <= 0 || k < 1 || !bank_ok(experts, &st) || (shared && !bank_ok(shared, &st))) return 0;
+    return layer_layout(T, k, experts, shared).total;
+}
+
+moe_status moe_layer(const uint16_t* x, int32_t T, const uint16_t* w_router, int32_t k,
+                     const moe_experts* experts, const moe_experts* shared, const float* shared_scale,
+                     uint16_t* y, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream,
+                     void* side_stream, void* const* routed_events) {
+    moe_status st = MOE_OK;
+    if (T < 0 || k < 1) return MOE_ERR_SHAPE;
+    if (!bank_ok(experts, &st)) return st;
+    const int E = experts->num_experts, H = experts->hidden;
+    if (k > E) return MOE_ERR_SHAPE;
+    if (k > 64 || (int64_t)T * k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    if (shared) {
+        if (!bank_ok(shared, &st)) return st;
+        if (shared->num_experts != 1 || shared->hidden != H) return MOE_ERR_SHAPE;
+    } else if (shared_scale) {
+        return MOE_ERR_SHAPE;
+    }
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !y) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
+    if (experts->gate.fmt == MOE_W_AWQ_G32_OM &&
+        ((uint64_t)T * H * 2 >= (1ull << 32) || (uint64_t)T * k * experts->inter * 2 >= (1ull << 32)))
+        return MOE_ERR_UNSUPPORTED;
+    const LayerLayout L = layer_layout(T, k, experts, shared);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (!ws) return MOE_ERR_NULL;
+    if (!aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t side = static_cast<hipStream_t>(side_stream);
+    SideEvents* ev = nullptr;
+    if (shared && side) {
+        if (side == s) return MOE_ERR_SHAPE;
+        if ((st = side_events(s, &ev)) != MOE_OK) return st;
+    }
+    char* w = static_cast<char*>(ws);
+    int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + L.idx);
+    float* tl = reinterpret_cast<float*>(w + L.tl);
+    float* gate = reinterpret_cast<float*>(w + L.gate);
+    int32_t* off = reinterpret_cast<int32_t*>(w + L.off);
+    int32_t* sp = reinterpret_cast<int32_t*>(w + L.sp);
+    int32_t* p2r = reinterpret_cast<int32_t*>(w + L.p2r);
+    int4* slots = reinterpret_cast<int4*>(w + L.slots);
+    uint16_t* rows = reinterpret_cast<uint16_t*>(w + L.rows);
+    uint16_t* srows = shared ? reinterpret_cast<uint16_t*>(w + L.srows) : nullptr;
+
+    moe::FfnArgs sf{};
+    if (shared) {
+        sf.x = x; sf.T = T; sf.k = 1; sf.H = H; sf.F = shared->inter; sf.E = 1; sf.ex = shared;
+        sf.offsets = nullptr; sf.sorted_pair = nullptr; sf.out_f32 = 0; sf.rows = srows;
+    }
+    // the shared expert needs only x: with a side stream it runs beside the
+    // routing and the routed experts (fork here, join before the combine)
+    if (ev) {
+        if ((st = hip_status(hipEventRecord(ev->fork, s))) != MOE_OK) return st;
+        if ((st = hip_status(hipStreamWaitEvent(side, ev->fork, 0))) != MOE_OK) return st;
+        if ((st = hip_status(moe::launch_ffn(sf, w + L.sh_ws, side))) != MOE_OK) return st;
+        if ((st = hip_status(hipEventRecord(ev->join, side))) != MOE_OK) return st;
+    }
+    // routing and permutation; the single-workgroup selection also writes
+    // the GEMV slot table when the routed call streams
+    const int P = T * k;
+    const int fmt = experts->gate.fmt;
+    const bool fused = !route_filtered(T, H, E) && moe::topk_permute_fits(T, k, E);
+    const bool pre_slots = fused && moe::ffn_takes_gemv(P, E, H, experts->inter, fmt);
+    if (fused) {
+        float* lbuf = reinterpret_cast<float*>(w + L.rp_ws);
+        if ((st = hip_status(moe::launch_exact_logits(x, w_router, T, H, E, lbuf, s))) != MOE_OK) return st;
+        st = hip_status(moe::launch_topk_permute(lbuf, T, E, k, idx, tl, gate, off, sp, p2r,
+                                                 pre_slots ? slots : nullptr, s));
+    } else {
+        st = moe_route_permute(x, w_router, T, H, E, k, idx, tl, gate, off, sp, p2r, w + L.rp_ws,
+                               route_permute_ws(T, k, E, H), stream);
+    }
+    if (st != MOE_OK) return st;
+    // routed experts
+    moe::FfnArgs f{};
+    f.x = x; f.T = T; f.k = k; f.H = H; f.F = experts->inter; f.E = E; f.ex = experts;
+    f.offsets = off; f.sorted_pair = sp; f.out_f32 = 0; f.rows = rows;
+    f.slots = pre_slots ? slots : nullptr;
+    if (routed_events && routed_events[0] &&
+        (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(routed_events[0]), s))) != MOE_OK)
+        return st;
+    if ((st = hip_status(moe::launch_ffn(f, w + L.ffn_ws, s))) != MOE_OK) return st;
+    if (routed_events && routed_events[1] &&
+        (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(routed_events[1]), s))) != MOE_OK)
+        return st;
+    if (shared && !ev && (st = hip_status(moe::launch_ffn(sf, w + L.sh_ws, s))) != MOE_OK) return st;
+    if (ev && (st = hip_status(hipStreamWaitEvent(s, ev->join, 0))) != MOE_OK) return st;
+    return hip_status(moe::launch_combine(rows, 0, p2r, gate, T, k, H, srows, shared_scale, y, s));
+}
 
 moe_status moe_combine(const void* rows, int32_t rows_dtype, const int32_t* pair_to_row,
                        const float* topk_gate, int32_t T, int32_t k, int32_t H,

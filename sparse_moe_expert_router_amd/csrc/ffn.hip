@@ -22,16 +22,18 @@ static size_t quant_x_bytes(int T, int H) { return ((size_t)T * H * sizeof(uint1
 size_t ffn_ws_bytes(int T, int k, int E, int H, int F, int fmt) {
     if (fmt == MOE_W_NVFP4) return quant_x_bytes(T, H) + ffn_ws_bytes(T, k, E, H, F, MOE_W_BF16);
     if (fmt == MOE_W_AWQ_G32_OM) {
-        // the MFMA path at any size; the other formats' bound covers it
+        // the MFMA GEMM or the streaming GEMV; the other formats' bound covers both
         const size_t om = om_gemm_ws_bytes((int)((long)T * k), F, E);
+        const size_t ov = om_gemv_ws_bytes((int)((long)T * k), F);
         const size_t other = ffn_ws_bytes(T, k, E, H, F, MOE_W_BF16);
-        return om > other ? om : other;
+        const size_t m = om > ov ? om : ov;
+        return m > other ? m : other;
     }
     const long P = (long)T * k;
     // shapes the GEMM does not take stream every row through the GEMV
     const bool gemm_ok = F % 128 == 0 && H % 256 == 0;
     const long Pg = (gemm_ok && P >= (long)kGemmMinRows * E) ? (long)kGemmMinRows * E : P;
-    const size_t g1 = gemv_ws_bytes((int)Pg, H, F, 1), g0 = gemv_ws_bytes((int)Pg, H, F, 0);
+    const size_t g1 = gemv_ws_bytes((int)Pg, H, F, 1, E), g0 = gemv_ws_bytes((int)Pg, H, F, 0, E);
     size_t need = g1 > g0 ? g1 : g0;
     if (F % 128 == 0 && H % 256 == 0 && P >= (long)kGemmMinRows * E) {
         const size_t gm = gemm_ws_bytes((int)P, F, E), om = om_gemm_ws_bytes((int)P, F, E);
@@ -39,6 +41,15 @@ size_t ffn_ws_bytes(int T, int k, int E, int H, int F, int fmt) {
         if (om > need) need = om;  // bf16 banks run the register-B GEMM
     }
     return need;
+}
+
+// Output-major AWQ codes stream through the MFMA GEMV for decode-sized calls
+// and run the MFMA GEMM otherwise (and for shapes the GEMV does not take).
+static bool om_streams(int P, int E, int H, int F) { return !use_gemm(P, E, H, F) && om_gemv_supported(H, F); }
+
+bool ffn_takes_gemv(int P, int E, int H, int F, int fmt) {
+    if (fmt == MOE_W_AWQ_G32_OM) return om_streams(P, E, H, F);
+    return !use_gemm(P, E, H, F);
 }
 
 hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
@@ -55,6 +66,7 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
     a.nvfp4 = f.ex->gate.fmt == MOE_W_NVFP4;
     a.offsets = f.offsets;
     a.sorted_pair = f.sorted_pair;
+    a.slots = f.slots;
     auto pj = [](const moe_proj& p) {
         ProjDev d;
         d.w = p.w;
@@ -81,7 +93,10 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
         a.x = xq;
         ws = static_cast<char*>(ws) + quant_x_bytes(f.T, f.H);
     }
-    if (f.ex->gate.fmt == MOE_W_AWQ_G32_OM) return launch_om_gemm(a, ws, s);
+    if (f.ex->gate.fmt == MOE_W_AWQ_G32_OM) {
+        if (om_streams(a.P, a.offsets ? a.E : 1, a.H, a.F)) return launch_om_gemv(a, ws, s);
+        return launch_om_gemm(a, ws, s);
+    }
     if (use_gemm(a.P, a.offsets ? a.E : 1, a.H, a.F)) {
         // bf16 weights go straight into registers on the register-B GEMM
         if (f.ex->gate.fmt == MOE_W_BF16 && om_gemm_supported(a.H, a.F)) return launch_om_gemm(a, ws, s);

@@ -23,6 +23,7 @@ namespace moe {
 
 constexpr int kAwqNib[8] = {0, 2, 4, 6, 1, 3, 5, 7};  // nibble j holds column 8c + kAwqNib[j]
 constexpr int kGemvMaxKPairs = 1024;                  // LDS activation pairs per row (2048 inputs)
+constexpr int kGemvMaxSplit = 8;  // input splits of the non-AWQ gate/up pass (more measured slower)
 
 __device__ __forceinline__ int row_token(const int32_t* sorted_pair, int k, int r) {
     return sorted_pair ? sorted_pair[r] / k : r;
@@ -993,7 +994,7 @@ int gemv_ksplit(const GroupedArgs& a) {
         const int cols = a.nvfp4 && a.F % nv_gate_cols(kNvGateLanes) == 0 ? nv_gate_cols(kNvGateLanes) : 32;
         const long wgs = (long)slots * (a.F / cols);
         int ks = 1;
-        while (wgs * ks < 1024 && ks < 8 && (a.H / 8) % (ks * 2) == 0) ks *= 2;
+        while (wgs * ks < 1024 && ks < kGemvMaxSplit && (a.H / 8) % (ks * 2) == 0) ks *= 2;
         return ks;
     }
     const int G = a.H / 32;
@@ -1009,8 +1010,9 @@ static size_t part_bytes(int P, int F, int ks) {
     return ((size_t)ks * P * 2 * F * sizeof(float) + 255) & ~(size_t)255;
 }
 
-size_t gemv_ws_bytes(int P, int H, int F, int awq) {
-    int ks = 8;  // at most 8 splits for bf16
+size_t gemv_ws_bytes(int P, int H, int F, int awq, int E) {
+    int ks = kGemvMaxSplit;  // bf16, FP8, NVFP4 bound
+    (void)E;
     if (awq) {
         GroupedArgs a{};
         a.H = H;
@@ -1055,12 +1057,15 @@ static hipError_t launch_gemv_rch(const GroupedArgs& a, void* ws, hipStream_t s)
         const size_t red_bytes = (size_t)RCH * F * sizeof(float);
         hipLaunchKernelGGL(awq_gateup_kernel<RCH>, dim3(2 * KS, slots), dim3(OW * RP), red_bytes, s,
                            a, KS, part);
+        const int OWd = H / 8, OWC = down_owc(OWd);
+        // few down workgroups share a row (5 at H = 2560): each forms the
+        // SwiGLU from the partial sums itself, which costs less than a launch
+        if (OWd / OWC <= 8) hbuf = nullptr;
         if (hbuf) {
             const long pairs = (long)a.P * (F / 2);
             hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
                                s, (const float*)part, KS, a.P, F, 0.0f, hbuf);
         }
-        const int OWd = H / 8, OWC = down_owc(OWd);
         const int RPd = row_phases(OWC);
         hipLaunchKernelGGL(awq_down_kernel<RCH>, dim3(OWd / OWC, slots), dim3(OWC * RPd),
                            (size_t)RCH * 8 * OWC * sizeof(float), s, a, KS, OWC,
@@ -1147,14 +1152,19 @@ __global__ __launch_bounds__(1024) void slot_table_kernel(const int32_t* __restr
     if (e >= total && e < nslots) slots[e] = make_int4(-1, 0, 0, 0);
 }
 
+int4* launch_slot_table(const int32_t* offsets, int E, int P, int4* tab, hipStream_t s) {
+    hipLaunchKernelGGL(slot_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, P < E ? P : E, tab);
+    return tab;
+}
+
 hipError_t launch_gemv(const GroupedArgs& a0, void* ws, hipStream_t s) {
     GroupedArgs a = a0;
-    a.slots = nullptr;
     if (a.offsets) {
         int4* tab = static_cast<int4*>(ws);
         ws = static_cast<char*>(ws) + slot_table_bytes(a.P);
-        hipLaunchKernelGGL(slot_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.P < a.E ? a.P : a.E, tab);
-        a.slots = tab;
+        if (!a0.slots) a.slots = launch_slot_table(a.offsets, a.E, a.P, tab, s);
+    } else {
+        a.slots = nullptr;
     }
     // rows per pass: a bf16 shared expert sees every token (all of a decode
     // batch in one pass); a routed expert at decode sees one or two, and the

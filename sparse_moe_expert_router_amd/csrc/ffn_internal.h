@@ -38,7 +38,7 @@ struct GroupedArgs {
 // GEMV family: gate/up partial sums [KS][P][2F] fp32 in `part`, then the down
 // projection (whose prologue finishes SwiGLU) writes `rows`.
 int gemv_ksplit(const GroupedArgs& a);
-size_t gemv_ws_bytes(int P, int H, int F, int awq);
+size_t gemv_ws_bytes(int P, int H, int F, int awq, int E);
 hipError_t launch_gemv(const GroupedArgs& a, void* ws, hipStream_t s);
 
 // MFMA family: h [P][F] bf16 in the workspace, then rows.
@@ -70,6 +70,16 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 // bf16 in the workspace after the tile table, then rows.
 size_t om_gemm_ws_bytes(int P, int F, int E);
 hipError_t launch_om_gemm(const GroupedArgs& a, void* ws, hipStream_t s);
+
+// Streaming GEMV on AWQ g32 codes stored output-major (ffn_gemv_om.hip): the
+// slot table, then h [P][F] bf16 in the workspace, then rows.
+bool om_gemv_supported(int H, int F);
+size_t om_gemv_ws_bytes(int P, int F);
+hipError_t launch_om_gemv(const GroupedArgs& a, void* ws, hipStream_t s);
+
+// Slot table of a grouped GEMV call (ffn_gemv.hip) into `tab` (min(P, E)
+// entries); returns tab.
+int4* launch_slot_table(const int32_t* offsets, int E, int P, int4* tab, hipStream_t s);
 
 // Dense fp32 GEMM on the same kernels (used by the router's screening pass).
 size_t dense_gemm_ws_bytes(int M);

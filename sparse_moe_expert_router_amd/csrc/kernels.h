@@ -16,11 +16,12 @@ hipError_t launch_exact_logits(const uint16_t* x, const uint16_t* wr, int T, int
                                float* logits, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int extra, int32_t* idx,
                        float* topk_logit, float* gate, hipStream_t s);
-// top-k followed by the permutation, one workgroup (when topk_permute_fits)
+// top-k followed by the permutation, one workgroup (when topk_permute_fits);
+// `slots` (nullable, min(T*k, E) entries) also receives the GEMV slot table
 bool topk_permute_fits(int T, int k, int E);
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* idx, float* topk_logit,
                                float* gate, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_to_row,
-                               hipStream_t s);
+                               int4* slots, hipStream_t s);
 size_t route_filter_ws_bytes(int T, int E, int H);
 hipError_t launch_route_filter(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
                                int extra, int32_t* idx, float* topk_logit, float* gate, void* ws,
@@ -40,8 +41,12 @@ struct FfnArgs {
     const int32_t* sorted_pair;   // [T*k], or nullptr
     int out_f32;                  // 1: rows are fp32, else bf16
     void* rows;                   // [T*k][H]
+    const int4* slots = nullptr;  // GEMV slot table already built (see launch_topk_permute), or nullptr
 };
 size_t ffn_ws_bytes(int T, int k, int E, int H, int F, int fmt);
+// whether a grouped call of P rows over E experts runs the streaming GEMV
+// kernels (which read a slot table) rather than an MFMA GEMM
+bool ffn_takes_gemv(int P, int E, int H, int F, int fmt);
 // hidden and inter sizes the output-major AWQ GEMM takes
 bool om_gemm_supported(int H, int F);
 hipError_t launch_awq_to_om(const int32_t* src, int32_t* dst, int E, int K, int N, hipStream_t s);

@@ -198,7 +198,10 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int extra, int3
 // topk_kernel does, keeping the ids in LDS and counting them per expert;
 // then an exclusive scan (one expert per thread) gives the offsets, and wave
 // 0 scatters the pairs in pair order exactly as the permutation kernels do.
-// The results equal those of launch_topk followed by launch_permute.
+// The results equal those of launch_topk followed by launch_permute.  With
+// `slots` it also writes the grouped GEMV's slot table (slot i = the i-th
+// non-empty expert in index order with its row range, expert -1 past the
+// last), which otherwise takes a launch of its own.
 // ---------------------------------------------------------------------------
 constexpr int kSelWaves = 16;
 
@@ -206,10 +209,12 @@ template <int VPL>
 __global__ __launch_bounds__(kSelWaves * kWave) void topk_permute_kernel(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
     float* __restrict__ topk_logit, float* __restrict__ gate, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_to_row) {
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_to_row, int4* __restrict__ slots,
+    int nslots) {
     __shared__ int cnt[1024];
     __shared__ int ids[kSmallPairs];
     __shared__ int wtot[kSelWaves];
+    __shared__ int wne[kSelWaves];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
@@ -229,6 +234,9 @@ __global__ __launch_bounds__(kSelWaves * kWave) void topk_permute_kernel(
         if (lane >= m) inc += o;
     }
     if (lane == kWave - 1) wtot[wave] = inc;
+    // non-empty experts of this wave, for the slot table
+    const uint64_t ne = __ballot(tid < E && c > 0);
+    if (lane == 0) wne[wave] = __popcll(ne);
     __syncthreads();
     int run = inc - c;
     for (int w = 0; w < wave; ++w) run += wtot[w];
@@ -237,6 +245,16 @@ __global__ __launch_bounds__(kSelWaves * kWave) void topk_permute_kernel(
         offsets[tid] = run;
     }
     if (tid == 0) offsets[E] = T * k;
+    if (slots) {
+        int before = 0, total = 0;
+        for (int w = 0; w < kSelWaves; ++w) {
+            before += w < wave ? wne[w] : 0;
+            total += wne[w];
+        }
+        const int pos = before + __popcll(ne & ((1ull << lane) - 1ull));
+        if (tid < E && c > 0 && pos < nslots) slots[pos] = make_int4(tid, run, run + c, 0);
+        if (tid >= total && tid < nslots) slots[tid] = make_int4(-1, 0, 0, 0);
+    }
     __syncthreads();
     if (wave == 0) wave_scatter<true>(ids, 0, T * k, E, bits_for(E), cnt, sorted_pair, pair_to_row);
 }
@@ -245,11 +263,12 @@ bool topk_permute_fits(int T, int k, int E) { return (long)T * k <= kSmallPairs 
 
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* idx, float* topk_logit,
                                float* gate, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_to_row,
-                               hipStream_t s) {
+                               int4* slots, hipStream_t s) {
     const int vpl = (E + kWave - 1) / kWave;
+    const int nslots = T * k < E ? T * k : E;
 #define MOE_SEL(V)                                                                                        \
     hipLaunchKernelGGL(topk_permute_kernel<V>, dim3(1), dim3(kSelWaves * kWave), 0, s, logits, T, E, k, idx, \
-                       topk_logit, gate, offsets, sorted_pair, pair_to_row)
+                       topk_logit, gate, offsets, sorted_pair, pair_to_row, slots, nslots)
     if (vpl <= 1) MOE_SEL(1);
     else if (vpl <= 2) MOE_SEL(2);
     else if (vpl <= 4) MOE_SEL(4);

@@ -197,3 +197,36 @@ def test_awq_to_output_major_validation():
                                      ctypes.byref(_bank(fmt=4, H=192, F=128)), None) == UNSUP
     # codes that overlap are refused (the fake banks point every tensor at one address)
     assert L.moe_awq_to_output_major(ctypes.byref(src), ctypes.byref(dst), None) == SHAPE
+
+
+def test_layer_validation():
+    """moe_layer checks everything the four calls it stands for check, before
+    any HIP call (the fake pointers are never dereferenced)."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    b, sh = _bank(E=16, H=256, F=128), _bank(E=1, H=256, F=256)
+    need = L.moe_layer_workspace_bytes(8, 2, ctypes.byref(b), ctypes.byref(sh))
+    assert need > 0
+    assert L.moe_layer_workspace_bytes(16, 2, ctypes.byref(b), ctypes.byref(sh)) >= need
+    assert L.moe_layer_workspace_bytes(8, 2, ctypes.byref(b), None) < need
+    assert L.moe_layer_workspace_bytes(0, 2, ctypes.byref(b), None) == 0
+    assert L.moe_layer_workspace_bytes(8, 2, ctypes.byref(_bank(fmt=5)), None) == 0
+
+    def call(T=8, k=2, bank=b, shared=sh, scale=None, x=fake, y=fake, ws=fake, n=need, side=None):
+        return L.moe_layer(x, T, fake, k, ctypes.byref(bank) if bank is not None else None,
+                           ctypes.byref(shared) if shared is not None else None, scale, y, None, ws, n, None,
+                           side, None)
+    assert call(k=0) == SHAPE
+    assert call(T=-1) == SHAPE
+    assert call(k=17) == SHAPE                              # k > E
+    assert call(bank=None) == NULL
+    assert call(bank=_bank(H=200)) == UNSUP
+    assert call(shared=_bank(E=2, H=256)) == SHAPE          # the shared bank holds one expert
+    assert call(shared=_bank(E=1, H=512, F=128)) == SHAPE   # of the same hidden size
+    assert call(shared=None, scale=fake) == SHAPE           # a scale without a shared expert
+    assert call(x=None) == NULL
+    assert call(y=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(n=need - 1) == WS
+    assert call(x=ctypes.c_void_p(258)) == UNSUP            # misaligned
+    assert call(T=0, x=None, y=None, ws=None, n=0) == OK

@@ -1,0 +1,110 @@
+"""moe_layer (the whole layer in one library call) against the four calls it
+stands for, made one after the other: the same bits for every weight format,
+both routing paths (the single-workgroup selection that also builds the GEMV
+slot table, and the screened router for larger batches), both grouped-expert
+families (streaming GEMV and MFMA GEMM), with the shared expert on the same
+stream or on a side stream.  The four calls are themselves checked against
+the oracle (test_gpu_layer.py, test_gpu_fullsize.py), and the layer call is
+also checked against the oracle directly on two formats."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.gpu_helpers import check_close, require_gpu
+from tests.test_gpu_layer import oracle_layer_sparse
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name):
+    if name == "gemm_bf16":        # 128 rows per expert: MFMA GEMM, screened router off (E % 256)
+        return workloads.scaled(workloads.get("tiny_bf16"), T=1024)
+    if name == "screened_awq":     # T >= 64, E = 512: screened router, streaming GEMV
+        return workloads.scaled(workloads.get("decode_awq"), T=96)
+    if name == "prefill_awq_om":   # output-major AWQ codes, MFMA GEMM, 40 rows per expert
+        return workloads.scaled(workloads.get("prefill_awq"), T=2048)
+    return workloads.get(name)
+
+
+CASES = ["tiny_bf16", "decode_bf16", "decode_awq", "decode_fp8", "decode_nvfp4", "gemm_bf16", "screened_awq",
+         "prefill_awq_om"]
+
+
+@pytest.mark.parametrize("name", CASES)
+@pytest.mark.parametrize("side", [False, True])
+def test_layer_call_equals_the_four_calls(name, side):
+    moe = require_gpu()
+    w = _case(name)
+    print(f"case {name} side={side} T={w.T} E={w.E} fmt={w.fmt}", flush=True)
+    d = workloads.generate(w, device="cuda")
+    bank = moe.awq_to_output_major(d["experts"]) if name.endswith("_om") else d["experts"]
+    ref, mid = moe.moe_layer(d["x"], d["router"], w.k, bank, d["shared"], keep_intermediates=True)
+    ref = ref.clone()
+    idx = torch.full((w.T, w.k), -1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream() if side else None
+    for _ in range(2):
+        y = moe.layer(d["x"], d["router"], w.k, bank, d["shared"], topk_idx=idx, side_stream=s)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), name
+        assert torch.equal(idx, mid["idx"])
+
+
+@pytest.mark.parametrize("name", ["decode_awq", "tiny_bf16"])
+def test_layer_call_matches_oracle(name):
+    moe = require_gpu()
+    w = workloads.get(name)
+    d = workloads.generate(w, seed=4, device="cuda")
+    sc = torch.linspace(-0.5, 1.5, w.T, device="cuda")
+    y = moe.layer(d["x"], d["router"], w.k, d["experts"], d["shared"], shared_scale=sc,
+                  side_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    ref_y, _, _ = oracle_layer_sparse(d["x"], d["router"], w.k, d["experts"], d["shared"],
+                                      shared_scale=sc.double().cpu().numpy())
+    check_close(y.float().cpu().numpy(), ref_y, name)
+
+
+def test_layer_call_without_shared_expert():
+    moe = require_gpu()
+    w = workloads.get("decode_awq")
+    d = workloads.generate(w, device="cuda")
+    ref = moe.moe_layer(d["x"], d["router"], w.k, d["experts"], None).clone()
+    y = moe.layer(d["x"], d["router"], w.k, d["experts"], None)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+
+
+def test_prepared_layer_call_and_routed_events():
+    """LayerCall repeats the same bits; the events bracket the routed call."""
+    moe = require_gpu()
+    w = workloads.get("decode_awq")
+    d = workloads.generate(w, device="cuda")
+    ref = moe.layer(d["x"], d["router"], w.k, d["experts"], d["shared"]).clone()
+    call = moe.LayerCall(d["x"], d["router"], w.k, d["experts"], d["shared"], side_stream=torch.cuda.Stream())
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+    for a, b in evs:  # torch creates the HIP events on first record
+        a.record()
+        b.record()
+    for a, b in evs:
+        y = call((a, b))
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+    for a, b in evs:
+        ms = a.elapsed_time(b)
+        assert 0.0 < ms < 100.0, ms
+    # a batch of different tokens through the same prepared call shape
+    x2 = workloads.generate(w, seed=7, device="cuda")["x"]
+    call.x.copy_(x2)
+    y2 = call().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y2, moe.layer(x2, d["router"], w.k, d["experts"], d["shared"]))
+    assert not torch.equal(y2, ref)
+
+
+def test_layer_call_zero_tokens():
+    moe = require_gpu()
+    w = workloads.get("tiny_bf16")
+    d = workloads.generate(w, device="cuda")
+    y = moe.layer(d["x"][:0], d["router"], w.k, d["experts"], d["shared"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, w.H)
