@@ -35,6 +35,10 @@ size_t ffn_ws_bytes(int T, int k, int E, int H, int F, int fmt) {
     const long Pg = (gemm_ok && P >= (long)kGemmMinRows * E) ? (long)kGemmMinRows * E : P;
     const size_t g1 = gemv_ws_bytes((int)Pg, H, F, 1, E), g0 = gemv_ws_bytes((int)Pg, H, F, 0, E);
     size_t need = g1 > g0 ? g1 : g0;
+    if (E == 1 && T <= 16 && skinny_supported(T, H, F)) {  // covered by g0; kept explicit
+        const size_t sk = skinny_ws_bytes(T, H, F);
+        if (sk > need) need = sk;
+    }
     if (F % 128 == 0 && H % 256 == 0 && P >= (long)kGemmMinRows * E) {
         const size_t gm = gemm_ws_bytes((int)P, F, E), om = om_gemm_ws_bytes((int)P, F, E);
         if (gm > need) need = gm;
@@ -97,6 +101,8 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
         if (om_streams(a.P, a.offsets ? a.E : 1, a.H, a.F)) return launch_om_gemv(a, ws, s);
         return launch_om_gemm(a, ws, s);
     }
+    // the shared expert of a decode step: one bf16 expert, a handful of tokens
+    if (!a.offsets && f.ex->gate.fmt == MOE_W_BF16 && skinny_supported(a.T, a.H, a.F)) return launch_skinny(a, ws, s);
     if (use_gemm(a.P, a.offsets ? a.E : 1, a.H, a.F)) {
         // bf16 weights go straight into registers on the register-B GEMM
         if (f.ex->gate.fmt == MOE_W_BF16 && om_gemm_supported(a.H, a.F)) return launch_om_gemm(a, ws, s);

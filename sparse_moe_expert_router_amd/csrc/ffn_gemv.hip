@@ -740,6 +740,13 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restr
     h[i] = swiglu_pair(part, KS, P, F, r, f, qa);
 }
 
+hipError_t launch_swiglu_reduce(const float* part, int KS, int P, int F, uint32_t* h, hipStream_t s) {
+    const long pairs = (long)P * (F / 2);
+    hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, part, KS, P, F,
+                       0.0f, h);
+    return hipGetLastError();
+}
+
 // Rows [rc, rc+nr) of h into LDS as bf16 pairs h2[RCH][F/2]: copied from hsrc
 // when the SwiGLU was formed by swiglu_reduce_kernel, else formed here.
 template <int RCH>

@@ -77,6 +77,16 @@ bool om_gemv_supported(int H, int F);
 size_t om_gemv_ws_bytes(int P, int F);
 hipError_t launch_om_gemv(const GroupedArgs& a, void* ws, hipStream_t s);
 
+// h = bf16(silu(sum_ks gate) * sum_ks up) of fp32 partial sums
+// part[KS][P][2F] (splits added in order), as bf16 pairs [P][F/2] (ffn_gemv.hip).
+hipError_t launch_swiglu_reduce(const float* part, int KS, int P, int F, uint32_t* h, hipStream_t s);
+
+// A one-expert bf16 call of at most 16 tokens (the shared expert at decode):
+// split-K MFMA GEMM (ffn_skinny.hip); workspace: partial sums, then h.
+bool skinny_supported(int T, int H, int F);
+size_t skinny_ws_bytes(int T, int H, int F);
+hipError_t launch_skinny(const GroupedArgs& a, void* ws, hipStream_t s);
+
 // Slot table of a grouped GEMV call (ffn_gemv.hip) into `tab` (min(P, E)
 // entries); returns tab.
 int4* launch_slot_table(const int32_t* offsets, int E, int P, int4* tab, hipStream_t s);
