@@ -72,7 +72,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--graph", choices=["on", "off"], default="off",
                    help="replay each layer step from one HIP graph (captured moe_layer call, side "
-                        "stream included)")
+                        "stream included); the roofline events then bracket the whole replay")
     p.add_argument("--shared-stream", choices=["on", "off"], default="on",
                    help="run the shared expert on a side stream beside the routed path (on) or on "
                         "the main stream before it (off)")
@@ -166,7 +166,7 @@ def measure(moe, w, steps, warmup, copies_arg, seed, graph, layout="om", side_st
         a.record(stream)
         b.record(stream)
     if graph:
-        step = graph_steps(w, calls, evs, step)
+        step = graph_steps(w, calls, step)
 
     for i in range(warmup):
         step(i)
@@ -196,7 +196,8 @@ def measure(moe, w, steps, warmup, copies_arg, seed, graph, layout="om", side_st
     bytes_call = n_touched * expert_bytes(w, w.fmt) + w.T * w.H * 2 + P * w.H * out_bytes
     flops_call = 2.0 * P * 3 * w.H * w.F
     roof = roofline(bytes_call, flops_call, ffn_ms)
-    roof["kernel"] = "moe_grouped_ffn (routed): gate/up + down kernels"
+    roof["kernel"] = ("whole layer (one graph replay; the events bracket the replay)" if graph
+                      else "moe_grouped_ffn (routed): gate/up + down kernels")
     roof["avg_ms"] = round(ffn_ms, 4)
     roof["algorithmic_bytes"] = int(bytes_call)
     roof["algorithmic_flops"] = int(flops_call)
@@ -276,35 +277,31 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def graph_steps(w, calls, evs, eager_step):
+def graph_steps(w, calls, eager_step):
     """Steps replayed from HIP graphs: one captured moe_layer call (side
-    stream and routed-call events included) per weight copy and timing slot.
-    Capture follows an eager pass, so the workspace has its final size."""
+    stream included) per weight copy.  Event records captured inside a graph
+    do not time the replayed work, so in this mode the events bracket the
+    whole replay.  Capture follows an eager pass, so the workspace has its
+    final size."""
     import torch
     if w.refill:
         raise ValueError("the Refill-RMS pass is not replayed from graphs")
     for i in range(len(calls)):
         eager_step(i)
     torch.cuda.synchronize()
-    graphs = {}
-
-    def get(i, ev):
-        key = (i % len(calls), None if ev is None else id(ev))
-        if key not in graphs:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                calls[key[0]](ev)
-            graphs[key] = g
-        return graphs[key]
-
-    for i in range(len(evs)):  # capture every (copy, events) pair before timing
-        get(i, evs[i])
-    for i in range(len(calls)):
-        get(i, None)
+    graphs = []
+    for c in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            c()
+        graphs.append(g)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
-        get(i, ev).replay()
+        if ev: ev[0].record(stream)
+        graphs[i % len(graphs)].replay()
+        if ev: ev[1].record(stream)
     return step
 
 

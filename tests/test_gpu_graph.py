@@ -33,3 +33,33 @@ def test_layer_graph_replays_match_eager(name, side_stream):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, ref)
+
+
+@pytest.mark.parametrize("name,side_stream,om", [("tiny_bf16", False, False), ("decode_awq", True, True),
+                                                 ("decode_bf16", True, False)])
+def test_layer_call_graph_replays_match_eager(name, side_stream, om):
+    """moe_layer captured whole (its side-stream fork and join become graph
+    edges): every replay equals the eager call, with eager calls of the same
+    prepared call shape on other inputs in between."""
+    moe = require_gpu()
+    w = workloads.get(name)
+    d = workloads.generate(w, device="cuda")
+    other = workloads.generate(w, seed=7, device="cuda")
+    bank = moe.awq_to_output_major(d["experts"]) if om else d["experts"]
+    bank_o = moe.awq_to_output_major(other["experts"]) if om else other["experts"]
+    side = torch.cuda.Stream() if side_stream else None
+    call = moe.LayerCall(d["x"], d["router"], w.k, bank, d["shared"], side_stream=side)
+    call_o = moe.LayerCall(other["x"], other["router"], w.k, bank_o, other["shared"], side_stream=side)
+    ref = call().clone()
+    ref_o = call_o().clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y = call()
+    for _ in range(3):
+        y2 = call_o()
+        torch.cuda.synchronize()
+        assert torch.equal(y2, ref_o)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
