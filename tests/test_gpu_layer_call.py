@@ -50,13 +50,17 @@ def test_layer_call_equals_the_four_calls(name, side):
         assert torch.equal(idx, mid["idx"])
 
 
-@pytest.mark.parametrize("name", ["decode_awq", "tiny_bf16"])
+@pytest.mark.parametrize("name", ["decode_awq", "decode_awq_om", "tiny_bf16"])
 def test_layer_call_matches_oracle(name):
+    """The layer call against the oracle directly; decode_awq_om runs the
+    16-token W4A16 layer on output-major codes, as bench.py does."""
     moe = require_gpu()
-    w = workloads.get(name)
+    om = name.endswith("_om")
+    w = workloads.get(name[:-3] if om else name)
     d = workloads.generate(w, seed=4, device="cuda")
+    bank = moe.awq_to_output_major(d["experts"]) if om else d["experts"]
     sc = torch.linspace(-0.5, 1.5, w.T, device="cuda")
-    y = moe.layer(d["x"], d["router"], w.k, d["experts"], d["shared"], shared_scale=sc,
+    y = moe.layer(d["x"], d["router"], w.k, bank, d["shared"], shared_scale=sc,
                   side_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     ref_y, _, _ = oracle_layer_sparse(d["x"], d["router"], w.k, d["experts"], d["shared"],
