@@ -2,7 +2,8 @@
 against moe_grouped_ffn with a caller workspace: the same kernels run on the
 library's per-GPU scratch array, so the rows must be identical bit for bit.
 Two calls in a row, the second smaller, on the streaming (few rows per
-expert), MFMA (many rows per expert), NVFP4 and shared-expert paths; a call
+expert, both AWQ code layouts), MFMA (many rows per expert, both GEMMs), NVFP4
+and shared-expert paths; a call
 whose scratch need exceeds the array is refused before anything runs."""
 import numpy as np
 import pytest
@@ -20,16 +21,20 @@ def _routed(moe, w, d, T):
     return x, off, sp
 
 
-@pytest.mark.parametrize("name,T1,T2,changes", [
-    ("decode_awq", 16, 5, {}),                                             # streaming kernels
-    ("decode_nvfp4", 16, 3, {}),                                           # + quantised input in scratch
-    ("tiny_bf16", 1024, 700, dict(T=1024, E=16, k=2)),                     # MFMA grouped GEMM
-    ("prefill_awq", 256, 200, dict(T=256, E=8, k=2)),                      # AWQ GEMM, full width
+@pytest.mark.parametrize("name,T1,T2,changes,om", [
+    ("decode_awq", 16, 5, {}, False),                                      # streaming kernels
+    ("decode_awq", 16, 5, {}, True),                                       # MFMA streaming, output-major codes
+    ("decode_nvfp4", 16, 3, {}, False),                                    # + quantised input in scratch
+    ("tiny_bf16", 1024, 700, dict(T=1024, E=16, k=2), False),              # MFMA grouped GEMM
+    ("prefill_awq", 256, 200, dict(T=256, E=8, k=2), False),               # AWQ GEMM, full width
+    ("prefill_awq", 256, 200, dict(T=256, E=8, k=2), True),                # register-B GEMM, output-major
 ])
-def test_noalloc_equals_workspace_call(name, T1, T2, changes):
+def test_noalloc_equals_workspace_call(name, T1, T2, changes, om):
     moe = require_gpu()
     w = workloads.scaled(workloads.get(name), **changes) if changes else workloads.get(name)
     d = workloads.generate(w, seed=7, device="cuda")
+    if om:
+        d["experts"] = moe.awq_to_output_major(d["experts"])
     for T in (T1, T2):
         x, off, sp = _routed(moe, w, d, T)
         need = moe.workspace_bytes(moe.OP_GROUPED_FFN_NVFP4 if w.fmt == "nvfp4" else moe.OP_GROUPED_FFN,
