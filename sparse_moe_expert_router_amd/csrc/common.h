@@ -31,6 +31,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// A 16-byte load of data that is read once per call (expert weights streamed
+// at decode), with the non-temporal hint: the lines do not displace data that
+// is reused (the staged activations, the scales, the outputs).  Measured on
+// the 16-token decode layers, routed call: bf16 243 -> 221 us, FP8 140 ->
+// 127 us, output-major AWQ 104 -> 96 us; NVFP4 unchanged.
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Two floats to a packed bf16 pair with one v_cvt_pk_bf16_f32 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));

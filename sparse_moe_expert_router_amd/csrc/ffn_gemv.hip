@@ -236,7 +236,7 @@ __device__ __forceinline__ void bf16_stream_dot(const uint4* const (&rows)[NR], 
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int n = 0; n < NR; ++n) w[u][n] = rows[n][v + 16 * u];
+            for (int n = 0; n < NR; ++n) w[u][n] = ld_stream(&rows[n][v + 16 * u]);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -256,7 +256,7 @@ __device__ __forceinline__ void bf16_stream_dot(const uint4* const (&rows)[NR], 
     for (; v < nv; v += 16) {
         uint4 w[NR];
 #pragma unroll
-        for (int n = 0; n < NR; ++n) w[n] = rows[n][v];
+        for (int n = 0; n < NR; ++n) w[n] = ld_stream(&rows[n][v]);
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const uint4 xv = xs[i * xstride + v];
@@ -384,7 +384,7 @@ __device__ __forceinline__ void fp8_stream_dot(const uint4* const (&rows)[NR],
             const int v = min(v0 + 16 * u, nv - 1);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
-                w[u][n] = rows[n][v];
+                w[u][n] = ld_stream(&rows[n][v]);
                 sc[u][n] = srow[n][(k0 + 16 * v) >> 7];
             }
         }
@@ -559,7 +559,7 @@ __device__ __forceinline__ void nvfp4_stream_dot(const uint4* const (&rows)[NR],
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
                 const int vv = v + LPR * u;
-                w[u][n] = rows[n][vv];
+                w[u][n] = ld_stream(&rows[n][vv]);
                 sc[u][n] = *reinterpret_cast<const uint16_t*>(srow[n] + ((k0 + 32 * vv) >> 4));
             }
 #pragma unroll
@@ -572,7 +572,7 @@ __device__ __forceinline__ void nvfp4_stream_dot(const uint4* const (&rows)[NR],
         uint32_t sc[NR];
 #pragma unroll
         for (int n = 0; n < NR; ++n) {
-            w[n] = rows[n][v];
+            w[n] = ld_stream(&rows[n][v]);
             sc[n] = *reinterpret_cast<const uint16_t*>(srow[n] + ((k0 + 32 * v) >> 4));
         }
 #pragma unroll
@@ -589,7 +589,7 @@ __device__ __forceinline__ void nvfp4_load_vec(const uint4* const (&rows)[NR], c
                                                int k0, int v, uint4 (&w)[NR], uint32_t (&sc)[NR]) {
 #pragma unroll
     for (int n = 0; n < NR; ++n) {
-        w[n] = rows[n][v];
+        w[n] = ld_stream(&rows[n][v]);
         sc[n] = *reinterpret_cast<const uint16_t*>(srow[n] + ((k0 + 32 * v) >> 4));
     }
 }

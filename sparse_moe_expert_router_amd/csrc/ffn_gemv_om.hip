@@ -108,11 +108,15 @@ struct OvCodes {
     u32x4_t c[PS];
 };
 
+// Cache policy of the code loads: non-temporal (the codes are read once per
+// call; 104 -> 96 us for the 16-token decode layer's routed call).
+constexpr int kOvCodePolicy = 2;
+
 template <int PS>
 __device__ __forceinline__ void ov_load(OvCodes<PS>& cd, rsrc_t cw, uint32_t vc, int NG) {
 #pragma unroll
     for (int p = 0; p < PS; ++p)
-        cd.c[p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(cw, vc, 16 * NG * p, 0));
+        cd.c[p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(cw, vc, 16 * NG * p, kOvCodePolicy));
 }
 
 // Shapes of one launch: I inputs, O output columns a projection, G = I / 32
