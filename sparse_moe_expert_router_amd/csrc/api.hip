@@ -409,17 +409,24 @@ moe_status moe_layer(const uint16_t* x, int32_t T, const uint16_t* w_router, int
         if ((st = hip_status(moe::launch_ffn(sf, w + L.sh_ws, side))) != MOE_OK) return st;
         if ((st = hip_status(hipEventRecord(ev->join, side))) != MOE_OK) return st;
     }
-    // routing and permutation; the single-workgroup selection also writes
-    // the GEMV slot table when the routed call streams
+    // routing and permutation.  Few tokens on output-major codes: the
+    // streaming kernels take their rows by (token, slot) pair, so the top-k
+    // runs one wave per token and there is no permutation; otherwise the
+    // single-workgroup selection permutes too, and writes the GEMV slot table
+    // when the routed call streams
     const int P = T * k;
     const int fmt = experts->gate.fmt;
     const bool fused = !route_filtered(T, H, E) && moe::topk_permute_fits(T, k, E);
-    const bool pre_slots = fused && moe::ffn_takes_gemv(P, E, H, experts->inter, fmt);
+    const bool pairs = fused && moe::pair_mode_fits(T, k, E, H, experts->inter, fmt);
+    const bool pre_slots = fused && !pairs && moe::ffn_takes_gemv(P, E, H, experts->inter, fmt);
     if (fused) {
         float* lbuf = reinterpret_cast<float*>(w + L.rp_ws);
         if ((st = hip_status(moe::launch_exact_logits(x, w_router, T, H, E, lbuf, s))) != MOE_OK) return st;
-        st = hip_status(moe::launch_topk_permute(lbuf, T, E, k, idx, tl, gate, off, sp, p2r,
-                                                 pre_slots ? slots : nullptr, s));
+        if (pairs)
+            st = hip_status(moe::launch_topk(lbuf, T, E, k, 0, idx, tl, gate, s));
+        else
+            st = hip_status(moe::launch_topk_permute(lbuf, T, E, k, idx, tl, gate, off, sp, p2r,
+                                                     pre_slots ? slots : nullptr, s));
     } else {
         st = moe_route_permute(x, w_router, T, H, E, k, idx, tl, gate, off, sp, p2r, w + L.rp_ws,
                                route_permute_ws(T, k, E, H), stream);
@@ -428,8 +435,9 @@ moe_status moe_layer(const uint16_t* x, int32_t T, const uint16_t* w_router, int
     // routed experts
     moe::FfnArgs f{};
     f.x = x; f.T = T; f.k = k; f.H = H; f.F = experts->inter; f.E = E; f.ex = experts;
-    f.offsets = off; f.sorted_pair = sp; f.out_f32 = 0; f.rows = rows;
+    f.offsets = pairs ? nullptr : off; f.sorted_pair = pairs ? nullptr : sp; f.out_f32 = 0; f.rows = rows;
     f.slots = pre_slots ? slots : nullptr;
+    f.pair_expert = pairs ? idx : nullptr;
     if (routed_events && routed_events[0] &&
         (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(routed_events[0]), s))) != MOE_OK)
         return st;
@@ -439,7 +447,7 @@ moe_status moe_layer(const uint16_t* x, int32_t T, const uint16_t* w_router, int
         return st;
     if (shared && !ev && (st = hip_status(moe::launch_ffn(sf, w + L.sh_ws, s))) != MOE_OK) return st;
     if (ev && (st = hip_status(hipStreamWaitEvent(s, ev->join, 0))) != MOE_OK) return st;
-    return hip_status(moe::launch_combine(rows, 0, p2r, gate, T, k, H, srows, shared_scale, y, s));
+    return hip_status(moe::launch_combine(rows, 0, pairs ? nullptr : p2r, gate, T, k, H, srows, shared_scale, y, s));
 }
 
 moe_status moe_combine(const void* rows, int32_t rows_dtype, const int32_t* pair_to_row,

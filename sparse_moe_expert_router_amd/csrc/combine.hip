@@ -76,7 +76,7 @@ __global__ __launch_bounds__(512) void combine_kernel(const void* __restrict__ r
     if (k <= kWave) {
         const int j = min(lane, k - 1);
         gl = __float_as_int(gate[pbase + j]);
-        rl = pair_to_row[pbase + j];
+        rl = pair_to_row ? pair_to_row[pbase + j] : (int)(pbase + j);
     }
     for (int v0 = blockIdx.y * blockDim.x + (threadIdx.x - lane); v0 < nv; v0 += stride) {
         const bool act = v0 + lane < nv;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(512) void combine_kernel(const void* __restrict__ r
             if (k > kWave) {
                 const int j = j0 + min(lane, nj - 1);
                 gl = __float_as_int(gate[pbase + j]);
-                rl = pair_to_row[pbase + j];
+                rl = pair_to_row ? pair_to_row[pbase + j] : (int)(pbase + j);
             }
             int j = 0;
             if constexpr (!kF32Rows) {

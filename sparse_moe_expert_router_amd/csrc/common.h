@@ -41,6 +41,13 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A 16-byte store with the non-temporal hint, for outputs that are written
+// once and read once by a later kernel (the prefill GEMMs' h and rows: the
+// pruned 32768-token layer 4.51 -> 4.44 ms a step).
+__device__ __forceinline__ void st_stream(void* p, u32x4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Two floats to a packed bf16 pair with one v_cvt_pk_bf16_f32 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -56,6 +56,12 @@ bool ffn_takes_gemv(int P, int E, int H, int F, int fmt) {
     return !use_gemm(P, E, H, F);
 }
 
+bool pair_mode_fits(int T, int k, int E, int H, int F, int fmt) {
+    const long P = (long)T * k;
+    return fmt == MOE_W_AWQ_G32_OM && T >= 1 && T <= kPairModeMaxT && P <= kPairModeMaxP &&
+           om_streams((int)P, E, H, F);
+}
+
 hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
     GroupedArgs a{};
     a.x = f.x;
@@ -71,6 +77,7 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
     a.offsets = f.offsets;
     a.sorted_pair = f.sorted_pair;
     a.slots = f.slots;
+    a.pair_expert = f.offsets ? nullptr : f.pair_expert;
     auto pj = [](const moe_proj& p) {
         ProjDev d;
         d.w = p.w;
@@ -96,6 +103,11 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
         if (err != hipSuccess) return err;
         a.x = xq;
         ws = static_cast<char*>(ws) + quant_x_bytes(f.T, f.H);
+    }
+    if (a.pair_expert) {
+        // rows by pair: only the output-major streaming GEMV takes them
+        if (!pair_mode_fits(f.T, f.k, a.E, a.H, a.F, f.ex->gate.fmt)) return hipErrorInvalidValue;
+        return launch_om_gemv(a, ws, s);
     }
     if (f.ex->gate.fmt == MOE_W_AWQ_G32_OM) {
         if (om_streams(a.P, a.offsets ? a.E : 1, a.H, a.F)) return launch_om_gemv(a, ws, s);

@@ -379,9 +379,9 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
                 const float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
                 const float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
                 if (row < nrows)
-                    *reinterpret_cast<uint4*>(&hbuf[(size_t)(m0 + row) * F + hcol + ch * 8]) =
-                        make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
-                                   pack_bf16x2(v1.z, v1.w));
+                    st_stream(&hbuf[(size_t)(m0 + row) * F + hcol + ch * 8],
+                              u32x4_t{pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
+                                      pack_bf16x2(v1.z, v1.w)});
             }
         } else if (a.out_f32) {
             float* out = static_cast<float*>(a.rows);
@@ -403,9 +403,9 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
                 const float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
                 const float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
                 if (row < nrows)
-                    *reinterpret_cast<uint4*>(&out[(size_t)(m0 + row) * H + ocol + ch * 8]) =
-                        make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
-                                   pack_bf16x2(v1.z, v1.w));
+                    st_stream(&out[(size_t)(m0 + row) * H + ocol + ch * 8],
+                              u32x4_t{pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
+                                      pack_bf16x2(v1.z, v1.w)});
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

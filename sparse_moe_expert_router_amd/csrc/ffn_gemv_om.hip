@@ -140,9 +140,9 @@ __host__ __device__ inline size_t ov_lds_bytes(const OvShape& h) {
 // in fp32 to gu [P][2 O]; MODE 1 writes the rows.
 template <int MODE, int PS, int R>
 __device__ __forceinline__ void ov_compute(const GroupedArgs& a, const OvShape& h, const OvCodes<PS>& cd, int m,
-                                           int c, int cl, int gb, int rc, int nr, const uint32_t* xrow,
-                                           const float* xsum, const uint16_t* ssc, const uint32_t* szr,
-                                           uint32_t msk, float* __restrict__ gu) {
+                                           int c, int cl, int gb, int rc, int nr, const int* prow,
+                                           const uint32_t* xrow, const float* xsum, const uint16_t* ssc,
+                                           const uint32_t* szr, uint32_t msk, float* __restrict__ gu) {
     const int znib = ov_nib(c & 7);
     float r[R];
 #pragma unroll
@@ -169,10 +169,11 @@ __device__ __forceinline__ void ov_compute(const GroupedArgs& a, const OvShape& 
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             if (i >= nr) break;
+            const int rid = prow ? prow[rc + i] : rc + i;
             if constexpr (MODE == 0) {
-                gu[(size_t)(rc + i) * (2 * h.O) + m * h.O + c] = r[i];
+                gu[(size_t)rid * (2 * h.O) + m * h.O + c] = r[i];
             } else {
-                const size_t o = (size_t)(rc + i) * h.O + c;
+                const size_t o = (size_t)rid * h.O + c;
                 if (a.out_f32) static_cast<float*>(a.rows)[o] = r[i];
                 else static_cast<uint16_t*>(a.rows)[o] = (uint16_t)f32_to_bf16_bits(r[i]);
             }
@@ -185,18 +186,47 @@ __device__ __forceinline__ void ov_compute(const GroupedArgs& a, const OvShape& 
 template <int MODE, int PS, int R>
 __device__ __forceinline__ void ov_run(const GroupedArgs& a, const OvShape& h, OvCodes<PS>& A, rsrc_t cw, int m,
                                        int st0, int st1, int cb, int cq, int j, int gb, int rc, int nr,
-                                       const uint32_t* xrow, const float* xsum, const uint16_t* ssc,
+                                       const int* prow, const uint32_t* xrow, const float* xsum, const uint16_t* ssc,
                                        const uint32_t* szr, uint32_t msk, float* __restrict__ gu) {
     OvCodes<PS> B;
     auto col = [&](int st) { return st * h.CS + 4 * cq + j; };
     auto voff = [&](int st) { return (uint32_t)col(st) * (h.I / 2) + 16u * gb; };
     for (int st = st0; st < st1; st += 2) {
         if (st + 1 < st1) ov_load<PS>(B, cw, voff(st + 1), h.NG);
-        ov_compute<MODE, PS, R>(a, h, A, m, col(st), col(st) - cb, gb, rc, nr, xrow, xsum, ssc, szr, msk, gu);
+        ov_compute<MODE, PS, R>(a, h, A, m, col(st), col(st) - cb, gb, rc, nr, prow, xrow, xsum, ssc, szr, msk, gu);
         if (st + 2 < st1) ov_load<PS>(A, cw, voff(st + 2), h.NG);
         if (st + 1 < st1)
-            ov_compute<MODE, PS, R>(a, h, B, m, col(st + 1), col(st + 1) - cb, gb, rc, nr, xrow, xsum, ssc, szr, msk,
-                                    gu);
+            ov_compute<MODE, PS, R>(a, h, B, m, col(st + 1), col(st + 1) - cb, gb, rc, nr, prow, xrow, xsum, ssc, szr,
+                                    msk, gu);
+    }
+}
+
+// Rows by pair (one wave): the pairs q with pe[q] == e, ascending, into
+// prow; info[0] = their count, info[1] = whether one precedes pair p.
+__device__ __forceinline__ void ov_pair_rows(const int32_t* __restrict__ pe, int P, int p, int e, int lane,
+                                             int* prow, int* info) {
+    constexpr int kB = 4;  // 64-pair chunks loaded at a time
+    const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
+    int n = 0;
+    bool dup = false;
+    for (int u0 = 0; u0 * kWave < P; u0 += kB) {
+        int v[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) v[u] = pe[min((u0 + u) * kWave + lane, P - 1)];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int q = (u0 + u) * kWave + lane;
+            const bool hit = q < P && v[u] == e;
+            const uint64_t mk = __ballot(hit);
+            dup |= __ballot(hit && q < p) != 0;
+            const int pos = n + __popcll(mk & below);
+            if (hit && pos < kPairModeMaxT) prow[pos] = q;
+            n += __popcll(mk);
+        }
+    }
+    if (lane == 0) {
+        info[0] = min(n, kPairModeMaxT);
+        info[1] = dup;
     }
 }
 
@@ -212,20 +242,30 @@ template <int MODE, int PS>
 __global__ __launch_bounds__(kOvThreads) __attribute__((amdgpu_waves_per_eu(ov_waves_per_simd(PS))))
 void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
     extern __shared__ __attribute__((aligned(16))) uint32_t ov_lds[];
+    __shared__ int prow_lds[kPairModeMaxT];  // rows by pair: this expert's pairs, ascending
+    __shared__ int pinfo[2];                 // their count, and whether an earlier pair has the expert
     uint32_t* xs = ov_lds;                                              // [4][I/2]
     float* xsum = reinterpret_cast<float*>(ov_lds + 2 * h.I);           // [G][4]
     uint16_t* ssc = reinterpret_cast<uint16_t*>(xsum + 4 * h.G);        // [G][CW]
     uint32_t* szr = reinterpret_cast<uint32_t*>(ssc + (size_t)h.G * h.CW);  // [G][CW/8]
-    int r0, r1;
-    const int e = a.offsets ? slot_expert(a.slots, blockIdx.y, &r0, &r1) : 0;
-    if (!a.offsets) {
-        r0 = 0;
-        r1 = a.T;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int r0 = 0, r1 = a.T, e = 0;
+    const int* prow = nullptr;
+    if (a.pair_expert) {
+        // workgroup y = pair p: it runs only when p is the first pair of its
+        // expert, and then takes every pair of that expert in ascending order
+        // (the rows a stable sort by expert would give it).  The pairs are
+        // scanned while the first codes are in flight (below); until then the
+        // workgroup has one row.
+        e = a.pair_expert[blockIdx.y];
+        r1 = 1;
+        prow = prow_lds;
+    } else if (a.offsets) {
+        e = slot_expert(a.slots, blockIdx.y, &r0, &r1);
+        if (e < 0) return;  // whole workgroup
     }
-    if (e < 0) return;  // whole workgroup
     const int I = h.I, O = h.O, G = h.G, nb8 = I / 8, nsets = O / h.CS;
     const int m = blockIdx.x / h.NWG, chunk = blockIdx.x % h.NWG;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int j = lane & 3, b = lane >> 2, gb = b % h.NG, cq = b / h.NG;
     const int cb = chunk * h.CW;
     const int st0 = (chunk * kOvWaves + wave) * h.SPW, st1 = min(st0 + h.SPW, nsets);
@@ -237,11 +277,16 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
     const rsrc_t cw = ov_rsrc(qw + (size_t)e * O * (I / 8), (uint32_t)O * (I / 2));
     const uint32_t msk = ov_mask();
     for (int rc = r0; rc < r1; rc += 4) {
-        const int nr = min(4, r1 - rc);
         OvCodes<PS> A;
         // the first set's codes are in flight while the workgroup stages
         if (st0 < st1) ov_load<PS>(A, cw, (uint32_t)(st0 * h.CS + 4 * cq + j) * (I / 2) + 16u * gb, h.NG);
-        __syncthreads();  // the previous chunk's rows have been read
+        if (prow && rc == r0 && wave == 0) ov_pair_rows(a.pair_expert, a.P, (int)blockIdx.y, e, lane, prow_lds, pinfo);
+        __syncthreads();  // the previous chunk's rows have been read; the pair scan is done
+        if (prow && rc == r0) {
+            if (pinfo[1]) return;  // whole workgroup: an earlier pair has the expert
+            r1 = pinfo[0];
+        }
+        const int nr = min(4, r1 - rc);
         if (rc == r0) {
             // scales and zero words of this workgroup's columns (coalesced)
             const int sv = h.CW / 8;  // 16-byte scale vectors, and zero words, a row
@@ -260,10 +305,10 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
             const int i = it / nb8, w8 = it % nb8;
             u32x4_t v;  // x0x1 x2x3 x4x5 x6x7
             if constexpr (MODE == 0) {
-                const int t = a.sorted_pair ? a.sorted_pair[rc + i] / a.k : rc + i;
+                const int t = prow ? prow[rc + i] / a.k : a.sorted_pair ? a.sorted_pair[rc + i] / a.k : rc + i;
                 v = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * I + 8 * w8);
             } else {
-                const float* gr = gu + (size_t)(rc + i) * (2 * I) + 8 * w8;
+                const float* gr = gu + (size_t)(prow ? prow[rc + i] : rc + i) * (2 * I) + 8 * w8;
                 const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gr), g1 = *reinterpret_cast<const f32x4_t*>(gr + 4);
                 const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(gr + I);
                 const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(gr + I + 4);
@@ -289,11 +334,11 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
         if (st0 < st1) {
             const uint32_t* xrow = xs + min(j, nr - 1) * (I / 2);  // rows past nr repeat the last
             if (nr == 1)
-                ov_run<MODE, PS, 1>(a, h, A, cw, m, st0, st1, cb, cq, j, gb, rc, nr, xrow, xsum, ssc, szr, msk, gu);
+                ov_run<MODE, PS, 1>(a, h, A, cw, m, st0, st1, cb, cq, j, gb, rc, nr, prow, xrow, xsum, ssc, szr, msk, gu);
             else if (nr == 2)
-                ov_run<MODE, PS, 2>(a, h, A, cw, m, st0, st1, cb, cq, j, gb, rc, nr, xrow, xsum, ssc, szr, msk, gu);
+                ov_run<MODE, PS, 2>(a, h, A, cw, m, st0, st1, cb, cq, j, gb, rc, nr, prow, xrow, xsum, ssc, szr, msk, gu);
             else
-                ov_run<MODE, PS, 4>(a, h, A, cw, m, st0, st1, cb, cq, j, gb, rc, nr, xrow, xsum, ssc, szr, msk, gu);
+                ov_run<MODE, PS, 4>(a, h, A, cw, m, st0, st1, cb, cq, j, gb, rc, nr, prow, xrow, xsum, ssc, szr, msk, gu);
         }
     }
 }
@@ -359,13 +404,15 @@ size_t om_gemv_ws_bytes(int P, int F) { return ov_table_bytes(P) + (size_t)P * 2
 hipError_t launch_om_gemv(const GroupedArgs& a0, void* ws, hipStream_t s) {
     GroupedArgs a = a0;
     char* w = static_cast<char*>(ws);
-    if (a.offsets) {
+    if (a.pair_expert) {
+        a.slots = nullptr;  // one workgroup slot per pair
+    } else if (a.offsets) {
         if (!a.slots) a.slots = launch_slot_table(a.offsets, a.E, a.P, reinterpret_cast<int4*>(w), s);
     } else {
         a.slots = nullptr;
     }
     float* gu = reinterpret_cast<float*>(w + ov_table_bytes(a.P));
-    const int slots = a.offsets ? (a.P < a.E ? a.P : a.E) : 1;
+    const int slots = a.pair_expert ? a.P : a.offsets ? (a.P < a.E ? a.P : a.E) : 1;
     hipError_t err = ov_launch<0>(a, a.H, a.F, slots, gu, s);
     if (err != hipSuccess) return err;
     return ov_launch<1>(a, a.F, a.H, slots, gu, s);

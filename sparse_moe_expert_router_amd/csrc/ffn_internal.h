@@ -30,6 +30,7 @@ struct GroupedArgs {
     const int32_t* offsets;     // [E+1] or nullptr (identity: E == 1, row r = token r)
     const int32_t* sorted_pair; // [P] or nullptr
     const int4* slots;          // GEMV work slots: (expert, first row, end row), expert -1 = none
+    const int32_t* pair_expert; // [P] expert of pair p, rows indexed by pair (offsets == nullptr), or nullptr
     ProjDev gate, up, down;
     int out_f32;
     void* rows;                 // [P][H]

@@ -42,11 +42,19 @@ struct FfnArgs {
     int out_f32;                  // 1: rows are fp32, else bf16
     void* rows;                   // [T*k][H]
     const int4* slots = nullptr;  // GEMV slot table already built (see launch_topk_permute), or nullptr
+    // [T*k] expert of each (token, slot) pair, with offsets == nullptr: rows
+    // are indexed by pair (row p = pair p), no permutation (see pair_mode_fits)
+    const int32_t* pair_expert = nullptr;
 };
 size_t ffn_ws_bytes(int T, int k, int E, int H, int F, int fmt);
 // whether a grouped call of P rows over E experts runs the streaming GEMV
 // kernels (which read a slot table) rather than an MFMA GEMM
 bool ffn_takes_gemv(int P, int E, int H, int F, int fmt);
+// whether a call of T tokens x k slots over E experts of format fmt can take
+// its rows by pair (FfnArgs::pair_expert): the output-major streaming GEMV,
+// at most kPairModeMaxT tokens and kPairModeMaxP pairs
+constexpr int kPairModeMaxT = 256, kPairModeMaxP = 1024;
+bool pair_mode_fits(int T, int k, int E, int H, int F, int fmt);
 // hidden and inter sizes the output-major AWQ GEMM takes
 bool om_gemm_supported(int H, int F);
 hipError_t launch_awq_to_om(const int32_t* src, int32_t* dst, int E, int K, int N, hipStream_t s);
@@ -56,7 +64,7 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int T, int n, float act_scal
                                  hipStream_t s);
 hipError_t launch_ffn(const FfnArgs& a, void* ws, hipStream_t s);
 
-// ---- combine (combine.hip)
+// ---- combine (combine.hip); pair_to_row == nullptr: row of pair p is p
 hipError_t launch_combine(const void* rows, int rows_f32, const int32_t* pair_to_row,
                           const float* gate, int T, int k, int H, const uint16_t* shared,
                           const float* shared_scale, uint16_t* y, hipStream_t s);

@@ -1,9 +1,10 @@
 """moe_layer (the whole layer in one library call) against the four calls it
 stands for, made one after the other: the same bits for every weight format,
-both routing paths (the single-workgroup selection that also builds the GEMV
-slot table, and the screened router for larger batches), both grouped-expert
-families (streaming GEMV and MFMA GEMM), with the shared expert on the same
-stream or on a side stream.  The four calls are themselves checked against
+every routing path (the single-workgroup selection that also builds the GEMV
+slot table; the per-token selection whose (token, slot) pairs the streaming
+kernels take directly, on output-major codes below 64 tokens; the screened
+router for larger batches), both grouped-expert families (streaming GEMV and
+MFMA GEMM), with the shared expert on the same stream or on a side stream.  The four calls are themselves checked against
 the oracle (test_gpu_layer.py, test_gpu_fullsize.py), and the layer call is
 also checked against the oracle directly on two formats."""
 import numpy as np
@@ -24,11 +25,19 @@ def _case(name):
         return workloads.scaled(workloads.get("decode_awq"), T=96)
     if name == "prefill_awq_om":   # output-major AWQ codes, MFMA GEMM, 40 rows per expert
         return workloads.scaled(workloads.get("prefill_awq"), T=2048)
+    # output-major codes below 64 tokens: the streaming kernels take their
+    # rows by (token, slot) pair, with no permutation
+    if name in ("decode_awq_om", "same_tokens_om"):
+        return workloads.get("decode_awq")
+    if name == "decode_awq_om_t1":
+        return workloads.scaled(workloads.get("decode_awq"), T=1)
+    if name == "decode_awq_om_t40":   # 400 pairs: the pair scan over seven 64-pair chunks
+        return workloads.scaled(workloads.get("decode_awq"), T=40)
     return workloads.get(name)
 
 
 CASES = ["tiny_bf16", "decode_bf16", "decode_awq", "decode_fp8", "decode_nvfp4", "gemm_bf16", "screened_awq",
-         "prefill_awq_om"]
+         "prefill_awq_om", "decode_awq_om", "decode_awq_om_t1", "decode_awq_om_t40", "same_tokens_om"]
 
 
 @pytest.mark.parametrize("name", CASES)
@@ -38,7 +47,10 @@ def test_layer_call_equals_the_four_calls(name, side):
     w = _case(name)
     print(f"case {name} side={side} T={w.T} E={w.E} fmt={w.fmt}", flush=True)
     d = workloads.generate(w, device="cuda")
-    bank = moe.awq_to_output_major(d["experts"]) if name.endswith("_om") else d["experts"]
+    if name == "same_tokens_om":
+        # every token routes to the same k experts: 16 rows each, in chunks of 4
+        d["x"] = d["x"][:1].expand_as(d["x"]).contiguous()
+    bank = moe.awq_to_output_major(d["experts"]) if "_om" in name else d["experts"]
     ref, mid = moe.moe_layer(d["x"], d["router"], w.k, bank, d["shared"], keep_intermediates=True)
     ref = ref.clone()
     idx = torch.full((w.T, w.k), -1, dtype=torch.int32, device="cuda")
