@@ -231,8 +231,8 @@ __device__ __forceinline__ void ov_pair_rows(const int32_t* __restrict__ pe, int
 }
 
 // Waves per SIMD: four (128 registers) unless the codes of two sets in flight
-// need more (from 5 passes), then three or two, rather than spilling.
-constexpr int ov_waves_per_simd(int PS) { return PS >= 7 ? 2 : PS >= 5 ? 3 : 4; }
+// need more (from 4 passes), then three or two, rather than spilling.
+constexpr int ov_waves_per_simd(int PS) { return PS >= 6 ? 2 : PS >= 4 ? 3 : 4; }
 
 // grid (NM x NWG column chunks, expert slot); block 4 waves, each wave SPW
 // consecutive column sets of one projection.  MODE 0: gate and up -> gu
@@ -276,21 +276,32 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
     const uint16_t* sc = MODE == 1 ? a.down.scales : m ? a.up.scales : a.gate.scales;
     const rsrc_t cw = ov_rsrc(qw + (size_t)e * O * (I / 8), (uint32_t)O * (I / 2));
     const uint32_t msk = ov_mask();
-    for (int rc = r0; rc < r1; rc += 4) {
-        OvCodes<PS> A;
-        // the first set's codes are in flight while the workgroup stages
-        if (st0 < st1) ov_load<PS>(A, cw, (uint32_t)(st0 * h.CS + 4 * cq + j) * (I / 2) + 16u * gb, h.NG);
-        if (prow && rc == r0 && wave == 0) ov_pair_rows(a.pair_expert, a.P, (int)blockIdx.y, e, lane, prow_lds, pinfo);
-        __syncthreads();  // the previous chunk's rows have been read; the pair scan is done
-        if (prow && rc == r0) {
-            if (pinfo[1]) return;  // whole workgroup: an earlier pair has the expert
-            r1 = pinfo[0];
-        }
-        const int nr = min(4, r1 - rc);
-        if (rc == r0) {
-            // scales and zero words of this workgroup's columns (coalesced)
-            const int sv = h.CW / 8;  // 16-byte scale vectors, and zero words, a row
-            for (int it = threadIdx.x; it < G * sv; it += kOvThreads) {
+    // Staging: the scales and zero words of the workgroup's columns go from
+    // memory straight into LDS (16- and 4-byte buffer loads to LDS: item
+    // it = g sv + v of a wave lands at its LDS base + lane x size), all in
+    // flight at once and in no register; the rows go through registers in
+    // batches whose loads are all issued before the first is used.  (A
+    // load-then-store loop waited a memory round trip per item: five for the
+    // scales and zero words, two for the rows.)
+    constexpr int kXB = MODE == 0 ? 2 : 1;  // row items a thread loads at once
+    const int sv = h.CW / 8;                // 16-byte scale vectors, and zero words, a group row
+    const int nst = G * sv;
+    const rsrc_t rsc = ov_rsrc(sc + (size_t)e * G * O, (uint32_t)G * O * 2u);
+    const rsrc_t rzr = ov_rsrc(qz + (size_t)e * G * (O / 8), (uint32_t)G * (O / 8) * 4u);
+    auto stage_scales = [&]() {
+        if (nst % kOvThreads == 0) {
+            // every wave's 64 items exist; columns past O read the next group
+            // row or, past the last, 0 (those columns are never computed)
+            for (int u0 = 0; u0 < nst; u0 += kOvThreads) {
+                const int it = u0 + threadIdx.x, g = it / sv, c0 = cb + 8 * (it % sv);
+                const int wb = u0 + wave * kWave;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (__attribute__((address_space(3))) void*)(ssc + 8 * wb), 16,
+                                                         (g * O + c0) * 2, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rzr, (__attribute__((address_space(3))) void*)(szr + wb), 4,
+                                                         (g * (O / 8) + c0 / 8) * 4, 0, 0, 0);
+            }
+        } else {
+            for (int it = threadIdx.x; it < nst; it += kOvThreads) {
                 const int g = it / sv, v = it % sv, c0 = cb + 8 * v;
                 u32x4_t val = {0u, 0u, 0u, 0u};
                 if (c0 < O) val = *reinterpret_cast<const u32x4_t*>(sc + ((size_t)e * G + g) * O + c0);
@@ -298,38 +309,76 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
                 szr[g * sv + v] = c0 < O ? (uint32_t)qz[((size_t)e * G + g) * (O / 8) + c0 / 8] : 0u;
             }
         }
+    };
+    for (int rc = r0; rc < r1; rc += 4) {
+        OvCodes<PS> A;
+        // the first set's codes, the scales and the zero words are in flight
+        // while the workgroup finds its rows and stages them
+        if (st0 < st1) ov_load<PS>(A, cw, (uint32_t)(st0 * h.CS + 4 * cq + j) * (I / 2) + 16u * gb, h.NG);
+        if (rc == r0) stage_scales();
+        if (prow && rc == r0 && wave == 0) ov_pair_rows(a.pair_expert, a.P, (int)blockIdx.y, e, lane, prow_lds, pinfo);
+        __syncthreads();  // the previous chunk's rows have been read; the pair scan is done
+        if (prow && rc == r0) {
+            if (pinfo[1]) return;  // whole workgroup: an earlier pair has the expert
+            r1 = pinfo[0];
+        }
+        const int nr = min(4, r1 - rc);
         // rows rc .. rc+nr-1 into LDS, and their group sums: a thread sums its
         // 8 inputs in order, then the 4 threads of a group (consecutive lanes,
         // all active together) add theirs in a fixed order
-        for (int it = threadIdx.x; it < nr * nb8; it += kOvThreads) {
-            const int i = it / nb8, w8 = it % nb8;
-            u32x4_t v;  // x0x1 x2x3 x4x5 x6x7
-            if constexpr (MODE == 0) {
-                const int t = prow ? prow[rc + i] / a.k : a.sorted_pair ? a.sorted_pair[rc + i] / a.k : rc + i;
-                v = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * I + 8 * w8);
-            } else {
-                const float* gr = gu + (size_t)(prow ? prow[rc + i] : rc + i) * (2 * I) + 8 * w8;
-                const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gr), g1 = *reinterpret_cast<const f32x4_t*>(gr + 4);
-                const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(gr + I);
-                const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(gr + I + 4);
-                v.x = pack_bf16x2(silu(g0.x) * u0.x, silu(g0.y) * u0.y);
-                v.y = pack_bf16x2(silu(g0.z) * u0.z, silu(g0.w) * u0.w);
-                v.z = pack_bf16x2(silu(g1.x) * u1.x, silu(g1.y) * u1.y);
-                v.w = pack_bf16x2(silu(g1.z) * u1.z, silu(g1.w) * u1.w);
-            }
-            u32x4_t o;
-            o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // (x0, x4)
-            o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // (x1, x5)
-            o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // (x2, x6)
-            o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // (x3, x7)
-            *reinterpret_cast<u32x4_t*>(&xs[i * (I / 2) + 4 * w8]) = o;
-            float sum = 0.0f;
+        const int nx = nr * nb8;
+        for (int x0 = 0; x0 < nx; x0 += kOvThreads * kXB) {
+            u32x4_t ld[kXB][MODE == 0 ? 1 : 4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) sum += bf16_to_f32(v[u] & 0xFFFFu) + bf16_to_f32(v[u] >> 16);
-            sum += __shfl_xor(sum, 1, kWave);
-            sum += __shfl_xor(sum, 2, kWave);
-            if ((w8 & 3) == 0) xsum[4 * (w8 >> 2) + i] = sum;
+            for (int u = 0; u < kXB; ++u) {
+                const int it = x0 + threadIdx.x + kOvThreads * u;
+                if (it < nx) {
+                    const int i = it / nb8, w8 = it % nb8;
+                    if constexpr (MODE == 0) {
+                        const int t = prow ? prow[rc + i] / a.k : a.sorted_pair ? a.sorted_pair[rc + i] / a.k : rc + i;
+                        ld[u][0] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * I + 8 * w8);
+                    } else {
+                        const float* gr = gu + (size_t)(prow ? prow[rc + i] : rc + i) * (2 * I) + 8 * w8;
+                        ld[u][0] = *reinterpret_cast<const u32x4_t*>(gr);
+                        ld[u][1] = *reinterpret_cast<const u32x4_t*>(gr + 4);
+                        ld[u][2] = *reinterpret_cast<const u32x4_t*>(gr + I);
+                        ld[u][3] = *reinterpret_cast<const u32x4_t*>(gr + I + 4);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kXB; ++u) {
+                const int it = x0 + threadIdx.x + kOvThreads * u;
+                if (it >= nx) continue;  // whole groups of 4 lanes (nb8 % 4 == 0)
+                const int i = it / nb8, w8 = it % nb8;
+                u32x4_t v;  // x0x1 x2x3 x4x5 x6x7
+                if constexpr (MODE == 0) {
+                    v = ld[u][0];
+                } else {
+                    const f32x4_t g0 = __builtin_bit_cast(f32x4_t, ld[u][0]), g1 = __builtin_bit_cast(f32x4_t, ld[u][1]);
+                    const f32x4_t u0 = __builtin_bit_cast(f32x4_t, ld[u][2]), u1 = __builtin_bit_cast(f32x4_t, ld[u][3]);
+                    v.x = pack_bf16x2(silu(g0.x) * u0.x, silu(g0.y) * u0.y);
+                    v.y = pack_bf16x2(silu(g0.z) * u0.z, silu(g0.w) * u0.w);
+                    v.z = pack_bf16x2(silu(g1.x) * u1.x, silu(g1.y) * u1.y);
+                    v.w = pack_bf16x2(silu(g1.z) * u1.z, silu(g1.w) * u1.w);
+                }
+                u32x4_t o;
+                o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // (x0, x4)
+                o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // (x1, x5)
+                o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // (x2, x6)
+                o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // (x3, x7)
+                *reinterpret_cast<u32x4_t*>(&xs[i * (I / 2) + 4 * w8]) = o;
+                float sum = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sum += bf16_to_f32(v[q] & 0xFFFFu) + bf16_to_f32(v[q] >> 16);
+                sum += __shfl_xor(sum, 1, kWave);
+                sum += __shfl_xor(sum, 2, kWave);
+                if ((w8 & 3) == 0) xsum[4 * (w8 >> 2) + i] = sum;
+            }
         }
+        // every load of this wave has landed (the scales and zero words in
+        // LDS among them) before the barrier publishes the stage
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) (bits 3:0 and 15:14), expcnt and lgkmcnt at their maxima
         __syncthreads();
         if (st0 < st1) {
             const uint32_t* xrow = xs + min(j, nr - 1) * (I / 2);  // rows past nr repeat the last
