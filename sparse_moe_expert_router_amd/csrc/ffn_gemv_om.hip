@@ -20,9 +20,12 @@
 // Unpacking: a code word w (8 inputs) gives the bf16 pairs (n0,n4), (n1,n5),
 // (n2,n6), (n3,n7) as 128 + q, one v_and_or each (after a shift for the last
 // three); (n0,n4),(n1,n5) feed one MFMA and (n2,n6),(n3,n7) the next.  The A
-// rows (token rows gathered through sorted_pair for gate/up, h rows for down;
-// at most 4 a chunk) are staged in LDS with every 8 inputs in the order
-// 0,4,1,5,2,6,3,7 so that a 16-byte LDS read is the A operand of two MFMAs.
+// rows (token rows gathered through sorted_pair, or taken by (token, slot)
+// pair, for gate/up; h rows for down; at most 4 a chunk) are staged in LDS
+// with every 8 inputs in the order 0,4,1,5,2,6,3,7 so that a 16-byte LDS read
+// is the A operand of two MFMAs.  The codes stream with the non-temporal hint;
+// the scales and zero words of a workgroup's columns go to LDS once, by
+// buffer loads to LDS issued with the first codes.
 // 8 MFMAs give, per block, D = sum_{i in g} x_i (128 + q_i) for the 4 rows;
 // the group's contribution s (D - (128 + z) sum_{i in g} x_i) is added in
 // fp32 for the chunk's real rows only, then the NG blocks of a column are
