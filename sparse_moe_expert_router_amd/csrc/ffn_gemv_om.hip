@@ -31,9 +31,11 @@
 // fp32 for the chunk's real rows only, then the NG blocks of a column are
 // summed across lanes in a fixed order (results are deterministic).
 //
-// Gate/up: a wave computes gate and up of the same 4 columns (NG = 16 at
-// in = 2560) and writes h = bf16(silu(gate) up); down: 16 columns a wave
-// (NG = 4 at in = 640) written to the rows.  No partial sums leave a wave.
+// Gate/up (MODE 0): workgroups of the gate and of the up projection each
+// write their columns in fp32 (4 columns a set at in = 2560, NG = 16); the
+// down pass (MODE 1, 16 columns a set at in = 640, NG = 4) forms
+// h = bf16(silu(gate) up) while staging its rows, and writes the output rows.
+// No partial sums leave a wave.
 #include "ffn_internal.h"
 
 namespace moe {
@@ -234,8 +236,8 @@ __device__ __forceinline__ void ov_pair_rows(const int32_t* __restrict__ pe, int
 }
 
 // Waves per SIMD: four (128 registers) unless the codes of two sets in flight
-// need more (from 4 passes), then three or two, rather than spilling.
-constexpr int ov_waves_per_simd(int PS) { return PS >= 6 ? 2 : PS >= 4 ? 3 : 4; }
+// need more (from 3 passes), then three or two, rather than spilling.
+constexpr int ov_waves_per_simd(int PS) { return PS >= 6 ? 2 : PS >= 3 ? 3 : 4; }
 
 // grid (NM x NWG column chunks, expert slot); block 4 waves, each wave SPW
 // consecutive column sets of one projection.  MODE 0: gate and up -> gu
@@ -287,6 +289,7 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
     // load-then-store loop waited a memory round trip per item: five for the
     // scales and zero words, two for the rows.)
     constexpr int kXB = MODE == 0 ? 2 : 1;  // row items a thread loads at once
+    static_assert(MODE != 0 || kOvMaxIn / 8 <= kOvThreads * kXB, "a row's items fit one batch");
     const int sv = h.CW / 8;                // 16-byte scale vectors, and zero words, a group row
     const int nst = G * sv;
     const rsrc_t rsc = ov_rsrc(sc + (size_t)e * G * O, (uint32_t)G * O * 2u);
@@ -319,18 +322,61 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
         // while the workgroup finds its rows and stages them
         if (st0 < st1) ov_load<PS>(A, cw, (uint32_t)(st0 * h.CS + 4 * cq + j) * (I / 2) + 16u * gb, h.NG);
         if (rc == r0) stage_scales();
-        if (prow && rc == r0 && wave == 0) ov_pair_rows(a.pair_expert, a.P, (int)blockIdx.y, e, lane, prow_lds, pinfo);
+        // gate/up: the first row's token is known before the pair scan (the
+        // workgroup's own pair, or the slot's first row), so its inputs load
+        // now as well
+        // stage item (row i, inputs 8 w8 .. +7) from its 8 bf16 inputs v: LDS
+        // in the order 0,4,1,5,2,6,3,7, and the group sums (a thread sums its
+        // 8 inputs in order, then the 4 threads of a group, consecutive lanes
+        // all active together, add theirs in a fixed order)
+        auto stage_item = [&](int i, int w8, const u32x4_t& v) {
+            u32x4_t o;
+            o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // (x0, x4)
+            o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // (x1, x5)
+            o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // (x2, x6)
+            o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // (x3, x7)
+            *reinterpret_cast<u32x4_t*>(&xs[i * (I / 2) + 4 * w8]) = o;
+            float sum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sum += bf16_to_f32(v[q] & 0xFFFFu) + bf16_to_f32(v[q] >> 16);
+            sum += __shfl_xor(sum, 1, kWave);
+            sum += __shfl_xor(sum, 2, kWave);
+            if ((w8 & 3) == 0) xsum[4 * (w8 >> 2) + i] = sum;
+        };
+        // gate/up: the first row's token is known before the pair scan (the
+        // workgroup's own pair, or the slot's first row), so its inputs load
+        // with the first codes and are staged before the barrier (no earlier
+        // chunk reads the stage); wave 0 scans the pairs first
+        int first = 0;  // first item staged after the barrier
+        if constexpr (MODE == 0) {
+            if (rc == r0) {
+                const int t0 = prow ? (int)blockIdx.y / a.k : a.sorted_pair ? a.sorted_pair[r0] / a.k : r0;
+                u32x4_t pre[kXB];
+#pragma unroll
+                for (int u = 0; u < kXB; ++u) {
+                    const int it = threadIdx.x + kOvThreads * u;
+                    if (it < nb8) pre[u] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)t0 * I + 8 * it);
+                }
+                if (prow && wave == 0) ov_pair_rows(a.pair_expert, a.P, (int)blockIdx.y, e, lane, prow_lds, pinfo);
+#pragma unroll
+                for (int u = 0; u < kXB; ++u) {
+                    const int it = threadIdx.x + kOvThreads * u;
+                    if (it < nb8) stage_item(0, it, pre[u]);
+                }
+                first = nb8;
+            }
+        }
+        if (MODE != 0 && prow && rc == r0 && wave == 0)
+            ov_pair_rows(a.pair_expert, a.P, (int)blockIdx.y, e, lane, prow_lds, pinfo);
         __syncthreads();  // the previous chunk's rows have been read; the pair scan is done
         if (prow && rc == r0) {
             if (pinfo[1]) return;  // whole workgroup: an earlier pair has the expert
             r1 = pinfo[0];
         }
         const int nr = min(4, r1 - rc);
-        // rows rc .. rc+nr-1 into LDS, and their group sums: a thread sums its
-        // 8 inputs in order, then the 4 threads of a group (consecutive lanes,
-        // all active together) add theirs in a fixed order
+        // the chunk's other rows, in batches whose loads all go out first
         const int nx = nr * nb8;
-        for (int x0 = 0; x0 < nx; x0 += kOvThreads * kXB) {
+        for (int x0 = first; x0 < nx; x0 += kOvThreads * kXB) {
             u32x4_t ld[kXB][MODE == 0 ? 1 : 4];
 #pragma unroll
             for (int u = 0; u < kXB; ++u) {
@@ -365,18 +411,7 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
                     v.z = pack_bf16x2(silu(g1.x) * u1.x, silu(g1.y) * u1.y);
                     v.w = pack_bf16x2(silu(g1.z) * u1.z, silu(g1.w) * u1.w);
                 }
-                u32x4_t o;
-                o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // (x0, x4)
-                o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // (x1, x5)
-                o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // (x2, x6)
-                o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // (x3, x7)
-                *reinterpret_cast<u32x4_t*>(&xs[i * (I / 2) + 4 * w8]) = o;
-                float sum = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) sum += bf16_to_f32(v[q] & 0xFFFFu) + bf16_to_f32(v[q] >> 16);
-                sum += __shfl_xor(sum, 1, kWave);
-                sum += __shfl_xor(sum, 2, kWave);
-                if ((w8 & 3) == 0) xsum[4 * (w8 >> 2) + i] = sum;
+                stage_item(i, w8, v);
             }
         }
         // every load of this wave has landed (the scales and zero words in
