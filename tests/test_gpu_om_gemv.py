@@ -1,7 +1,9 @@
 """The streaming GEMV on output-major AWQ codes (decode-sized calls: fewer than
 32 rows per active expert) against the oracle: the full layer geometry, both
 projection shapes the pass split takes (1 to 5 passes, 16, 8 and 4 blocks a
-column), experts with more rows than one 4-row chunk (ragged chunks), the
+column), experts with more rows than one 4-row chunk (ragged chunks), a
+hidden size whose LDS stage takes half the column sets a wave (hidden 3584:
+the scales and zero words staged through registers, not by loads to LDS), the
 one-expert identity call of a shared expert, a single token, and a shape the
 GEMV does not take (hidden 8192, which falls back to the MFMA GEMM)."""
 import numpy as np
@@ -36,6 +38,7 @@ def _routing(T, k, E, seed, heavy=None):
     (12, 16, 2, 512, 384, 7),         # 16 blocks x 1 pass; 4 blocks x 3 passes
     (6, 8, 3, 1024, 256, None),       # 16 blocks x 2 passes; 8 blocks x 1 pass
     (1, 32, 4, 2560, 640, None),      # one token
+    (5, 8, 2, 3584, 256, None),       # 7 passes: half the sets a wave, scales staged through registers
     (4, 2, 1, 8192, 128, None),       # hidden beyond the GEMV's LDS stage: the MFMA GEMM
 ])
 def test_om_gemv_matches_oracle(T, E, k, H, F, heavy):
