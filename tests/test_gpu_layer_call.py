@@ -2,7 +2,8 @@
 stands for, made one after the other: the same bits for every weight format,
 every routing path (the single-workgroup selection that also builds the GEMV
 slot table; the per-token selection whose (token, slot) pairs the streaming
-kernels take directly, on output-major codes below 64 tokens; the screened
+kernels take directly, on output-major codes below 64 tokens, at 1 to 63
+tokens and over 384 or 512 experts; the screened
 router for larger batches), both grouped-expert families (streaming GEMV and
 MFMA GEMM), with the shared expert on the same stream or on a side stream.  The four calls are themselves checked against
 the oracle (test_gpu_layer.py, test_gpu_fullsize.py), and the layer call is
@@ -33,11 +34,16 @@ def _case(name):
         return workloads.scaled(workloads.get("decode_awq"), T=1)
     if name == "decode_awq_om_t40":   # 400 pairs: the pair scan over seven 64-pair chunks
         return workloads.scaled(workloads.get("decode_awq"), T=40)
+    if name == "decode_awq_om_t63":   # 630 pairs: three batches of the pair scan, the largest fused batch
+        return workloads.scaled(workloads.get("decode_awq"), T=63)
+    if name == "decode_awq_om_e384":  # a 384-expert bank (E384of512 pruning) at decode
+        return workloads.scaled(workloads.get("decode_awq"), E=384)
     return workloads.get(name)
 
 
 CASES = ["tiny_bf16", "decode_bf16", "decode_awq", "decode_fp8", "decode_nvfp4", "gemm_bf16", "screened_awq",
-         "prefill_awq_om", "decode_awq_om", "decode_awq_om_t1", "decode_awq_om_t40", "same_tokens_om"]
+         "prefill_awq_om", "decode_awq_om", "decode_awq_om_t1", "decode_awq_om_t40", "decode_awq_om_t63",
+         "decode_awq_om_e384", "same_tokens_om"]
 
 
 @pytest.mark.parametrize("name", CASES)
