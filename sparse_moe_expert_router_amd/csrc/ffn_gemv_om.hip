@@ -322,9 +322,6 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
         // while the workgroup finds its rows and stages them
         if (st0 < st1) ov_load<PS>(A, cw, (uint32_t)(st0 * h.CS + 4 * cq + j) * (I / 2) + 16u * gb, h.NG);
         if (rc == r0) stage_scales();
-        // gate/up: the first row's token is known before the pair scan (the
-        // workgroup's own pair, or the slot's first row), so its inputs load
-        // now as well
         // stage item (row i, inputs 8 w8 .. +7) from its 8 bf16 inputs v: LDS
         // in the order 0,4,1,5,2,6,3,7, and the group sums (a thread sums its
         // 8 inputs in order, then the 4 threads of a group, consecutive lanes
@@ -370,7 +367,13 @@ void ov_kernel(GroupedArgs a, OvShape h, float* __restrict__ gu) {
             ov_pair_rows(a.pair_expert, a.P, (int)blockIdx.y, e, lane, prow_lds, pinfo);
         __syncthreads();  // the previous chunk's rows have been read; the pair scan is done
         if (prow && rc == r0) {
-            if (pinfo[1]) return;  // whole workgroup: an earlier pair has the expert
+            if (pinfo[1]) {
+                // whole workgroup: an earlier pair has the expert.  Its loads
+                // to LDS land before it ends, so that none writes the LDS of
+                // a workgroup that takes its place
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                return;
+            }
             r1 = pinfo[0];
         }
         const int nr = min(4, r1 - rc);
