@@ -86,14 +86,39 @@ def test_layer_call_matches_oracle(name):
     check_close(y.float().cpu().numpy(), ref_y, name)
 
 
-def test_layer_call_without_shared_expert():
+@pytest.mark.parametrize("om", [False, True])
+def test_layer_call_without_shared_expert(om):
     moe = require_gpu()
     w = workloads.get("decode_awq")
     d = workloads.generate(w, device="cuda")
-    ref = moe.moe_layer(d["x"], d["router"], w.k, d["experts"], None).clone()
-    y = moe.layer(d["x"], d["router"], w.k, d["experts"], None)
+    bank = moe.awq_to_output_major(d["experts"]) if om else d["experts"]
+    ref = moe.moe_layer(d["x"], d["router"], w.k, bank, None).clone()
+    y = moe.layer(d["x"], d["router"], w.k, bank, None)
     torch.cuda.synchronize()
     assert torch.equal(y, ref)
+
+
+@pytest.mark.parametrize("T", [1, 16, 63])
+@pytest.mark.parametrize("side", [False, True])
+def test_layer_call_pairs_with_shared_scale(T, side):
+    """Rows by (token, slot) pair on output-major codes, with a per-token
+    shared scale, the shared expert on the same stream or on a side stream:
+    the same bits as the four calls, on three calls in a row with different
+    tokens in between (nothing of one call's intermediates leaks into the
+    next)."""
+    moe = require_gpu()
+    w = workloads.scaled(workloads.get("decode_awq"), T=T)
+    print(f"case T={T} side={side}", flush=True)
+    d = workloads.generate(w, seed=11, device="cuda")
+    bank = moe.awq_to_output_major(d["experts"])
+    sc = torch.linspace(-0.75, 1.25, w.T, device="cuda")
+    x2 = workloads.generate(w, seed=12, device="cuda")["x"]
+    s = torch.cuda.Stream() if side else None
+    for x in (d["x"], x2, d["x"]):
+        ref = moe.moe_layer(x, d["router"], w.k, bank, d["shared"], shared_scale=sc).clone()
+        y = moe.layer(x, d["router"], w.k, bank, d["shared"], shared_scale=sc, side_stream=s)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
 
 
 def test_prepared_layer_call_and_routed_events():
