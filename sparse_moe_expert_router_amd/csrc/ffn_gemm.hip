@@ -25,12 +25,9 @@
 // bits), fma(m, s, c) = (q - z) * s exactly, then one RNE to bf16.  The four
 // rows of a column are contiguous in the K-major LDS tile: one 8-byte store.
 //
-// FP8 and NVFP4 B tiles are widened to bf16 on the way into LDS (both are
-// exact in bf16: an E4M3 code times its fp32 block scale is rounded once; an
-// E2M1 value times its E4M3 group scale has at most 6 significant bits).  For
-// NVFP4 the activations arrive quantised, the global factors (activation times
-// weight global scale) multiply the accumulators, and the gate/up epilogue
-// quantises h per 16 columns for the down pass.
+// FP8 B tiles are widened to bf16 on the way into LDS (an E4M3 code times its
+// fp32 block scale, rounded once).  NVFP4 banks run on the register-B GEMM
+// (ffn_gemm_om.hip), whose B words hold the same 8 consecutive inputs.
 //
 // Tiles are enumerated per expert (ceil(rows / BM) each) by a small kernel;
 // workgroup ids are remapped so that each XCD (ids are dealt round-robin over
@@ -38,7 +35,6 @@
 // tile adjacent: the A rows and the expert's weights are then reused from that
 // XCD's L2.
 #include "ffn_internal.h"
-#include "nvfp4.h"
 
 namespace moe {
 
@@ -202,38 +198,14 @@ __device__ __forceinline__ void fp8_store_chunk(uint4 c, float sc, uint16_t* Bs,
     *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh + 1)]) = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// NVFP4 B tile: chunk q (< BPER/2) is B-column q/2, inputs 16*(q%2)..+15 of
-// the step: 16 E2M1 codes (8 bytes, low nibble first) and one E4M3 scale s;
-// each value e2m1 * s is exact in bf16.
-__device__ __forceinline__ void nvfp4_store_chunk(uint4 c, uint32_t sbyte, uint16_t* Bs, int q) {
-    const float sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)sbyte, false)[0];
-    const uint32_t cw[2] = {c.x, c.y};
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], 1.0f, 0);
-        const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], 1.0f, 1);
-        const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], 1.0f, 2);
-        const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], 1.0f, 3);
-        o[4 * i + 0] = pack_bf16x2(v0[0] * sc, v0[1] * sc);
-        o[4 * i + 1] = pack_bf16x2(v1[0] * sc, v1[1] * sc);
-        o[4 * i + 2] = pack_bf16x2(v2[0] * sc, v2[1] * sc);
-        o[4 * i + 3] = pack_bf16x2(v3[0] * sc, v3[1] * sc);
-    }
-    const int bc = q / 2, kh = q % 2;
-    *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh)]) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh + 1)]) = make_uint4(o[4], o[5], o[6], o[7]);
-}
-
 // Registers of one K step -> LDS stage (A chunks; bf16 B chunks or dequantised AWQ words).
 template <int MODE, int WF, int BM>
 __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APER],
                                             const uint4 (&rb)[GemmShape<BM>::BPER],
                                             const uint32_t (&rw)[GemmShape<BM>::RPT], const float2* Ps,
                                             uint16_t* As, uint16_t* Bs, int tid) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32, FP8
     (void)FP8;
-    (void)NV4;
     using S = GemmShape<BM>;
 #pragma unroll
     for (int i = 0; i < S::APER; ++i) {
@@ -244,9 +216,6 @@ __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APE
 #pragma unroll
         for (int i = 0; i < S::BPER / 2; ++i)
             fp8_store_chunk(rb[i], __uint_as_float(rw[i]), Bs, tid + i * S::NT);
-    } else if (NV4) {
-#pragma unroll
-        for (int i = 0; i < S::BPER / 2; ++i) nvfp4_store_chunk(rb[i], rw[i], Bs, tid + i * S::NT);
     } else if (!AWQ) {
 #pragma unroll
         for (int i = 0; i < S::BPER; ++i) {
@@ -286,7 +255,7 @@ __device__ __forceinline__ bf16x8_t a_frag(const uint16_t* As, int mi, int wm, i
 
 // A K step is cut into 8 slices of PER = TM*TN/8 MFMAs.  Slices 0..kPipeSplit-1
 // (step_pre) also store the next step's LDS stage (A chunks, and bf16 B chunks
-// or the dequantised AWQ/FP8/NVFP4 columns), then the block barrier makes that
+// or the dequantised AWQ/FP8 columns), then the block barrier makes that
 // stage visible, and the remaining slices (step_post) read the next step's
 // fragments while this step's last MFMAs run.  With three LDS stages nothing
 // is written to a stage that another wave may still be reading: stage kt+1 is
@@ -312,7 +281,7 @@ __device__ __forceinline__ void step_pre(bf16x8_t (&af)[GemmShape<BM>::TM], cons
                                          const uint4 (&rb)[GemmShape<BM>::BPER],
                                          const uint32_t (&rw)[GemmShape<BM>::RPT], const float2* Ps, uint16_t* As,
                                          uint16_t* Bs, int tid, const uint16_t* Acur, int wm, int lane) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32, FP8
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
     constexpr int PER = TM * TN / 8, SB = kPipeSplit;
@@ -334,8 +303,6 @@ __device__ __forceinline__ void step_pre(bf16x8_t (&af)[GemmShape<BM>::TM], cons
         }
         if (FP8) {
             if (j < S::BPER / 2) fp8_store_chunk(rb[j], __uint_as_float(rw[j]), Bs, tid + j * S::NT);
-        } else if (NV4) {
-            if (j < S::BPER / 2) nvfp4_store_chunk(rb[j], rw[j], Bs, tid + j * S::NT);
         } else if (!AWQ) {
             if (j < S::BPER) {
                 const int q = tid + j * S::NT;
@@ -384,9 +351,8 @@ template <int MODE, int WF, int BM>
 __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_eu(GemmShape<BM>::MINW))) void grouped_gemm_kernel(GroupedArgs a,
                                                                const int32_t* __restrict__ tiles,
                                                                uint16_t* __restrict__ hbuf, int NT) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2, NV4 = WF == 3;  // B format: bf16, AWQ g32, FP8, NVFP4
+    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32, FP8
     (void)FP8;
-    (void)NV4;
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN, APER = S::APER, BPER = S::BPER, NTHR = S::NT;
     __shared__ __attribute__((aligned(16))) uint16_t As[3][BM * kBK];
@@ -429,7 +395,6 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
     const uint16_t* bsrc[BPER];
     const uint8_t* fsrc[BPER / 2 > 0 ? BPER / 2 : 1];   // FP8 code chunks
     const float* fscl[BPER / 2 > 0 ? BPER / 2 : 1];     // their block-scale rows
-    const uint8_t* gsrc[BPER / 2 > 0 ? BPER / 2 : 1];   // NVFP4: group-scale rows
     const int32_t* wsrc = nullptr;
     const int32_t* zsrc = nullptr;
     const uint16_t* ssrc = nullptr;
@@ -447,18 +412,6 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
             const int col = MODE == MODE_GATEUP ? n0 + bc % (kBN / 2) : n0 + bc;
             fsrc[i] = codes + (size_t)e * NOUT * K + (size_t)col * K + kh * 16;
             fscl[i] = bsc + ((size_t)e * (NOUT / 128) + col / 128) * (K / 128);
-        }
-    } else if (NV4) {
-#pragma unroll
-        for (int i = 0; i < BPER / 2; ++i) {
-            const int q = tid + i * NTHR;
-            const int bc = q / 2, kh = q % 2;
-            const bool upm = MODE == MODE_GATEUP && bc >= kBN / 2;
-            const uint8_t* codes = MODE == MODE_DOWN ? a.down.codes : (upm ? a.up.codes : a.gate.codes);
-            const uint8_t* gsc = MODE == MODE_DOWN ? a.down.gscales : (upm ? a.up.gscales : a.gate.gscales);
-            const int col = MODE == MODE_GATEUP ? n0 + bc % (kBN / 2) : n0 + bc;
-            fsrc[i] = codes + ((size_t)e * NOUT + col) * (K / 2) + kh * 8;
-            gsrc[i] = gsc + ((size_t)e * NOUT + col) * (K / 16) + kh;
         }
     } else if (!AWQ) {
 #pragma unroll
@@ -509,37 +462,6 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
     uint4 rb0[BPER], rb1[BPER];
     uint32_t rw0[S::RPT], rw1[S::RPT];
     uint32_t pz0 = 0, pz1 = 0, ps0 = 0, ps1 = 0;  // zero word and scale of the parameter column
-    // NVFP4: each B chunk's codes (8 bytes per K step) and scale byte for NVD
-    // consecutive K steps, fetched together NVD steps ahead of use, so that a
-    // column's 128-byte code line (and scale line) is requested in bursts
-    // rather than one small piece per step; lines evicted between steps were
-    // otherwise fetched from HBM again at every step (NVFP4 prefill: routed
-    // call 1.31 -> 1.15 ms).  NVD = 8 would cover a whole code line but takes
-    // the 96-row tile to 268 registers, one wave per SIMD.
-    constexpr int NVC = NV4 ? BPER / 2 : 1;
-    constexpr int NVD = 4;
-    u32x2_t nvc_cur[NVC][NVD], nvc_nxt[NVC][NVD];  // native vectors (HIP's uint2 class would sit in scratch)
-    u32x2_t nvs_cur[NVC], nvs_nxt[NVC];            // scale bytes, step u in byte u
-#pragma unroll
-    for (int i = 0; i < NVC; ++i) {
-        nvs_cur[i] = nvs_nxt[i] = u32x2_t{0u, 0u};
-#pragma unroll
-        for (int u = 0; u < NVD; ++u) nvc_cur[i][u] = nvc_nxt[i][u] = u32x2_t{0u, 0u};
-    }
-    // steps K0 .. K0+NVD-1 (clamped to the last step) into the "next" cache
-#define MOE_NV_FETCH(K0)                                                                      \
-    do {                                                                                      \
-        _Pragma("unroll") for (int i = 0; i < NVC; ++i) {                                     \
-            uint32_t sp_[2] = {0u, 0u};                                                       \
-            _Pragma("unroll") for (int u = 0; u < NVD; ++u) {                                 \
-                const int st_ = min((K0) + u, nk - 1);                                        \
-                nvc_nxt[i][u] = *reinterpret_cast<const u32x2_t*>(fsrc[i] + st_ * (kBK / 2)); \
-                sp_[u / 4] |= (uint32_t)gsrc[i][st_ * (kBK / 16)] << (8 * (u % 4));           \
-            }                                                                                 \
-            nvs_nxt[i] = u32x2_t{sp_[0], sp_[1]};                                             \
-        }                                                                                     \
-    } while (0)
-    if (NV4) MOE_NV_FETCH(0);
 
 #define MOE_LOAD(RA, RB, RW, PZ, PS, KT)                                                      \
     do {                                                                                      \
@@ -553,24 +475,6 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
             _Pragma("unroll") for (int i = 0; i < BPER / 2; ++i) {                            \
                 RB[i] = *reinterpret_cast<const uint4*>(fsrc[i] + k0_);                       \
                 RW[i] = __float_as_uint(fscl[i][k0_ >> 7]);                                   \
-            }                                                                                 \
-        } else if (NV4) {                                                                     \
-            /* codes and scales come from the step cache; a step that is a */                 \
-            /* multiple of NVD moves the next group in and requests the one after */          \
-            const int kq_ = kt_ % NVD;                                                        \
-            if (kq_ == 0) {                                                                   \
-                _Pragma("unroll") for (int i = 0; i < NVC; ++i) {                             \
-                    _Pragma("unroll") for (int u = 0; u < NVD; ++u) nvc_cur[i][u] = nvc_nxt[i][u]; \
-                    nvs_cur[i] = nvs_nxt[i];                                                  \
-                }                                                                             \
-                MOE_NV_FETCH(kt_ + NVD);                                                      \
-            }                                                                                 \
-            _Pragma("unroll") for (int i = 0; i < BPER / 2; ++i) {                            \
-                u32x2_t c_ = nvc_cur[i][0];                                                   \
-                _Pragma("unroll") for (int u = 1; u < NVD; ++u) c_ = kq_ == u ? nvc_cur[i][u] : c_; \
-                RB[i] = make_uint4(c_[0], c_[1], 0u, 0u);                                     \
-                const uint32_t sw_ = kq_ < 4 ? nvs_cur[i][0] : nvs_cur[i][1];                 \
-                RW[i] = (sw_ >> (8 * (kq_ % 4))) & 0xFFu;                                     \
             }                                                                                 \
         } else {                                                                              \
             _Pragma("unroll") for (int i = 0; i < BPER; ++i) RB[i] =                          \
@@ -627,7 +531,6 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
     }
 #undef MOE_LOAD
 #undef MOE_PARAMS
-#undef MOE_NV_FETCH
 
     // ---- epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile.
     // Each wave passes its tile through a private 4.5 KB LDS region (the
@@ -642,17 +545,6 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
     float* st = reinterpret_cast<float*>(wave < 4 ? reinterpret_cast<char*>(&Bs[0][0]) + wave * kStage
                                                   : reinterpret_cast<char*>(&As[0][0]) + (wave - 4) * kStage);
     const int wrow = m0 + wm * S::MW;  // first row of the wave tile
-    // NVFP4 global factors of the accumulators (1 for the other formats)
-    float cg = 1.0f, cu = 1.0f, cd = 1.0f;
-    if (NV4) {
-        if (MODE == MODE_GATEUP) {
-            cg = a.gate.act * a.gate.wglobal[e];
-            cu = a.gate.act * a.up.wglobal[e];
-        } else {
-            cd = a.down.act * a.down.wglobal[e];
-        }
-    }
-    (void)cd;
     if (MODE == MODE_GATEUP) {
         constexpr int HC = S::NW / 2, LD = HC + 4;  // 32 h columns per wave
         const int hcol = n0 + wn * HC;
@@ -663,21 +555,11 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     st[(4 * (lane / 16) + r) * LD + nj * 16 + lane % 16] =
-                        silu(acc[mi][nj][r] * cg) * (acc[mi][nj + TN / 2][r] * cu);
+                        silu(acc[mi][nj][r]) * acc[mi][nj + TN / 2][r];
             wave_lds_sync();
             const int rr = lane / 4, ch = lane % 4;  // 16 rows x 4 chunks of 8 columns
-            float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
-            float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
-            if (NV4) {  // groups of 16 h columns: chunk pairs (0,1), (2,3) of lanes 4i..4i+3
-                float am = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
-                                 fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
-                am = fmaxf(am, __shfl_xor(am, 1, kWave));
-                const float qa = a.down.act, sc = nvfp4_group_scale(am, qa);
-                v0 = make_float4(nvfp4_qv(v0.x, sc, qa), nvfp4_qv(v0.y, sc, qa), nvfp4_qv(v0.z, sc, qa),
-                                 nvfp4_qv(v0.w, sc, qa));
-                v1 = make_float4(nvfp4_qv(v1.x, sc, qa), nvfp4_qv(v1.y, sc, qa), nvfp4_qv(v1.z, sc, qa),
-                                 nvfp4_qv(v1.w, sc, qa));
-            }
+            const float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
+            const float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
             const int row = wrow + mi * 16 + rr;
             if (row < m1)
                 *reinterpret_cast<uint4*>(&hbuf[(size_t)row * F + hcol + ch * 8]) =
@@ -694,7 +576,7 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
             for (int nj = 0; nj < TN; ++nj)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    st[(4 * (lane / 16) + r) * LD + nj * 16 + lane % 16] = NV4 ? acc[mi][nj][r] * cd : acc[mi][nj][r];
+                    st[(4 * (lane / 16) + r) * LD + nj * 16 + lane % 16] = acc[mi][nj][r];
             wave_lds_sync();
             if (a.out_f32) {
                 float* out = static_cast<float*>(a.rows);
@@ -765,12 +647,7 @@ template <int BM>
 static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int mt,
                            hipStream_t s) {
     const int NT1 = a.F / (kBN / 2), NT2 = a.H / kBN;
-    if (a.nvfp4) {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, 3, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
-                           s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 3, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
-                           s, a, tiles, hbuf, NT2);
-    } else if (a.fp8) {
+    if (a.fp8) {
         hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, 2, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT1);
         hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 2, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
@@ -789,6 +666,7 @@ static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t*
 }
 
 hipError_t launch_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
+    if (a.nvfp4) return hipErrorInvalidValue;  // NVFP4 banks run on the register-B GEMM
     const int E = a.offsets ? a.E : 1;
     const int BM = a.offsets ? pick_bm(a.P, E) : pick_bm_dense(a.P, a.F / (kBN / 2));
     const int mt = max_tiles(a.P, E, BM);

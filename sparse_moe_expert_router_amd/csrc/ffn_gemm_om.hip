@@ -59,6 +59,7 @@
 #include <type_traits>
 
 #include "ffn_internal.h"
+#include "nvfp4.h"
 
 namespace moe {
 
@@ -135,6 +136,44 @@ __device__ __forceinline__ rsrc_t om_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// NVFP4 (W4A4) codes in the same place: codes [E][out][in/2], byte j of a
+// column's row holding inputs 2j (bits 0..3) and 2j+1 (bits 4..7) as E2M1, so
+// a 32-bit word is again 8 consecutive inputs; E4M3 group scales
+// [E][out][in/16].  A lane's 32 inputs of a step span two groups (words 0-1
+// and 2-3).  Both factors of a weight e2m1 * s go into fp16 exactly:
+// nv_quad: pq[b] = the pair of inputs 2b, 2b+1 as fp16 e2m1 * 2^8, by the
+// gfx950 scaled conversion (its scale operand acts as a power of two only: a
+// probe over every byte value and byte position matched
+// bf16(e2m1 * 2^floor(log2 s)) everywhere, so 2^8 is exact and the E4M3
+// mantissa cannot go there); nv_scales: the two E4M3 bytes of a step moved
+// into the two halves of an fp16 pair, whose value is then s * 2^-8 exactly
+// (exponent field e, mantissa m: 2^(e-15) (1 + m/8), and for e = 0 the fp16
+// subnormal m 2^-17, as E4M3 has 2^(e-7) (1 + m/8) and m 2^-9); nv_pair(b):
+// one mixed-precision fma a weight reads both halves, + -0 (a register, so
+// that the fma is not folded into a multiply) keeps the sign of a zero
+// product, then one RNE to bf16 (exact: at most 6 significant bits).  The
+// global factors are applied to the accumulators.
+__device__ __forceinline__ void nv_quad(uint32_t w, uint32_t (&pq)[4]) {
+    pq[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0));
+    pq[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1));
+    pq[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2));
+    pq[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3));
+}
+__device__ __forceinline__ uint32_t nv_scales(uint32_t sbits) {
+    return ((sbits & 0x7Fu) << 7) | ((sbits & 0x80u) << 8) | ((sbits & 0x7F00u) << 15) | ((sbits & 0x8000u) << 16);
+}
+__device__ __forceinline__ uint32_t nv_pair(int b, const uint32_t (&pq)[4], uint32_t sc, bool hi, float nz) {
+    const f16x2_t v = __builtin_bit_cast(f16x2_t, pq[b]);
+    const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sc);
+    const float s = (float)(hi ? s2.y : s2.x);
+    return pack_bf16x2(fmaf((float)v.x, s, nz), fmaf((float)v.y, s, nz));
+}
+__device__ __forceinline__ float om_neg_zero() {
+    float z;
+    asm volatile("v_mov_b32 %0, 0x80000000" : "=v"(z));
+    return z;
+}
+
 // (s, -(1024 + z) s) of a lane's column from its raw scale bits and zero word.
 __device__ __forceinline__ void om_params(uint32_t sbits, uint32_t zw, int znib, float& s, float& c) {
     s = f16_to_f32(sbits & 0xFFFFu);
@@ -142,14 +181,17 @@ __device__ __forceinline__ void om_params(uint32_t sbits, uint32_t zw, int znib,
     c = -(1024.0f + z) * s;
 }
 
-// WF: weight format, 1 = AWQ g32 codes output-major, 0 = bf16 [E][out][in]
-// (a lane's 8 inputs are 16 contiguous bytes of its weight row; no dequant).
+// WF: weight format, 1 = AWQ g32 codes output-major, 3 = NVFP4, 0 = bf16
+// [E][out][in] (a lane's 8 inputs are 16 contiguous bytes of its weight row;
+// no dequant).
 template <int MODE, int WF, int TM>
 __global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(OmShape<TM>::MINW, OmShape<TM>::MINW)))
 void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* __restrict__ hbuf, int NT) {
     using S = OmShape<TM>;
     constexpr int BM = S::BM, AP = S::AP;
-    constexpr bool W4 = WF == 1;
+    constexpr bool AQ = WF == 1, NV = WF == 3;
+    constexpr bool W4 = AQ || NV;  // 4-bit codes, dequantised in registers
+    constexpr int LB = AQ ? 6 : 4;  // W4: loads a load_b issues (codes, scales and, AWQ, zero words)
     __shared__ __attribute__((aligned(16))) uint16_t smem[S::SMEM];
 
     const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
@@ -189,14 +231,16 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     const ProjDev& p0 = MODE == OM_GATEUP ? a.gate : a.down;
     const ProjDev& p1 = MODE == OM_GATEUP ? a.up : a.down;
     const uint32_t qbytes = W4 ? (uint32_t)a.E * (uint32_t)N * (uint32_t)(K / 2) : (uint32_t)a.E * (uint32_t)N * (uint32_t)K * 2u;
-    const uint32_t sbytes = (uint32_t)a.E * (uint32_t)(K / 32) * (uint32_t)N * 2u;
-    const uint32_t zbytes = sbytes / 4u;
-    const rsrc_t rq0 = om_rsrc(W4 ? (const void*)p0.qweight : (const void*)p0.w, qbytes);
-    const rsrc_t rq1 = om_rsrc(W4 ? (const void*)p1.qweight : (const void*)p1.w, qbytes);
-    const rsrc_t rs0 = om_rsrc(p0.scales, W4 ? sbytes : 0u), rs1 = om_rsrc(p1.scales, W4 ? sbytes : 0u);
-    const rsrc_t rz0 = om_rsrc(p0.qzeros, W4 ? zbytes : 0u), rz1 = om_rsrc(p1.qzeros, W4 ? zbytes : 0u);
+    const uint32_t sbytes = NV ? (uint32_t)a.E * (uint32_t)N * (uint32_t)(K / 16)
+                               : (uint32_t)a.E * (uint32_t)(K / 32) * (uint32_t)N * 2u;
+    const uint32_t zbytes = AQ ? sbytes / 4u : 0u;
+    auto qsrc = [&](const ProjDev& p) { return NV ? (const void*)p.codes : AQ ? (const void*)p.qweight : (const void*)p.w; };
+    const rsrc_t rq0 = om_rsrc(qsrc(p0), qbytes), rq1 = om_rsrc(qsrc(p1), qbytes);
+    const rsrc_t rs0 = om_rsrc(NV ? (const void*)p0.gscales : (const void*)p0.scales, W4 ? sbytes : 0u);
+    const rsrc_t rs1 = om_rsrc(NV ? (const void*)p1.gscales : (const void*)p1.scales, W4 ? sbytes : 0u);
+    const rsrc_t rz0 = om_rsrc(p0.qzeros, zbytes), rz1 = om_rsrc(p1.qzeros, zbytes);
     uint32_t boff[kOmTN];   // byte offset of the lane's B data in step 0
-    uint32_t soff[kOmTN];   // W4: byte offset of its scale in step 0
+    uint32_t soff[kOmTN];   // W4: byte offset of its scale (NVFP4: its two group scales) in step 0
     uint32_t zoff[kOmTN];   // W4: byte offset of its zero word in step 0
     int znib[kOmTN];
 #pragma unroll
@@ -207,11 +251,11 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
         const uint32_t row = (uint32_t)e * (uint32_t)N + (uint32_t)col;
         boff[f] = W4 ? (row * (uint32_t)(K / 8) + 4u * (uint32_t)g) * 4u      // 4 code words
                      : (row * (uint32_t)K + 32u * (uint32_t)g) * 2u;          // 32 bf16 inputs
-        soff[f] = (grp0 * (uint32_t)N + (uint32_t)col) * 2u;
+        soff[f] = NV ? row * (uint32_t)(K / 16) + 2u * (uint32_t)g : (grp0 * (uint32_t)N + (uint32_t)col) * 2u;
         zoff[f] = (grp0 * (uint32_t)(N / 8) + (uint32_t)(col >> 3)) * 4u;
         znib[f] = awq_nib(col & 7);
     }
-    const uint32_t sstep = 4u * (uint32_t)N, zstep = (uint32_t)N;  // bytes per step (two groups)
+    const uint32_t sstep = NV ? 4u : 4u * (uint32_t)N, zstep = (uint32_t)N;  // bytes per step (AWQ: two groups; NVFP4: four)
     const int bstep = W4 ? 32 : 2 * kOmKS;                          // B bytes per step and lane
 
     f32x16_t acc[TM][kOmTN];
@@ -232,7 +276,7 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
             const bool hi = MODE == OM_GATEUP && f == 1;
             cw[buf][f] = __builtin_amdgcn_raw_buffer_load_b128(hi ? rq1 : rq0, (int)boff[f], j * bstep, 0);
             sb[buf][f] = __builtin_amdgcn_raw_buffer_load_b16(hi ? rs1 : rs0, (int)soff[f], (int)(sstep * (uint32_t)j), 0);
-            zw[buf][f] = __builtin_amdgcn_raw_buffer_load_b32(hi ? rz1 : rz0, (int)zoff[f], (int)(zstep * (uint32_t)j), 0);
+            if (AQ) zw[buf][f] = __builtin_amdgcn_raw_buffer_load_b32(hi ? rz1 : rz0, (int)zoff[f], (int)(zstep * (uint32_t)j), 0);
         }
     };
     auto load_braw = [&](int h, int j) {
@@ -262,7 +306,7 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     for (int h = 0; h < 4; ++h) afr[h] = (lane & 31) * kOmKS + (((4 * g + h) ^ om_swz(lane & 31)) << 3);
 
     u32x4_t bfr[2][kOmTN];        // W4: dequantised B of two k-chunks (bf16 pairs)
-    float ps[kOmTN], pc[kOmTN];   // W4: (s, c) of the step being dequantised
+    float ps[kOmTN], pc[kOmTN];   // W4: (s, c) of the step being dequantised (NVFP4: ps = its two group scales)
     uint32_t pq[kOmTN][4];        // W4: fp16 pairs of the code word being dequantised
     const uint32_t msk = om_mask();
 
@@ -280,8 +324,8 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     // s_waitcnt counter, and each step issues them in one fixed order:
     //   W4:   [mid step m: A(m+3)] [piece 3 TM - 1: B(m+2)]
     //   bf16: [k-chunk h end: its B of step m+1] with A(m+3) at mid step
-    // so at the mid-step wait of step j at most 12 + TM loads issued after
-    // A(j+1) can be outstanding.  The prologue issues steps 0..2's loads in the
+    // so at the mid-step wait of step j at most 2 LB + TM loads issued after
+    // A(j+1) can be outstanding (W4; 12 + TM is a stricter wait for bf16).  The prologue issues steps 0..2's loads in the
     // order the two steps before step 0 would have, so that this holds from
     // step 0 on.
     auto stg = [&](int i) { return smem + i * S::STAGE; };
@@ -291,7 +335,7 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
         load_b(0, 0);
         load_a(stg(2), min(2, NJ - 1));
         load_b(1, min(1, NJ - 1));
-        wait_vm(std::integral_constant<int, 12 + 2 * TM>{});   // A(0)
+        wait_vm(std::integral_constant<int, 2 * LB + 2 * TM>{});   // A(0)
     } else {
         load_braw(0, 0);
         load_braw(1, 0);
@@ -300,13 +344,23 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
         load_braw(3, 0);
         wait_vm(std::integral_constant<int, 8 + 2 * TM>{});    // A(0)
     }
+    // NVFP4: the two group scales of a lane's step as an fp16 pair (in ps)
+    const float nz = NV ? om_neg_zero() : 0.0f;
+    auto nv_params = [](uint32_t sbits, float& s01, float&) { s01 = __uint_as_float(nv_scales(sbits)); };
     if (W4) {
 #pragma unroll
         for (int f = 0; f < kOmTN; ++f) {
-            om_params(sb[0][f], zw[0][f], znib[f], ps[f], pc[f]);
-            om_quad(cw[0][f][0], msk, pq[f]);
+            if (NV) {
+                nv_params(sb[0][f], ps[f], pc[f]);
+                nv_quad(cw[0][f][0], pq[f]);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) bfr[0][f][b] = om_pair(b, pq[f], ps[f], pc[f]);
+                for (int b = 0; b < 4; ++b) bfr[0][f][b] = nv_pair(b, pq[f], __float_as_uint(ps[f]), false, nz);
+            } else {
+                om_params(sb[0][f], zw[0][f], znib[f], ps[f], pc[f]);
+                om_quad(cw[0][f][0], msk, pq[f]);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) bfr[0][f][b] = om_pair(b, pq[f], ps[f], pc[f]);
+            }
         }
     }
     __syncthreads();
@@ -332,8 +386,15 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
 #pragma unroll
                 for (int u = mi * PPC; u < (mi + 1) * PPC && u < 4 * kOmTN; ++u) {
                     const int f = u / 4, b = u % 4;
-                    if (b == 0) om_quad(h < 3 ? cw[cur][f][h + 1] : cw[W4 ? nxt : 0][f][0], msk, pq[f]);
-                    bfr[(h + 1) & 1][f][b] = om_pair(b, pq[f], ps[f], pc[f]);
+                    const uint32_t w = h < 3 ? cw[cur][f][h + 1] : cw[W4 ? nxt : 0][f][0];
+                    if (NV) {
+                        // words 0-1 of a step take its first group scale, 2-3 the second
+                        if (b == 0) nv_quad(w, pq[f]);
+                        bfr[(h + 1) & 1][f][b] = nv_pair(b, pq[f], __float_as_uint(ps[f]), h == 1 || h == 2, nz);
+                    } else {
+                        if (b == 0) om_quad(w, msk, pq[f]);
+                        bfr[(h + 1) & 1][f][b] = om_pair(b, pq[f], ps[f], pc[f]);
+                    }
                 }
             } else if (mi == TM - 1) {
                 load_braw(h, min(j + 1, NJ - 1));  // k-chunk h of step j+1 into the registers just used
@@ -341,7 +402,7 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
             if (p == 2 * TM - 1) {
                 // A(j+1) has landed in its stage: publish it, then request A(j+3)
                 // into the stage step j-1 used (every wave is past step j-1 here)
-                wait_vm(std::integral_constant<int, 12 + TM>{});
+                wait_vm(std::integral_constant<int, (W4 ? 2 * LB : 12) + TM>{});
                 __syncthreads();
                 load_a(stg((j + 3) & 3), min(j + 3, NJ - 1));
             }
@@ -350,7 +411,10 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
                 // j+1's parameters for k-chunk 3's share
                 load_b(cur, min(j + 2, NJ - 1));
 #pragma unroll
-                for (int f = 0; f < kOmTN; ++f) om_params(sb[nxt][f], zw[nxt][f], znib[f], ps[f], pc[f]);
+                for (int f = 0; f < kOmTN; ++f) {
+                    if (NV) nv_params(sb[nxt][f], ps[f], pc[f]);
+                    else om_params(sb[nxt][f], zw[nxt][f], znib[f], ps[f], pc[f]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -375,17 +439,26 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     static_assert(S::SMEM * sizeof(uint16_t) >= 4 * 32 * LD * sizeof(float), "epilogue staging");
     const int nrows = m1 - m0;
     const int col = lane & 31;
+    // NVFP4: the global factors (input scale x weight scale) of the
+    // accumulators of fragment 0 and 1
+    float cf0 = 1.0f, cf1 = 1.0f;
+    if (NV) {
+        cf0 = (MODE == OM_GATEUP ? a.gate.act : a.down.act) * p0.wglobal[e];
+        cf1 = (MODE == OM_GATEUP ? a.gate.act : a.down.act) * p1.wglobal[e];
+    }
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
         if (MODE == OM_GATEUP) {
 #pragma unroll
             for (int k = 0; k < 16; ++k)
-                st[(8 * (k >> 2) + 4 * g + (k & 3)) * LD + col] = silu(acc[mi][0][k]) * acc[mi][1][k];
+                st[(8 * (k >> 2) + 4 * g + (k & 3)) * LD + col] =
+                    NV ? silu(acc[mi][0][k] * cf0) * (acc[mi][1][k] * cf1) : silu(acc[mi][0][k]) * acc[mi][1][k];
         } else {
 #pragma unroll
             for (int f = 0; f < kOmTN; ++f)
 #pragma unroll
-                for (int k = 0; k < 16; ++k) st[(8 * (k >> 2) + 4 * g + (k & 3)) * LD + 32 * f + col] = acc[mi][f][k];
+                for (int k = 0; k < 16; ++k)
+                    st[(8 * (k >> 2) + 4 * g + (k & 3)) * LD + 32 * f + col] = NV ? acc[mi][f][k] * cf0 : acc[mi][f][k];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -396,8 +469,20 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
             for (int pass = 0; pass < 2; ++pass) {  // 16 rows x 4 chunks of 8 h columns
                 const int rr = pass * 16 + (lane >> 2), ch = lane & 3;
                 const int row = 32 * mi + rr;
-                const float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
-                const float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
+                float4 v0 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8]);
+                float4 v1 = *reinterpret_cast<const float4*>(&st[rr * LD + ch * 8 + 4]);
+                if (NV) {
+                    // the down projection's input quantised in groups of 16 h
+                    // columns (chunks 0-1 and 2-3 of the row's lanes 4i .. 4i+3)
+                    float am = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                                     fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+                    am = fmaxf(am, __shfl_xor(am, 1, kWave));
+                    const float qa = a.down.act, sc = nvfp4_group_scale(am, qa);
+                    v0 = make_float4(nvfp4_qv(v0.x, sc, qa), nvfp4_qv(v0.y, sc, qa), nvfp4_qv(v0.z, sc, qa),
+                                     nvfp4_qv(v0.w, sc, qa));
+                    v1 = make_float4(nvfp4_qv(v1.x, sc, qa), nvfp4_qv(v1.y, sc, qa), nvfp4_qv(v1.z, sc, qa),
+                                     nvfp4_qv(v1.w, sc, qa));
+                }
                 if (row < nrows)
                     st_stream(&hbuf[(size_t)(m0 + row) * F + hcol + ch * 8],
                               u32x4_t{pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
@@ -542,7 +627,10 @@ hipError_t launch_om_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
     hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TMG, tiles);
     if (TMD != TMG) hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TMD, tiles_d);
     else tiles_d = tiles;
-    if (a.awq) {
+    if (a.nvfp4) {
+        launch_om_wf<OM_GATEUP, 3>(a, tiles, hbuf, E, TMG, s);
+        launch_om_wf<OM_DOWN, 3>(a, tiles_d, hbuf, E, TMD, s);
+    } else if (a.awq) {
         launch_om_wf<OM_GATEUP, 1>(a, tiles, hbuf, E, TMG, s);
         launch_om_wf<OM_DOWN, 1>(a, tiles_d, hbuf, E, TMD, s);
     } else {

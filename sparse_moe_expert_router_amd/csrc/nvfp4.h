@@ -58,9 +58,27 @@ __device__ __forceinline__ float nvfp4_group_scale(float amax, float ga) {
     return e4m3_val(e4m3_rne(__fdiv_rn(amax, 6.0f * ga)));
 }
 
-// v quantised with block scale s (s > 0) under ga: e2m1(code) * s, exact.
+// The value of e2m1_rne(a) for a >= 0, computed directly: on [0, 1) the grid
+// is the multiples of 0.5 (rint ties to even, so 0.25 -> 0 and 0.75 -> 1);
+// from 1 up it is the floats with one mantissa bit, reached by rounding the
+// fp32 to one mantissa bit (ties to even) in its bit pattern, then
+// saturated at 6 (+inf too).  Equal to e2m1_val(e2m1_rne(a)) for every
+// non-negative float: checked exhaustively on the host, 2^31 - 2^23 + 1
+// values.
+__device__ __forceinline__ float e2m1_round(float a) {
+    if (a < 1.0f) return __builtin_rintf(2.0f * a) * 0.5f;
+    uint32_t b = __float_as_uint(a);
+    b += 0x1FFFFFu + ((b >> 22) & 1u);
+    return fminf(__uint_as_float(b & 0xFFC00000u), 6.0f);
+}
+
+// v quantised with block scale s (s > 0) under ga: e2m1(code) * s, exact
+// (a zero code is +0, as e2m1_val gives it).
 __device__ __forceinline__ float nvfp4_qv(float v, float s, float ga) {
-    return s == 0.0f ? 0.0f : e2m1_val(e2m1_rne(__fdiv_rn(v, s * ga))) * s;
+    if (s == 0.0f) return 0.0f;
+    const float q = __fdiv_rn(v, s * ga);
+    const float r = e2m1_round(fabsf(q));
+    return r == 0.0f ? 0.0f : __builtin_copysignf(r, q) * s;
 }
 
 }  // namespace moe
