@@ -1,9 +1,13 @@
 // Grouped SwiGLU experts for many rows per expert on AWQ W4A16 g32 codes
-// stored output-major: bf16 MFMA with the weights dequantised in registers.
+// stored output-major (and on NVFP4 codes and bf16 weights, which are
+// output-major as stored): bf16 MFMA with the weights dequantised in registers.
 //
 // Qwen3.8-Flash-Next architecture sheet, FFN / MoE entries: SwiGLU experts
 // (gate, up, down), no bias, no clamp.  AWQ-g32 card, "Checkpoint": asymmetric
 // W4A16, group 32 along the input, integer zeros, fp16 scales, w = (q - z) s.
+// NVFP4 release card, precision table: W4A4 experts, E2M1 values in groups of
+// 16 with E4M3 group scales and fp32 global scales (the layout and the
+// activation recipe are this library's reading, as in nvfp4.h).
 //
 // Code layout: qweight [E][out][in/8] int32, nibble j of word w holds input
 // 8w + j of that output column (the AWQ codes rearranged once by
