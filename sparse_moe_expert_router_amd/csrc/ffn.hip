@@ -116,8 +116,9 @@ hipError_t launch_ffn(const FfnArgs& f, void* ws, hipStream_t s) {
     // the shared expert of a decode step: one bf16 expert, a handful of tokens
     if (!a.offsets && f.ex->gate.fmt == MOE_W_BF16 && skinny_supported(a.T, a.H, a.F)) return launch_skinny(a, ws, s);
     if (use_gemm(a.P, a.offsets ? a.E : 1, a.H, a.F)) {
-        // bf16 weights and NVFP4 codes go straight into registers on the register-B GEMM
-        if ((f.ex->gate.fmt == MOE_W_BF16 || f.ex->gate.fmt == MOE_W_NVFP4) && om_gemm_supported(a.H, a.F))
+        // bf16 weights, FP8 and NVFP4 codes go straight into registers on the register-B GEMM
+        const int fm = f.ex->gate.fmt;
+        if ((fm == MOE_W_BF16 || fm == MOE_W_FP8_BLOCK || fm == MOE_W_NVFP4) && om_gemm_supported(a.H, a.F))
             return launch_om_gemm(a, ws, s);
         return launch_gemm(a, ws, s);
     }

@@ -25,9 +25,8 @@
 // bits), fma(m, s, c) = (q - z) * s exactly, then one RNE to bf16.  The four
 // rows of a column are contiguous in the K-major LDS tile: one 8-byte store.
 //
-// FP8 B tiles are widened to bf16 on the way into LDS (an E4M3 code times its
-// fp32 block scale, rounded once).  NVFP4 banks run on the register-B GEMM
-// (ffn_gemm_om.hip), whose B words hold the same 8 consecutive inputs.
+// FP8 and NVFP4 banks run on the register-B GEMM (ffn_gemm_om.hip), whose B
+// words hold 8 consecutive inputs of a column, as those formats store them.
 //
 // Tiles are enumerated per expert (ceil(rows / BM) each) by a small kernel;
 // workgroup ids are remapped so that each XCD (ids are dealt round-robin over
@@ -179,44 +178,20 @@ __device__ __forceinline__ void awq_split(const uint32_t (&rw)[RPT], uint32_t (&
     }
 }
 
-// FP8 B tile: a thread's chunk q (< BPER/2) is B-column q/2, inputs
-// 16*(q%2)..+15 of the step: 16 E4M3 codes, widened two at a time
-// (v_cvt_pk_f32_fp8), times the block scale, rounded to bf16 and stored as the
-// column's two 8-input LDS chunks.
-__device__ __forceinline__ void fp8_store_chunk(uint4 c, float sc, uint16_t* Bs, int q) {
-    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], true);
-        o[2 * i] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
-        o[2 * i + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
-    }
-    const int bc = q / 2, kh = q % 2;
-    *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh)]) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(&Bs[lds_off(bc, 2 * kh + 1)]) = make_uint4(o[4], o[5], o[6], o[7]);
-}
-
 // Registers of one K step -> LDS stage (A chunks; bf16 B chunks or dequantised AWQ words).
 template <int MODE, int WF, int BM>
 __device__ __forceinline__ void store_stage(const uint4 (&ra)[GemmShape<BM>::APER],
                                             const uint4 (&rb)[GemmShape<BM>::BPER],
                                             const uint32_t (&rw)[GemmShape<BM>::RPT], const float2* Ps,
                                             uint16_t* As, uint16_t* Bs, int tid) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32, FP8
-    (void)FP8;
+    constexpr bool AWQ = WF == 1;  // B format: bf16, AWQ g32
     using S = GemmShape<BM>;
 #pragma unroll
     for (int i = 0; i < S::APER; ++i) {
         const int q = tid + i * S::NT;
         if (S::AQ % S::NT == 0 || q < S::AQ) *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[i];
     }
-    if (FP8) {
-#pragma unroll
-        for (int i = 0; i < S::BPER / 2; ++i)
-            fp8_store_chunk(rb[i], __uint_as_float(rw[i]), Bs, tid + i * S::NT);
-    } else if (!AWQ) {
+    if (!AWQ) {
 #pragma unroll
         for (int i = 0; i < S::BPER; ++i) {
             const int q = tid + i * S::NT;
@@ -255,7 +230,7 @@ __device__ __forceinline__ bf16x8_t a_frag(const uint16_t* As, int mi, int wm, i
 
 // A K step is cut into 8 slices of PER = TM*TN/8 MFMAs.  Slices 0..kPipeSplit-1
 // (step_pre) also store the next step's LDS stage (A chunks, and bf16 B chunks
-// or the dequantised AWQ/FP8 columns), then the block barrier makes that
+// or the dequantised AWQ columns), then the block barrier makes that
 // stage visible, and the remaining slices (step_post) read the next step's
 // fragments while this step's last MFMAs run.  With three LDS stages nothing
 // is written to a stage that another wave may still be reading: stage kt+1 is
@@ -281,7 +256,7 @@ __device__ __forceinline__ void step_pre(bf16x8_t (&af)[GemmShape<BM>::TM], cons
                                          const uint4 (&rb)[GemmShape<BM>::BPER],
                                          const uint32_t (&rw)[GemmShape<BM>::RPT], const float2* Ps, uint16_t* As,
                                          uint16_t* Bs, int tid, const uint16_t* Acur, int wm, int lane) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32, FP8
+    constexpr bool AWQ = WF == 1;  // B format: bf16, AWQ g32
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN;
     constexpr int PER = TM * TN / 8, SB = kPipeSplit;
@@ -301,9 +276,7 @@ __device__ __forceinline__ void step_pre(bf16x8_t (&af)[GemmShape<BM>::TM], cons
             const int q = tid + j * S::NT;
             if (S::AQ % S::NT == 0 || q < S::AQ) *reinterpret_cast<uint4*>(&As[lds_off(q / 4, q % 4)]) = ra[j];
         }
-        if (FP8) {
-            if (j < S::BPER / 2) fp8_store_chunk(rb[j], __uint_as_float(rw[j]), Bs, tid + j * S::NT);
-        } else if (!AWQ) {
+        if (!AWQ) {
             if (j < S::BPER) {
                 const int q = tid + j * S::NT;
                 *reinterpret_cast<uint4*>(&Bs[lds_off(q / 4, q % 4)]) = rb[j];
@@ -351,8 +324,7 @@ template <int MODE, int WF, int BM>
 __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_eu(GemmShape<BM>::MINW))) void grouped_gemm_kernel(GroupedArgs a,
                                                                const int32_t* __restrict__ tiles,
                                                                uint16_t* __restrict__ hbuf, int NT) {
-    constexpr bool AWQ = WF == 1, FP8 = WF == 2;  // B format: bf16, AWQ g32, FP8
-    (void)FP8;
+    constexpr bool AWQ = WF == 1;  // B format: bf16, AWQ g32
     using S = GemmShape<BM>;
     constexpr int TM = S::TM, TN = S::TN, APER = S::APER, BPER = S::BPER, NTHR = S::NT;
     __shared__ __attribute__((aligned(16))) uint16_t As[3][BM * kBK];
@@ -393,27 +365,12 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
     // threads < 256 also fetch one column's zero word and scale for the
     // per-step parameter table.
     const uint16_t* bsrc[BPER];
-    const uint8_t* fsrc[BPER / 2 > 0 ? BPER / 2 : 1];   // FP8 code chunks
-    const float* fscl[BPER / 2 > 0 ? BPER / 2 : 1];     // their block-scale rows
     const int32_t* wsrc = nullptr;
     const int32_t* zsrc = nullptr;
     const uint16_t* ssrc = nullptr;
     int pnib = 0;  // nibble of the parameter column in its zero word
     const int OW = NOUT / 8;
-    if (FP8) {
-#pragma unroll
-        for (int i = 0; i < BPER / 2; ++i) {
-            const int q = tid + i * NTHR;
-            const int bc = q / 2, kh = q % 2;
-            const bool upm = MODE == MODE_GATEUP && bc >= kBN / 2;
-            // select by value (a reference into the kernel-argument struct would force a stack copy)
-            const uint8_t* codes = MODE == MODE_DOWN ? a.down.codes : (upm ? a.up.codes : a.gate.codes);
-            const float* bsc = MODE == MODE_DOWN ? a.down.bscales : (upm ? a.up.bscales : a.gate.bscales);
-            const int col = MODE == MODE_GATEUP ? n0 + bc % (kBN / 2) : n0 + bc;
-            fsrc[i] = codes + (size_t)e * NOUT * K + (size_t)col * K + kh * 16;
-            fscl[i] = bsc + ((size_t)e * (NOUT / 128) + col / 128) * (K / 128);
-        }
-    } else if (!AWQ) {
+    if (!AWQ) {
 #pragma unroll
         for (int i = 0; i < BPER; ++i) {
             const int q = tid + i * NTHR;
@@ -471,11 +428,6 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
             PS = (uint32_t)ssrc[(size_t)kt_ * NOUT];                                          \
             _Pragma("unroll") for (int i = 0; i < S::RPT; ++i) RW[i] =                        \
                 (uint32_t)wsrc[(size_t)(k0_ + i) * OW];                                       \
-        } else if (FP8) {                                                                     \
-            _Pragma("unroll") for (int i = 0; i < BPER / 2; ++i) {                            \
-                RB[i] = *reinterpret_cast<const uint4*>(fsrc[i] + k0_);                       \
-                RW[i] = __float_as_uint(fscl[i][k0_ >> 7]);                                   \
-            }                                                                                 \
         } else {                                                                              \
             _Pragma("unroll") for (int i = 0; i < BPER; ++i) RB[i] =                          \
                 *reinterpret_cast<const uint4*>(bsrc[i] + k0_);                               \
@@ -647,12 +599,7 @@ template <int BM>
 static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t* hbuf, int mt,
                            hipStream_t s) {
     const int NT1 = a.F / (kBN / 2), NT2 = a.H / kBN;
-    if (a.fp8) {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, 2, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
-                           s, a, tiles, hbuf, NT1);
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 2, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
-                           s, a, tiles, hbuf, NT2);
-    } else if (a.awq) {
+    if (a.awq) {
         hipLaunchKernelGGL((grouped_gemm_kernel<MODE_GATEUP, 1, BM>), gemm_grid(mt, NT1), dim3(GemmShape<BM>::NT), 0,
                            s, a, tiles, hbuf, NT1);
         hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 1, BM>), gemm_grid(mt, NT2), dim3(GemmShape<BM>::NT), 0,
@@ -666,7 +613,7 @@ static void launch_gemm_bm(const GroupedArgs& a, const int32_t* tiles, uint16_t*
 }
 
 hipError_t launch_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
-    if (a.nvfp4) return hipErrorInvalidValue;  // NVFP4 banks run on the register-B GEMM
+    if (a.nvfp4 || a.fp8) return hipErrorInvalidValue;  // FP8 and NVFP4 banks run on the register-B GEMM
     const int E = a.offsets ? a.E : 1;
     const int BM = a.offsets ? pick_bm(a.P, E) : pick_bm_dense(a.P, a.F / (kBN / 2));
     const int mt = max_tiles(a.P, E, BM);

@@ -178,6 +178,17 @@ __device__ __forceinline__ float om_neg_zero() {
     return z;
 }
 
+// FP8 E4M3 codes [E][out][in] with fp32 block scales [E][out/128][in/128]: a
+// k-chunk's 8 inputs are 8 bytes of the column's row (two words), and a
+// step's 64 inputs lie in one scale block.  f8_pair(b): inputs 2b, 2b+1
+// widened by v_cvt_pk_f32_fp8, times the block scale in fp32, rounded once to
+// bf16 (the arithmetic the first GEMM applies to FP8 tiles).
+__device__ __forceinline__ uint32_t f8_pair(int b, uint32_t w0, uint32_t w1, float s) {
+    const int w = (int)(b < 2 ? w0 : w1);
+    const auto v = (b & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    return pack_bf16x2(v[0] * s, v[1] * s);
+}
+
 // (s, -(1024 + z) s) of a lane's column from its raw scale bits and zero word.
 __device__ __forceinline__ void om_params(uint32_t sbits, uint32_t zw, int znib, float& s, float& c) {
     s = f16_to_f32(sbits & 0xFFFFu);
@@ -185,17 +196,17 @@ __device__ __forceinline__ void om_params(uint32_t sbits, uint32_t zw, int znib,
     c = -(1024.0f + z) * s;
 }
 
-// WF: weight format, 1 = AWQ g32 codes output-major, 3 = NVFP4, 0 = bf16
-// [E][out][in] (a lane's 8 inputs are 16 contiguous bytes of its weight row;
-// no dequant).
+// WF: weight format, 1 = AWQ g32 codes output-major, 2 = FP8, 3 = NVFP4, 0 =
+// bf16 [E][out][in] (a lane's 8 inputs are 16 contiguous bytes of its weight
+// row; no dequant).
 template <int MODE, int WF, int TM>
 __global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(OmShape<TM>::MINW, OmShape<TM>::MINW)))
 void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* __restrict__ hbuf, int NT) {
     using S = OmShape<TM>;
     constexpr int BM = S::BM, AP = S::AP;
-    constexpr bool AQ = WF == 1, NV = WF == 3;
-    constexpr bool W4 = AQ || NV;  // 4-bit codes, dequantised in registers
-    constexpr int LB = AQ ? 6 : 4;  // W4: loads a load_b issues (codes, scales and, AWQ, zero words)
+    constexpr bool AQ = WF == 1, F8 = WF == 2, NV = WF == 3;
+    constexpr bool W4 = AQ || F8 || NV;  // codes dequantised in registers
+    constexpr int LB = NV ? 4 : 6;  // W4: loads a load_b issues (codes, scales and, AWQ, zero words)
     __shared__ __attribute__((aligned(16))) uint16_t smem[S::SMEM];
 
     const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
@@ -234,17 +245,23 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     const int g = lane >> 5;
     const ProjDev& p0 = MODE == OM_GATEUP ? a.gate : a.down;
     const ProjDev& p1 = MODE == OM_GATEUP ? a.up : a.down;
-    const uint32_t qbytes = W4 ? (uint32_t)a.E * (uint32_t)N * (uint32_t)(K / 2) : (uint32_t)a.E * (uint32_t)N * (uint32_t)K * 2u;
+    const uint32_t qbytes = (AQ || NV) ? (uint32_t)a.E * (uint32_t)N * (uint32_t)(K / 2)
+                                       : (uint32_t)a.E * (uint32_t)N * (uint32_t)K * (F8 ? 1u : 2u);
     const uint32_t sbytes = NV ? (uint32_t)a.E * (uint32_t)N * (uint32_t)(K / 16)
+                          : F8 ? (uint32_t)a.E * (uint32_t)(N / 128) * (uint32_t)(K / 128) * 4u
                                : (uint32_t)a.E * (uint32_t)(K / 32) * (uint32_t)N * 2u;
     const uint32_t zbytes = AQ ? sbytes / 4u : 0u;
-    auto qsrc = [&](const ProjDev& p) { return NV ? (const void*)p.codes : AQ ? (const void*)p.qweight : (const void*)p.w; };
+    auto qsrc = [&](const ProjDev& p) {
+        return (NV || F8) ? (const void*)p.codes : AQ ? (const void*)p.qweight : (const void*)p.w;
+    };
+    auto ssrc = [&](const ProjDev& p) {
+        return NV ? (const void*)p.gscales : F8 ? (const void*)p.bscales : (const void*)p.scales;
+    };
     const rsrc_t rq0 = om_rsrc(qsrc(p0), qbytes), rq1 = om_rsrc(qsrc(p1), qbytes);
-    const rsrc_t rs0 = om_rsrc(NV ? (const void*)p0.gscales : (const void*)p0.scales, W4 ? sbytes : 0u);
-    const rsrc_t rs1 = om_rsrc(NV ? (const void*)p1.gscales : (const void*)p1.scales, W4 ? sbytes : 0u);
+    const rsrc_t rs0 = om_rsrc(ssrc(p0), W4 ? sbytes : 0u), rs1 = om_rsrc(ssrc(p1), W4 ? sbytes : 0u);
     const rsrc_t rz0 = om_rsrc(p0.qzeros, zbytes), rz1 = om_rsrc(p1.qzeros, zbytes);
     uint32_t boff[kOmTN];   // byte offset of the lane's B data in step 0
-    uint32_t soff[kOmTN];   // W4: byte offset of its scale (NVFP4: its two group scales) in step 0
+    uint32_t soff[kOmTN];   // W4: byte offset of its scale (NVFP4: its two group scales; FP8: block scale) in step 0
     uint32_t zoff[kOmTN];   // W4: byte offset of its zero word in step 0
     int znib[kOmTN];
 #pragma unroll
@@ -253,14 +270,17 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
                                           : nt * kOmBN + 64 * wn + 32 * f + (lane & 31);
         const uint32_t grp0 = (uint32_t)e * (uint32_t)(K / 32) + (uint32_t)g;
         const uint32_t row = (uint32_t)e * (uint32_t)N + (uint32_t)col;
-        boff[f] = W4 ? (row * (uint32_t)(K / 8) + 4u * (uint32_t)g) * 4u      // 4 code words
-                     : (row * (uint32_t)K + 32u * (uint32_t)g) * 2u;          // 32 bf16 inputs
-        soff[f] = NV ? row * (uint32_t)(K / 16) + 2u * (uint32_t)g : (grp0 * (uint32_t)N + (uint32_t)col) * 2u;
+        boff[f] = (AQ || NV) ? (row * (uint32_t)(K / 8) + 4u * (uint32_t)g) * 4u   // 4 code words
+                : F8 ? row * (uint32_t)K + 32u * (uint32_t)g                       // 32 E4M3 codes
+                     : (row * (uint32_t)K + 32u * (uint32_t)g) * 2u;               // 32 bf16 inputs
+        soff[f] = NV ? row * (uint32_t)(K / 16) + 2u * (uint32_t)g
+                : F8 ? ((uint32_t)e * (uint32_t)(N / 128) + (uint32_t)(col / 128)) * (uint32_t)(K / 128) * 4u
+                     : (grp0 * (uint32_t)N + (uint32_t)col) * 2u;
         zoff[f] = (grp0 * (uint32_t)(N / 8) + (uint32_t)(col >> 3)) * 4u;
         znib[f] = awq_nib(col & 7);
     }
     const uint32_t sstep = NV ? 4u : 4u * (uint32_t)N, zstep = (uint32_t)N;  // bytes per step (AWQ: two groups; NVFP4: four)
-    const int bstep = W4 ? 32 : 2 * kOmKS;                          // B bytes per step and lane
+    const int bstep = (AQ || NV) ? 32 : F8 ? kOmKS : 2 * kOmKS;   // B bytes per step and lane
 
     f32x16_t acc[TM][kOmTN];
 #pragma unroll
@@ -271,15 +291,21 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     // W4: raw B of two steps (buffer = step parity): four code words, scale
     // bits, zero word.  bf16: the current step's 4 k-chunks of B, each
     // refilled with the next step's once its MFMAs have issued.
-    u32x4_t cw[W4 ? 2 : 1][kOmTN];
+    u32x4_t cw[W4 ? 2 : 1][kOmTN][F8 ? 2 : 1];  // FP8: 32 codes in two vectors
     uint32_t sb[2][kOmTN], zw[2][kOmTN];
     u32x4_t braw[W4 ? 1 : 4][kOmTN];
     auto load_b = [&](int buf, int j) {
 #pragma unroll
         for (int f = 0; f < kOmTN; ++f) {
             const bool hi = MODE == OM_GATEUP && f == 1;
-            cw[buf][f] = __builtin_amdgcn_raw_buffer_load_b128(hi ? rq1 : rq0, (int)boff[f], j * bstep, 0);
-            sb[buf][f] = __builtin_amdgcn_raw_buffer_load_b16(hi ? rs1 : rs0, (int)soff[f], (int)(sstep * (uint32_t)j), 0);
+            cw[buf][f][0] = __builtin_amdgcn_raw_buffer_load_b128(hi ? rq1 : rq0, (int)boff[f], j * bstep, 0);
+            if (F8) {
+                cw[buf][f][F8 ? 1 : 0] = __builtin_amdgcn_raw_buffer_load_b128(hi ? rq1 : rq0, (int)boff[f] + 16, j * bstep, 0);
+                // the step's 64 inputs lie in block j / 2 of 128
+                sb[buf][f] = __builtin_amdgcn_raw_buffer_load_b32(hi ? rs1 : rs0, (int)soff[f], (j >> 1) * 4, 0);
+            } else {
+                sb[buf][f] = __builtin_amdgcn_raw_buffer_load_b16(hi ? rs1 : rs0, (int)soff[f], (int)(sstep * (uint32_t)j), 0);
+            }
             if (AQ) zw[buf][f] = __builtin_amdgcn_raw_buffer_load_b32(hi ? rz1 : rz0, (int)zoff[f], (int)(zstep * (uint32_t)j), 0);
         }
     };
@@ -354,14 +380,18 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     if (W4) {
 #pragma unroll
         for (int f = 0; f < kOmTN; ++f) {
-            if (NV) {
+            if (F8) {
+                ps[f] = __uint_as_float(sb[0][f]);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) bfr[0][f][b] = f8_pair(b, cw[0][f][0][0], cw[0][f][0][1], ps[f]);
+            } else if (NV) {
                 nv_params(sb[0][f], ps[f], pc[f]);
-                nv_quad(cw[0][f][0], pq[f]);
+                nv_quad(cw[0][f][0][0], pq[f]);
 #pragma unroll
                 for (int b = 0; b < 4; ++b) bfr[0][f][b] = nv_pair(b, pq[f], __float_as_uint(ps[f]), false, nz);
             } else {
                 om_params(sb[0][f], zw[0][f], znib[f], ps[f], pc[f]);
-                om_quad(cw[0][f][0], msk, pq[f]);
+                om_quad(cw[0][f][0][0], msk, pq[f]);
 #pragma unroll
                 for (int b = 0; b < 4; ++b) bfr[0][f][b] = om_pair(b, pq[f], ps[f], pc[f]);
             }
@@ -390,8 +420,13 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
 #pragma unroll
                 for (int u = mi * PPC; u < (mi + 1) * PPC && u < 4 * kOmTN; ++u) {
                     const int f = u / 4, b = u % 4;
-                    const uint32_t w = h < 3 ? cw[cur][f][h + 1] : cw[W4 ? nxt : 0][f][0];
-                    if (NV) {
+                    const uint32_t w = h < 3 ? cw[cur][f][0][(h + 1) & 3] : cw[W4 ? nxt : 0][f][0][0];
+                    if (F8) {
+                        // k-chunk (h + 1) mod 4: words 2 kc, 2 kc + 1 of the step's eight
+                        const int kc = (h + 1) & 3;
+                        const u32x4_t& v = cw[h < 3 ? cur : (W4 ? nxt : 0)][f][(kc >> 1) & (F8 ? 1 : 0)];
+                        bfr[(h + 1) & 1][f][b] = f8_pair(b, v[2 * (kc & 1)], v[2 * (kc & 1) + 1], ps[f]);
+                    } else if (NV) {
                         // words 0-1 of a step take its first group scale, 2-3 the second
                         if (b == 0) nv_quad(w, pq[f]);
                         bfr[(h + 1) & 1][f][b] = nv_pair(b, pq[f], __float_as_uint(ps[f]), h == 1 || h == 2, nz);
@@ -416,7 +451,8 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
                 load_b(cur, min(j + 2, NJ - 1));
 #pragma unroll
                 for (int f = 0; f < kOmTN; ++f) {
-                    if (NV) nv_params(sb[nxt][f], ps[f], pc[f]);
+                    if (F8) ps[f] = __uint_as_float(sb[nxt][f]);
+                    else if (NV) nv_params(sb[nxt][f], ps[f], pc[f]);
                     else om_params(sb[nxt][f], zw[nxt][f], znib[f], ps[f], pc[f]);
                 }
             }
@@ -634,6 +670,9 @@ hipError_t launch_om_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
     if (a.nvfp4) {
         launch_om_wf<OM_GATEUP, 3>(a, tiles, hbuf, E, TMG, s);
         launch_om_wf<OM_DOWN, 3>(a, tiles_d, hbuf, E, TMD, s);
+    } else if (a.fp8) {
+        launch_om_wf<OM_GATEUP, 2>(a, tiles, hbuf, E, TMG, s);
+        launch_om_wf<OM_DOWN, 2>(a, tiles_d, hbuf, E, TMD, s);
     } else if (a.awq) {
         launch_om_wf<OM_GATEUP, 1>(a, tiles, hbuf, E, TMG, s);
         launch_om_wf<OM_DOWN, 1>(a, tiles_d, hbuf, E, TMD, s);
