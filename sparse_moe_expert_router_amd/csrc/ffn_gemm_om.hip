@@ -1,5 +1,5 @@
 // Grouped SwiGLU experts for many rows per expert on AWQ W4A16 g32 codes
-// stored output-major (and on NVFP4 codes and bf16 weights, which are
+// stored output-major (and on FP8 and NVFP4 codes and bf16 weights, which are
 // output-major as stored): bf16 MFMA with the weights dequantised in registers.
 //
 // Qwen3.8-Flash-Next architecture sheet, FFN / MoE entries: SwiGLU experts
@@ -7,7 +7,9 @@
 // W4A16, group 32 along the input, integer zeros, fp16 scales, w = (q - z) s.
 // NVFP4 release card, precision table: W4A4 experts, E2M1 values in groups of
 // 16 with E4M3 group scales and fp32 global scales (the layout and the
-// activation recipe are this library's reading, as in nvfp4.h).
+// activation recipe are this library's reading, as in nvfp4.h).  The AWQ-g32
+// card's optional FP8 draft: routed experts in E4M3 with explicit block
+// scales (128 x 128 blocks: this library's reading).
 //
 // Code layout: qweight [E][out][in/8] int32, nibble j of word w holds input
 // 8w + j of that output column (the AWQ codes rearranged once by
