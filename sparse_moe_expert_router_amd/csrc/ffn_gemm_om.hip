@@ -201,22 +201,16 @@ __device__ __forceinline__ void om_params(uint32_t sbits, uint32_t zw, int znib,
 // WF: weight format, 1 = AWQ g32 codes output-major, 2 = FP8, 3 = NVFP4, 0 =
 // bf16 [E][out][in] (a lane's 8 inputs are 16 contiguous bytes of its weight
 // row; no dequant).
+// One row tile (rows m0 .. m1 - 1 of expert e, at most 32 TM) x B-column tile
+// nt, computed as TM blocks of 32 rows.
 template <int MODE, int WF, int TM>
-__global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(OmShape<TM>::MINW, OmShape<TM>::MINW)))
-void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* __restrict__ hbuf, int NT) {
+__device__ __forceinline__ void om_gemm_tile(const GroupedArgs& a, uint16_t* __restrict__ smem,
+                                             uint16_t* __restrict__ hbuf, int e, int m0, int m1, int nt) {
     using S = OmShape<TM>;
-    constexpr int BM = S::BM, AP = S::AP;
+    constexpr int AP = S::AP;
     constexpr bool AQ = WF == 1, F8 = WF == 2, NV = WF == 3;
     constexpr bool W4 = AQ || F8 || NV;  // codes dequantised in registers
     constexpr int LB = NV ? 4 : 6;  // W4: loads a load_b issues (codes, scales and, AWQ, zero words)
-    __shared__ __attribute__((aligned(16))) uint16_t smem[S::SMEM];
-
-    const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
-    if (l < 0) return;
-    const int tile = l / NT, nt = l % NT;
-    const int e = tiles[1 + 3 * tile];
-    const int m0 = tiles[2 + 3 * tile];
-    const int m1 = tiles[3 + 3 * tile];
 
     const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
     const int H = a.H, F = a.F;
@@ -558,6 +552,39 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// The grouped GEMM over a tile table.  In the gate/up pass with tiles of 192
+// or 256 rows, a tile of fewer rows runs a copy of the loop with one or two
+// row blocks fewer (chosen per tile, outside the K loop, so that every copy
+// keeps a static schedule): an expert whose rows just exceed a multiple of
+// 32 TM is split into tiles one block short, and its last tile is often
+// shorter still.  Shorter tiles compute TM - 2 blocks.
+template <int MODE, int WF, int TM>
+__global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(OmShape<TM>::MINW, OmShape<TM>::MINW)))
+void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* __restrict__ hbuf, int NT) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[OmShape<TM>::SMEM];
+    const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
+    if (l < 0) return;
+    const int tile = l / NT, nt = l % NT;
+    const int e = tiles[1 + 3 * tile];
+    const int m0 = tiles[2 + 3 * tile];
+    const int m1 = tiles[3 + 3 * tile];
+    const int tv = (m1 - m0 + 31) >> 5;  // row blocks the tile needs, 1 .. TM
+    // gate/up tiles of 192 or 256 rows only: the down projection's short
+    // tiles (two workgroups a compute unit) measured slower with the copies
+    constexpr bool VAR = MODE == OM_GATEUP && TM >= 6;
+    constexpr int T1 = VAR ? TM - 1 : TM, T2 = VAR ? TM - 2 : TM;
+    if constexpr (T1 == TM) {
+        om_gemm_tile<MODE, WF, TM>(a, smem, hbuf, e, m0, m1, nt);
+    } else if constexpr (T2 == T1) {
+        if (tv > T1) om_gemm_tile<MODE, WF, TM>(a, smem, hbuf, e, m0, m1, nt);
+        else om_gemm_tile<MODE, WF, T1>(a, smem, hbuf, e, m0, m1, nt);
+    } else {
+        if (tv > T1) om_gemm_tile<MODE, WF, TM>(a, smem, hbuf, e, m0, m1, nt);
+        else if (tv > T2) om_gemm_tile<MODE, WF, T1>(a, smem, hbuf, e, m0, m1, nt);
+        else om_gemm_tile<MODE, WF, T2>(a, smem, hbuf, e, m0, m1, nt);
     }
 }
 
