@@ -1,8 +1,9 @@
 """AWQ W4A16 g32 experts with output-major codes (MOE_W_AWQ_G32_OM): the code
 conversion against an independent numpy repacker, bit for bit, and the MFMA
 grouped GEMM that reads the layout against the oracle on every row-tile size
-(64, 96, 128, 192 and 256 rows), ragged last tiles, decode batches and the
-full layer width."""
+(64, 96, 128, 192 and 256 rows), tiles of 192- and 256-row kernels that run
+one or two row blocks short, ragged last tiles, decode batches and the full
+layer width."""
 import numpy as np
 import pytest
 import torch
@@ -42,6 +43,8 @@ def _routing(T, k, E, seed):
                                        (400, 8, 2, 256, 128),     # 100 rows: 128-row tiles
                                        (560, 8, 2, 256, 128),     # 140 rows: 192-row tiles
                                        (1100, 8, 2, 256, 128),    # 275 rows: 256-row tiles + ragged tails
+                                       (1700, 8, 2, 256, 128),    # 425 rows: tiles of 7 or 8 row blocks
+                                       (220, 2, 2, 2560, 640),    # 220 rows, full width: one 7-block tile
                                        (100, 4, 2, 2560, 640),    # full width
                                        (16, 512, 10, 2560, 640),  # decode batch: 1-2 rows per expert
                                        (900, 3, 1, 512, 384)])    # one expert idle or nearly

@@ -177,6 +177,7 @@ def _random_routing(T, k, E, seed):
                                        (400, 8, 2, 256, 128),     # 100 rows: 128-row tiles
                                        (600, 8, 2, 256, 128),     # 150 rows: 192-row tiles
                                        (1100, 8, 2, 256, 128),    # 275 rows: 256-row tiles + tails
+                                       (1700, 8, 2, 256, 128),    # 425 rows: tiles of 7 or 8 row blocks
                                        (8, 4, 2, 2560, 640),      # full width, streaming
                                        (16, 512, 10, 2560, 640),  # decode geometry, streaming
                                        (100, 4, 2, 2560, 640),    # full width, MFMA
