@@ -2,7 +2,9 @@
 // (Qwen3.8-Flash-Next architecture sheet, MoE entries: routed outputs weighted
 // by the renormalised gates plus the always-on shared expert).  fp32
 // accumulation in slot order, one bf16 rounding.  HBM-bound streaming: each
-// thread owns 8 consecutive hidden columns (one 16-byte bf16 vector).
+// thread owns 8 consecutive hidden columns (one 16-byte bf16 vector).  bf16
+// rows are read and y is written with the non-temporal hint (each is touched
+// once; 32768-token pruned layer 4.29 -> 4.26 ms a step).
 #include "common.h"
 #include "kernels.h"
 
@@ -44,7 +46,7 @@ __device__ __forceinline__ void combine_batch(const void* rows, int H, int v, in
 #pragma unroll
         for (int u = 0; u < N; ++u) {
             const size_t r = (size_t)__builtin_amdgcn_readlane(rl, j + u);
-            w[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(rows) + r * H + v * 8);
+            w[u] = ld_stream(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(rows) + r * H + v * 8));
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(512) void combine_kernel(const void* __restrict__ r
             out.y = pack_bf16x2(acc[2], acc[3]);
             out.z = pack_bf16x2(acc[4], acc[5]);
             out.w = pack_bf16x2(acc[6], acc[7]);
-            *reinterpret_cast<uint4*>(y + (size_t)t * H + v * 8) = out;
+            st_stream(y + (size_t)t * H + v * 8, u32x4_t{out.x, out.y, out.z, out.w});
         }
     }
 }
