@@ -555,12 +555,11 @@ __device__ __forceinline__ void om_gemm_tile(const GroupedArgs& a, uint16_t* __r
     }
 }
 
-// The grouped GEMM over a tile table.  In the gate/up pass with tiles of 192
-// or 256 rows, a tile of fewer rows runs a copy of the loop with one or two
-// row blocks fewer (chosen per tile, outside the K loop, so that every copy
-// keeps a static schedule): an expert whose rows just exceed a multiple of
-// 32 TM is split into tiles one block short, and its last tile is often
-// shorter still.  Shorter tiles compute TM - 2 blocks.
+// The grouped GEMM over a tile table.  A tile of fewer rows than 32 TM may
+// run a copy of the loop with fewer row blocks (chosen per tile, outside the
+// K loop, so that every copy keeps a static schedule): an expert whose rows
+// just exceed a multiple of 32 TM is split into tiles one block short, and
+// its last tile is often shorter still.
 template <int MODE, int WF, int TM>
 __global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(OmShape<TM>::MINW, OmShape<TM>::MINW)))
 void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* __restrict__ hbuf, int NT) {
@@ -572,10 +571,13 @@ void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* 
     const int m0 = tiles[2 + 3 * tile];
     const int m1 = tiles[3 + 3 * tile];
     const int tv = (m1 - m0 + 31) >> 5;  // row blocks the tile needs, 1 .. TM
-    // gate/up tiles of 192 or 256 rows only: the down projection's short
-    // tiles (two workgroups a compute unit) measured slower with the copies
+    // gate/up tiles of 192 or 256 rows: copies one and two blocks short.
+    // Down tiles of 128 rows (two workgroups a compute unit): one copy of two
+    // blocks, for an expert's last tile of at most 64 rows (copies of two and
+    // three blocks measured slower than none)
     constexpr bool VAR = MODE == OM_GATEUP && TM >= 6;
-    constexpr int T1 = VAR ? TM - 1 : TM, T2 = VAR ? TM - 2 : TM;
+    constexpr bool VD = MODE == OM_DOWN && TM == 4;
+    constexpr int T1 = VAR ? TM - 1 : VD ? 2 : TM, T2 = VAR ? TM - 2 : VD ? 2 : TM;
     if constexpr (T1 == TM) {
         om_gemm_tile<MODE, WF, TM>(a, smem, hbuf, e, m0, m1, nt);
     } else if constexpr (T2 == T1) {
