@@ -49,9 +49,10 @@
 // 16-byte chunks XOR-swizzled by row (om_swz).
 //
 // Row tiles: an expert's rows are split into ceil(rows / BM) tiles of equal
-// size (a multiple of 32), so that no tile is mostly padding.  (Skipping the
-// MFMAs of 32-row blocks past a tile's end with a branch inside the step
-// measured 14% slower than computing them.)
+// size (a multiple of 32), so that no tile is mostly padding; a tile that
+// needs fewer 32-row blocks may run a copy of the loop compiled for fewer
+// (om_gemm_kernel).  (Skipping the MFMAs of 32-row blocks past a tile's end
+// with a branch inside the step measured 14% slower than computing them.)
 //
 // Pipeline: a step is 4 TM pieces (k-chunk h = piece / TM, A fragment mi =
 // piece % TM), each 2 MFMAs plus a share of the dequantisation of the next
