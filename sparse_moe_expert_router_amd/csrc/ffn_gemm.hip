@@ -647,7 +647,12 @@ hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t
     a.down.w = B;
     a.out_f32 = 1;
     a.rows = C;
-    const int BM = pick_bm_dense(M, N / kBN);
+    // 128-row tiles from a grid of 256 workgroups (one a compute unit): the
+    // router's screening product runs beside the shared expert's GEMMs, and
+    // the larger tile reads the router weights half as often (32768 tokens
+    // over 256 experts: 81.6 -> 73.7 us alone, layer 4.15 -> 4.11 ms)
+    int BM = pick_bm_dense(M, N / kBN);
+    if (BM == 64 && (long)((M + 127) / 128) * (N / kBN) >= 256) BM = 128;
     const int mt = max_tiles(M, 1, BM);
     int32_t* tiles = static_cast<int32_t*>(ws);
     uint16_t* Ain = const_cast<uint16_t*>(A);
