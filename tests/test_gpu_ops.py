@@ -241,7 +241,9 @@ def test_nvfp4_quantize_ragged_rows_and_empty():
     assert moe.nvfp4_quantize(empty, 0.01).shape == (0, 64)
 
 
-@pytest.mark.parametrize("T,H,F", [(16, 2560, 640), (100, 2560, 640), (5, 256, 128), (700, 256, 128)])
+# 700 and 600 tokens: 256-row gate/up and down tiles with a ragged last tile
+@pytest.mark.parametrize("T,H,F", [(16, 2560, 640), (100, 2560, 640), (5, 256, 128), (700, 256, 128),
+                                   (600, 2560, 640)])
 def test_shared_expert_identity_mode(T, H, F):
     moe = require_gpu()
     w = _wl(T, H, 8, F=F)
