@@ -331,11 +331,13 @@ __global__ __launch_bounds__(GemmShape<BM>::NT) __attribute__((amdgpu_waves_per_
     __shared__ __attribute__((aligned(16))) uint16_t Bs[3][kBN * kBK];
     __shared__ __attribute__((aligned(16))) float2 Ps[3][kBN];  // AWQ (s, -(16 + z) s) per column
 
-    const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
+    // tiles == nullptr: one expert, tile i is rows i BM .. (the dense product)
+    const int ntl = tiles ? tiles[0] : (a.P + BM - 1) / BM;
+    const int l = xcd_remap(blockIdx.x, ntl * NT);
     if (l < 0) return;
     const int tile = l / NT, nt = l % NT;
-    const int e = tiles[1 + 2 * tile];
-    const int m0 = tiles[2 + 2 * tile];
+    const int e = tiles ? tiles[1 + 2 * tile] : 0;
+    const int m0 = tiles ? tiles[2 + 2 * tile] : tile * BM;
     const int m1 = a.offsets ? min(m0 + BM, (int)a.offsets[e + 1]) : min(m0 + BM, a.P);
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -654,10 +656,10 @@ hipError_t launch_dense_gemm_f32(const uint16_t* A, int M, int K, const uint16_t
     int BM = pick_bm_dense(M, N / kBN);
     if (BM == 64 && (long)((M + 127) / 128) * (N / kBN) >= 256) BM = 128;
     const int mt = max_tiles(M, 1, BM);
-    int32_t* tiles = static_cast<int32_t*>(ws);
+    // one expert: the kernel derives its tiles from the block index
+    const int32_t* tiles = nullptr;
+    (void)ws;
     uint16_t* Ain = const_cast<uint16_t*>(A);
-    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, (const int32_t*)nullptr, 1, M, BM,
-                       tiles);
     const int NT = N / kBN;
     if (BM == 256)
         hipLaunchKernelGGL((grouped_gemm_kernel<MODE_DOWN, 0, 256>), gemm_grid(mt, NT), dim3(GemmShape<256>::NT), 0,

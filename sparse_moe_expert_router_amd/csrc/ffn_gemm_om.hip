@@ -565,12 +565,16 @@ template <int MODE, int WF, int TM>
 __global__ __launch_bounds__(kOmThreads) __attribute__((amdgpu_waves_per_eu(OmShape<TM>::MINW, OmShape<TM>::MINW)))
 void om_gemm_kernel(GroupedArgs a, const int32_t* __restrict__ tiles, uint16_t* __restrict__ hbuf, int NT) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[OmShape<TM>::SMEM];
-    const int l = xcd_remap(blockIdx.x, tiles[0] * NT);
+    // tiles == nullptr: one expert (identity mode), split as the tile table
+    // splits an expert: ceil(P / 32 TM) tiles of equal size, a multiple of 32
+    const int ntl = tiles ? tiles[0] : (a.P + 32 * TM - 1) / (32 * TM);
+    const int l = xcd_remap(blockIdx.x, ntl * NT);
     if (l < 0) return;
     const int tile = l / NT, nt = l % NT;
-    const int e = tiles[1 + 3 * tile];
-    const int m0 = tiles[2 + 3 * tile];
-    const int m1 = tiles[3 + 3 * tile];
+    const int isz = tiles ? 0 : ((a.P + ntl - 1) / ntl + 31) / 32 * 32;
+    const int e = tiles ? tiles[1 + 3 * tile] : 0;
+    const int m0 = tiles ? tiles[2 + 3 * tile] : tile * isz;
+    const int m1 = tiles ? tiles[3 + 3 * tile] : min(m0 + isz, a.P);
     const int tv = (m1 - m0 + 31) >> 5;  // row blocks the tile needs, 1 .. TM
     // gate/up tiles of 192 or 256 rows: copies one and two blocks short.
     // Down tiles of 128 rows (two workgroups a compute unit): one copy of two
@@ -700,9 +704,16 @@ hipError_t launch_om_gemm(const GroupedArgs& a, void* ws, hipStream_t s) {
     int32_t* tiles = static_cast<int32_t*>(ws);
     int32_t* tiles_d = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + om_tiles_bytes(a.P, E));
     uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + 2 * om_tiles_bytes(a.P, E));
-    hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TMG, tiles);
-    if (TMD != TMG) hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TMD, tiles_d);
-    else tiles_d = tiles;
+    if (!a.offsets) {
+        // one expert: the kernels derive their tiles from the block index
+        tiles = nullptr;
+        tiles_d = nullptr;
+    } else {
+        hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TMG, tiles);
+        if (TMD != TMG)
+            hipLaunchKernelGGL(om_tile_table_kernel, dim3(1), dim3(1024), 0, s, a.offsets, E, a.P, 32 * TMD, tiles_d);
+        else tiles_d = tiles;
+    }
     if (a.nvfp4) {
         launch_om_wf<OM_GATEUP, 3>(a, tiles, hbuf, E, TMG, s);
         launch_om_wf<OM_DOWN, 3>(a, tiles_d, hbuf, E, TMD, s);
